@@ -1,0 +1,126 @@
+"""CPU oracle for the BASP / Ulysses attention-boundary re-layout.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
+with the HIP library under ``sequence_re_layout_amd/``, and that library never
+imports it.
+
+The arithmetic lives in ``oracle.c`` (a plain element loop over the
+destination, written from the pages' definitions; see its header for the
+sources and the readings).  This module only marshals NumPy arrays into it and
+states the fused layout of the three-tensor calls:
+
+* fused seq->head output = HEAD(Q) || HEAD(K) || HEAD(V), each tensor's
+  head-sharded buffer in full, in that order (one output allocation for the
+  three tensors; the Q part is then itself a valid head-sharded O).
+
+Arrays are raw bit containers (``uint16`` for 2-byte types, ``uint32`` for
+4-byte types); the oracle never interprets values.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+ULYSSES = 0
+BASP = 1
+HEAD_MAJOR = 0
+TOKEN_MAJOR = 1
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        lib.orc_groups.argtypes = [i32, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                   ctypes.POINTER(i64)]
+        lib.orc_groups.restype = i32
+        for fn in (lib.orc_seq_to_head, lib.orc_head_to_seq):
+            fn.argtypes = [i32, i32, i64, i64, i64, i64, i64, i64, vp, vp, vp, i32]
+            fn.restype = i32
+        lib.orc_max_threads.argtypes = []
+        lib.orc_max_threads.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _use_library(path: str) -> None:
+    """Point this module at another build of the oracle (the mutation tests
+    load copies with planted mistakes)."""
+    global _lib
+    _lib = None
+    _build.LIB = path
+    _load()
+
+
+def max_threads() -> int:
+    """Threads an OpenMP region of the oracle gets by default."""
+    return int(_load().orc_max_threads())
+
+
+def groups(mode: int, N: int, B: int):
+    """(G, P, Bl) of the scheme, or None when the pages' conditions fail."""
+    G, P, Bl = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    rc = _load().orc_groups(mode, N, B, ctypes.byref(G), ctypes.byref(P), ctypes.byref(Bl))
+    if rc != 0:
+        return None
+    return G.value, P.value, Bl.value
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _run(fn, x, mode, layout, N, B, S, H, d, traffic, threads):
+    x = np.ascontiguousarray(x).reshape(-1)
+    if x.size != B * S * H * d:
+        raise ValueError("input holds %d elements, expected B*S*H*d = %d" % (x.size, B * S * H * d))
+    out = np.empty_like(x)
+    tm = np.zeros((N, N), dtype=np.int64) if traffic else None
+    threads = max_threads() if threads is None else threads
+    rc = fn(mode, layout, N, B, S, H, d, x.itemsize, _ptr(x), _ptr(out),
+            _ptr(tm) if traffic else None, threads)
+    if rc != 0:
+        raise ValueError("oracle rejected mode=%d layout=%d N=%d B=%d S=%d H=%d d=%d"
+                         % (mode, layout, N, B, S, H, d))
+    return (out, tm) if traffic else out
+
+
+def seq_to_head(x, mode, N, B, S, H, d, layout=HEAD_MAJOR, traffic=False, threads=None):
+    """One tensor, sequence-sharded -> head-sharded.  With ``traffic`` also
+    returns the N x N matrix of elements moved from rank i to rank j."""
+    return _run(_load().orc_seq_to_head, x, mode, layout, N, B, S, H, d, traffic, threads)
+
+
+def head_to_seq(x, mode, N, B, S, H, d, layout=HEAD_MAJOR, traffic=False, threads=None):
+    """One tensor, head-sharded -> sequence-sharded (the inverse exchange)."""
+    return _run(_load().orc_head_to_seq, x, mode, layout, N, B, S, H, d, traffic, threads)
+
+
+def seq_to_head_qkv(q, k, v, mode, N, B, S, Hq, Hkv, d, layout=HEAD_MAJOR, threads=None):
+    """Fused Q/K/V seq->head: HEAD(Q) || HEAD(K) || HEAD(V) in one array."""
+    parts = [seq_to_head(q, mode, N, B, S, Hq, d, layout, threads=threads),
+             seq_to_head(k, mode, N, B, S, Hkv, d, layout, threads=threads),
+             seq_to_head(v, mode, N, B, S, Hkv, d, layout, threads=threads)]
+    return np.concatenate(parts)
+
+
+def head_to_seq_qkv(x, mode, N, B, S, Hq, Hkv, d, layout=HEAD_MAJOR, threads=None):
+    """Fused inverse for the gradients dQ/dK/dV: splits HEAD(dQ) || HEAD(dK) ||
+    HEAD(dV) and returns the three sequence-sharded arrays."""
+    x = np.ascontiguousarray(x).reshape(-1)
+    nq, nkv = B * S * Hq * d, B * S * Hkv * d
+    if x.size != nq + 2 * nkv:
+        raise ValueError("fused input holds %d elements, expected %d" % (x.size, nq + 2 * nkv))
+    return (head_to_seq(x[:nq], mode, N, B, S, Hq, d, layout, threads=threads),
+            head_to_seq(x[nq:nq + nkv], mode, N, B, S, Hkv, d, layout, threads=threads),
+            head_to_seq(x[nq + nkv:], mode, N, B, S, Hkv, d, layout, threads=threads))
