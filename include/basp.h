@@ -1,0 +1,236 @@
+/*
+ * basp.h -- C ABI of libbasp: the attention-boundary re-layout of Ulysses
+ * sequence parallelism and of BASP (Batch-Aware Sequence Parallelism) for
+ * one MI355X (gfx950), with all N virtual ranks in one device allocation.
+ *
+ * Method: "BASP: Communication-Efficient Batch-Aware Sequence Parallelism
+ * for LLM Training" (Ghimire, Calhoun).  Citations below name the evolve.pub
+ * review page of the paper ("review") and the fugumt.com abstract page
+ * ("abstract"), with the section on that page.
+ *
+ * ---------------------------------------------------------------------------
+ * What is computed
+ * ---------------------------------------------------------------------------
+ * N ranks share the attention of B sequences of S tokens, H heads, d channels.
+ *
+ *   Ulysses:  one N-way exchange for the whole batch            [review, Summary]
+ *             G = 1 group, P = N members, Bl = B sequences per group.
+ *   BASP:     N = K*B ranks in B disjoint groups of K = N/B, each group owns
+ *             one sequence and exchanges K-way; every rank keeps B*S/N tokens
+ *                                             [review, Summary; Key claims]
+ *             G = B, P = K, Bl = 1.  With B > N the method falls back to data
+ *             parallelism [review, Frequently asked questions]: G = N, P = 1,
+ *             Bl = B/N (B must then be a multiple of N).
+ *
+ * Rank r is member j = r % P of group g = r / P (contiguous rank assignment,
+ * [review, Summary]); group g owns sequences [g*Bl, (g+1)*Bl).  Member j holds
+ * the tokens [j*St, (j+1)*St), St = S/P, before attention and the heads
+ * [j*Hl, (j+1)*Hl), Hl = H/P, after it (heads split evenly over the members,
+ * [review, Frequently asked questions]).
+ *
+ * Memory layouts (element order; a buffer is the concatenation of the N rank
+ * shards in rank order, one allocation):
+ *   sequence-sharded   rank shard [Bl][St][H][d]
+ *   head-sharded       rank shard [Bl][Hl][S][d]   (BASP_LAYOUT_HEAD_MAJOR)
+ *                      rank shard [Bl][S][Hl][d]   (BASP_LAYOUT_TOKEN_MAJOR)
+ * For BASP with B <= N the sequence-sharded buffer is exactly the global
+ * [B][S][H][d] tensor.
+ *
+ * The re-layout copies elements bit for bit ("identical model accuracy",
+ * [abstract, Abstract]): only the element size matters, values are never
+ * interpreted, so NaN payloads, signed zeros and subnormals pass unchanged.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions common to every call
+ * ---------------------------------------------------------------------------
+ * - Pointers named q, k, v, o, in, out, dq, dk, dv, ws are DEVICE pointers on
+ *   the current HIP device; the caller allocates and owns them.  The library
+ *   never allocates, frees or keeps device memory or pointers after a call.
+ * - stream is a hipStream_t passed as void*; NULL is the null stream.  Every
+ *   call that launches work is asynchronous on that stream and does not
+ *   synchronise.
+ * - A plan is immutable host memory.  It may be used from several threads
+ *   and streams at once.
+ * - Every call returns a basp_status (0 = BASP_OK) and also stores it for
+ *   basp_last_error() in the calling thread.  Calls that return a pointer
+ *   return NULL on error.
+ * - Pointer checks made before any launch: a NULL pointer to a non-empty
+ *   buffer is BASP_ERR_INVALID; a pointer not aligned to the element size is
+ *   BASP_ERR_ALIGN; an output range overlapping an input range, or another
+ *   output range, is BASP_ERR_ALIAS.  Inputs may overlap each other.  Wider
+ *   alignment (up to 16 bytes) of all pointers and of d*elem_size lets the
+ *   kernels use wider vector accesses; the result is the same.
+ * - A launch failure reported by the HIP runtime is BASP_ERR_HIP.
+ * - With S = 0 every buffer is empty: calls check the plan and return
+ *   BASP_OK without touching memory (pointers may then be NULL).
+ */
+#ifndef BASP_H
+#define BASP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum basp_status {
+    BASP_OK = 0,
+    BASP_ERR_INVALID = 1,     /* NULL plan/pointer, size <= 0, unknown enum   */
+    BASP_ERR_INDIVISIBLE = 2, /* N % B, B % N (B > N), S % P or H % P != 0    */
+    BASP_ERR_UNSUPPORTED = 3, /* sizes beyond the library's index limits     */
+    BASP_ERR_ALIGN = 4,       /* pointer not aligned to the element size     */
+    BASP_ERR_ALIAS = 5,       /* an output overlaps an input or an output    */
+    BASP_ERR_HIP = 6          /* the HIP runtime reported an error           */
+} basp_status;
+
+typedef enum basp_dtype {
+    BASP_BF16 = 0,  /* 2 bytes */
+    BASP_FP16 = 1,  /* 2 bytes */
+    BASP_FP32 = 2,  /* 4 bytes */
+    BASP_INT32 = 3  /* 4 bytes */
+} basp_dtype;
+
+typedef enum basp_mode {
+    BASP_MODE_ULYSSES = 0, /* one N-way group                              */
+    BASP_MODE_BASP = 1     /* B groups of K = N/B (or data parallel, B > N) */
+} basp_mode;
+
+typedef enum basp_layout {
+    BASP_LAYOUT_HEAD_MAJOR = 0, /* head shard [Bl][Hl][S][d] (default)  */
+    BASP_LAYOUT_TOKEN_MAJOR = 1 /* head shard [Bl][S][Hl][d]            */
+} basp_layout;
+
+typedef struct basp_plan basp_plan;
+
+/* Everything a caller needs to size buffers and to account for traffic.
+ * Element counts are in elements, byte counts in bytes. */
+typedef struct basp_plan_info {
+    int32_t N, B, Hq, Hkv, d, elem_size;
+    int64_t S;
+    int32_t mode, layout, dtype;
+    int32_t G, P, Bl;             /* groups, members per group, sequences per group */
+    int64_t St;                   /* tokens per rank and sequence, S/P             */
+    int32_t Hl_q, Hl_kv;          /* heads per rank, Hq/P and Hkv/P                */
+    int64_t tokens_per_rank;      /* Bl*St = B*S/N                                 */
+    int32_t peers_per_rank;       /* ranks exchanged with, self excluded: P-1      */
+    int64_t q_elems, kv_elems;    /* elements of Q (= O) and of K (= V), all ranks */
+    int64_t q_elems_per_rank, kv_elems_per_rank;
+    int64_t qkv_elems;            /* q_elems + 2*kv_elems: the fused buffer        */
+    int64_t qkv_offset_q, qkv_offset_k, qkv_offset_v; /* element offsets in it   */
+    int64_t per_peer_bytes_q, per_peer_bytes_kv;   /* Bl*St*Hl*d*elem_size        */
+    int64_t cross_rank_bytes_q, cross_rank_bytes_kv; /* (P-1)/P of each tensor    */
+    int64_t qkv_bytes_moved;      /* 2*(q_elems + 2*kv_elems)*elem_size            */
+    int64_t o_bytes_moved;        /* 2*q_elems*elem_size                           */
+} basp_plan_info;
+
+/*
+ * Create a plan.  Host only: no device call, no device memory.
+ *   N    virtual ranks (>= 1)           B    sequences in the micro-batch (>= 1)
+ *   S    tokens per sequence (>= 0)     Hq   query/output heads (>= 1)
+ *   Hkv  key/value heads (>= 1; Hkv < Hq is grouped-query attention, each
+ *        tensor is re-laid with its own head count, no head replication)
+ *   d    channels per head (>= 1)       dtype, mode as above
+ * Errors (NULL returned, code in basp_last_error()):
+ *   BASP_ERR_INVALID      an argument out of range or an unknown enum
+ *   BASP_ERR_INDIVISIBLE  BASP with B <= N and N % B != 0 [review, Summary];
+ *                         BASP with B > N and B % N != 0; S % P, Hq % P or
+ *                         Hkv % P != 0 [review, Frequently asked questions]
+ *   BASP_ERR_UNSUPPORTED  a buffer of more than 2^62 bytes, or more than
+ *                         2^31 - 1 work tiles in one launch
+ * basp_plan_create uses BASP_LAYOUT_HEAD_MAJOR.
+ */
+basp_plan *basp_plan_create(int N, int B, int64_t S, int Hq, int Hkv, int d,
+                            basp_dtype dtype, basp_mode mode);
+basp_plan *basp_plan_create_ex(int N, int B, int64_t S, int Hq, int Hkv, int d,
+                               basp_dtype dtype, basp_mode mode, basp_layout layout);
+
+/* Free a plan.  NULL is allowed. */
+void basp_plan_destroy(basp_plan *plan);
+
+/* Fill *info.  BASP_ERR_INVALID if plan or info is NULL. */
+basp_status basp_plan_query(const basp_plan *plan, basp_plan_info *info);
+
+/*
+ * Fused Q/K/V seq -> head: the exchange before attention, for the three
+ * tensors in one launch [review, Summary; Scope & Claims].
+ *   q    sequence-sharded, q_elems elements  (Hq heads)
+ *   k, v sequence-sharded, kv_elems elements each (Hkv heads)
+ *   out  qkv_elems elements: head-sharded Q, then head-sharded K, then
+ *        head-sharded V, at element offsets qkv_offset_q/_k/_v.  The Q part
+ *        is itself a valid head-sharded O for basp_head_to_seq.
+ */
+basp_status basp_seq_to_head(const basp_plan *plan, const void *q, const void *k,
+                             const void *v, void *out, void *stream);
+
+/*
+ * O head -> seq: the exchange after attention, the inverse of the Q part of
+ * basp_seq_to_head [review, Scope & Claims: the attention-phase all-to-all].
+ *   o    head-sharded, q_elems elements (Hq heads)
+ *   out  sequence-sharded, q_elems elements
+ */
+basp_status basp_head_to_seq(const basp_plan *plan, const void *o, void *out, void *stream);
+
+/*
+ * Backward pass of the same boundary (training, [abstract, Abstract]):
+ * the gradient of head -> seq is seq -> head and the reverse.
+ *
+ * basp_seq_to_head_o: dO sequence-sharded (q_elems, Hq heads) -> head-sharded
+ *   (q_elems).  Same mapping as the Q part of basp_seq_to_head.
+ * basp_head_to_seq_qkv: fused dQ/dK/dV head -> seq, the exact inverse of
+ *   basp_seq_to_head.  in holds qkv_elems elements laid out as that call's
+ *   out; dq (q_elems), dk and dv (kv_elems each) receive sequence-sharded
+ *   gradients.  dq, dk, dv must not overlap in or each other.
+ */
+basp_status basp_seq_to_head_o(const basp_plan *plan, const void *dout, void *out,
+                               void *stream);
+basp_status basp_head_to_seq_qkv(const basp_plan *plan, const void *in, void *dq, void *dk,
+                                 void *dv, void *stream);
+
+/*
+ * Unfused three-pass seq -> head, kept as an internal baseline: the
+ * collective written out as (1) pack each rank's shard by destination member,
+ * (2) exchange the per-peer chunks, (3) unpack into the head-sharded layout.
+ * Same inputs and output as basp_seq_to_head (bit-identical result), three
+ * times the memory traffic.
+ *   ws   device workspace of basp_unfused_workspace_bytes(plan) bytes, owned by
+ *        the caller, aligned like the inputs; its contents on return are
+ *        unspecified.  It must not overlap any input or out (BASP_ERR_ALIAS).
+ * Each tensor must be smaller than 2 GiB here (BASP_ERR_UNSUPPORTED otherwise).
+ * basp_unfused_workspace_bytes returns 0 for a NULL plan.
+ */
+size_t basp_unfused_workspace_bytes(const basp_plan *plan);
+basp_status basp_seq_to_head_unfused(const basp_plan *plan, const void *q, const void *k,
+                                     const void *v, void *out, void *ws, void *stream);
+
+/*
+ * Launch shape of a plan, for tuning sweeps.  Zero fields keep the built-in
+ * choice.  Results never depend on these values, only the speed does.
+ *   vectors_per_thread   1, 2, 4 or 8 (16-byte vectors held in flight per lane)
+ *   tile_tokens          tokens per work tile (>= 1)
+ *   tile_heads           heads per work tile (>= 1, clamped to H/P)
+ *   cache_policy         1 = plain loads and stores, 2 = non-temporal stores,
+ *                        3 = non-temporal loads and stores
+ *   max_grid             cap on work-groups per launch (tiles loop beyond it)
+ * BASP_ERR_INVALID on a NULL plan or an out-of-range value.  Not thread-safe
+ * against concurrent launches with the same plan.
+ */
+typedef struct basp_tuning {
+    int32_t vectors_per_thread;
+    int32_t tile_tokens;
+    int32_t tile_heads;
+    int32_t cache_policy;
+    int32_t max_grid;
+} basp_tuning;
+basp_status basp_plan_set_tuning(basp_plan *plan, const basp_tuning *tuning);
+basp_status basp_plan_get_tuning(const basp_plan *plan, basp_tuning *tuning);
+
+/* Status of the last call made by this thread, and a static description. */
+basp_status basp_last_error(void);
+const char *basp_status_str(basp_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BASP_H */

@@ -1,0 +1,378 @@
+// launch.cpp -- host-side planning of every kernel launch: pointer checks,
+// vector width, tile shape, descriptors and grid.  Plain C++ with no device
+// calls, so that the same code can also drive a CPU emulation of the kernels.
+#include <algorithm>
+#include <cstring>
+
+#ifndef BASP_HD
+#define BASP_HD
+#endif
+#include "launch.hpp"
+#include "plan_internal.hpp"
+
+namespace basp {
+namespace {
+
+constexpr int kDefaultVpt = 4;           // 16-byte vectors in flight per lane
+constexpr int kDefaultPolicy = 2;        // non-temporal stores
+constexpr uint32_t kGridCap = 1u << 22;  // work-groups per launch at most
+
+int resolved_vpt(const basp_tuning &t) { return t.vectors_per_thread ? t.vectors_per_thread : kDefaultVpt; }
+int resolved_policy(const basp_tuning &t) { return t.cache_policy ? t.cache_policy : kDefaultPolicy; }
+
+uint64_t addr(const void *p) { return reinterpret_cast<uint64_t>(p); }
+
+// Widest vector (16, 8, 4 or 2 bytes, never below the element size) that
+// divides the row and every address.
+int vector_width(const basp_plan &p, const uint64_t *addrs, int n)
+{
+    int vw = 16;
+    while (vw > p.es) {
+        bool fits = p.row_bytes % vw == 0;
+        for (int i = 0; i < n && fits; ++i)
+            fits = addrs[i] % vw == 0;
+        if (fits)
+            break;
+        vw /= 2;
+    }
+    return vw;
+}
+
+struct TileShape {
+    uint32_t Ts, Th, ntb, nhb;
+    uint64_t ntiles;
+};
+
+// Tile of one tensor with Hl heads per rank and A vectors per row: about
+// kBlock*vpt vectors, lanes along the head-sharded layout's contiguous axis.
+TileShape tile_shape(const basp_plan &p, const basp_tuning &t, uint32_t Hl, uint32_t A)
+{
+    const bool s_fast = p.layout == BASP_LAYOUT_HEAD_MAJOR;
+    const uint64_t rows = std::max<uint64_t>(1, uint64_t(kBlock) * resolved_vpt(t) / A);
+    uint64_t th = t.tile_heads ? uint64_t(t.tile_heads) : (s_fast ? 1 : std::min<uint64_t>(Hl, rows));
+    th = std::min<uint64_t>(th, Hl);
+    uint64_t ts = t.tile_tokens ? uint64_t(t.tile_tokens) : std::max<uint64_t>(1, rows / th);
+    ts = std::min<uint64_t>(ts, uint64_t(std::max<int64_t>(p.St, 1)));
+    TileShape s;
+    s.Ts = uint32_t(ts);
+    s.Th = uint32_t(th);
+    s.ntb = uint32_t((uint64_t(p.St) + ts - 1) / ts);
+    s.nhb = uint32_t((Hl + th - 1) / th);
+    s.ntiles = uint64_t(p.G) * p.P * p.Bl * s.nhb * p.P * s.ntb;
+    return s;
+}
+
+struct Strides {
+    uint64_t seq_rank, seq_bl, seq_tok;
+    uint64_t head_rank, head_bl, head_tok, head_head;
+};
+
+// Byte strides of both layouts for a tensor of H heads (basp.h, "Memory layouts").
+Strides strides(const basp_plan &p, uint32_t H)
+{
+    const uint64_t row = p.row_bytes, Hl = H / p.P, S = p.S, St = p.St, Bl = p.Bl;
+    Strides s;
+    s.seq_tok = H * row;
+    s.seq_bl = St * s.seq_tok;
+    s.seq_rank = Bl * s.seq_bl;
+    if (p.layout == BASP_LAYOUT_HEAD_MAJOR) {
+        s.head_tok = row;
+        s.head_head = S * row;
+        s.head_bl = Hl * S * row;
+    } else {
+        s.head_head = row;
+        s.head_tok = Hl * row;
+        s.head_bl = S * Hl * row;
+    }
+    s.head_rank = Bl * s.head_bl;
+    return s;
+}
+
+// Every offset a lane computes inside a tile stays below kI31Max.
+bool tile_offsets_fit(const basp_plan &p, uint32_t H, const TileShape &ts)
+{
+    const Strides s = strides(p, H);
+    const uint64_t seq_max = (ts.Ts - 1) * s.seq_tok + uint64_t(ts.Th) * p.row_bytes;
+    const uint64_t head_max = (ts.Ts - 1) * s.head_tok + (ts.Th - 1) * s.head_head + p.row_bytes;
+    return seq_max <= kI31Max && head_max <= kI31Max && s.seq_tok <= kI31Max &&
+           s.head_tok <= kI31Max && (ts.Th == 1 || s.head_head <= kI31Max);
+}
+
+struct SegSpec {
+    uint64_t seq, head;   // addresses
+    uint32_t H;           // heads of this tensor
+};
+
+int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, TileLaunch &L)
+{
+    std::memset(&L, 0, sizeof(L));
+    uint64_t addrs[6];
+    for (int i = 0; i < nseg; ++i) {
+        addrs[2 * i] = segs[i].seq;
+        addrs[2 * i + 1] = segs[i].head;
+    }
+    const int vw = vector_width(p, addrs, 2 * nseg);
+    const uint32_t A = uint32_t(p.row_bytes / vw);
+    TileDesc &D = L.D;
+    D.St = uint32_t(p.St);
+    D.row = uint32_t(p.row_bytes);
+    D.s_fast = p.layout == BASP_LAYOUT_HEAD_MAJOR;
+    D.P = make_fastdiv(p.P);
+    D.Bl = make_fastdiv(p.Bl);
+    D.A = make_fastdiv(A);
+    uint64_t total = 0;
+    for (int i = 0; i < 3; ++i) {
+        TileSeg &sg = D.seg[i];
+        if (i >= nseg) {            // unused slot: an empty range after the last tensor
+            sg = D.seg[i - 1];
+            sg.tile_begin = sg.tile_end;
+            continue;
+        }
+        const uint32_t H = segs[i].H, Hl = H / p.P;
+        const TileShape ts = tile_shape(p, p.tuning, Hl, A);
+        if (!tile_offsets_fit(p, H, ts))
+            return BASP_ERR_UNSUPPORTED;
+        const Strides st = strides(p, H);
+        sg.seq = segs[i].seq;
+        sg.head = segs[i].head;
+        sg.seq_bytes = uint64_t(p.B) * p.S * H * p.row_bytes;
+        sg.head_bytes = sg.seq_bytes;
+        sg.seq_rank = st.seq_rank;
+        sg.seq_bl = st.seq_bl;
+        sg.head_rank = st.head_rank;
+        sg.head_bl = st.head_bl;
+        sg.head_head = st.head_head;
+        sg.seq_tok = uint32_t(st.seq_tok);
+        sg.head_tok = uint32_t(st.head_tok);
+        sg.head_head_lane = ts.Th == 1 ? 0u : uint32_t(st.head_head);
+        sg.Hl = Hl;
+        sg.Ts = ts.Ts;
+        sg.Th = ts.Th;
+        sg.ntb = make_fastdiv(ts.ntb);
+        sg.nhb = make_fastdiv(ts.nhb);
+        sg.fast = make_fastdiv(D.s_fast ? ts.Ts : ts.Th);
+        sg.tile_begin = uint32_t(total);
+        total += ts.ntiles;
+        if (total > kI31Max || uint64_t(ts.Ts) * ts.Th * A > kI31Max)
+            return BASP_ERR_UNSUPPORTED;
+        sg.tile_end = uint32_t(total);
+    }
+    D.ntiles = uint32_t(total);
+    const uint32_t cap = p.tuning.max_grid ? uint32_t(p.tuning.max_grid) : kGridCap;
+    L.grid = uint32_t(std::min<uint64_t>(total, cap));
+    L.vw = vw;
+    L.vpt = resolved_vpt(p.tuning);
+    L.policy = resolved_policy(p.tuning);
+    L.s2h = s2h;
+    return BASP_OK;
+}
+
+bool overlaps(uint64_t a, uint64_t na, uint64_t b, uint64_t nb)
+{
+    return na && nb && a < b + nb && b < a + na;
+}
+
+struct Buf {
+    const void *ptr;
+    uint64_t bytes;
+};
+
+// NULL, alignment and aliasing checks (basp.h, "Conventions").
+int check_buffers(const basp_plan &p, const Buf *ins, int nin, const Buf *outs, int nout)
+{
+    for (int i = 0; i < nin + nout; ++i) {
+        const Buf &b = i < nin ? ins[i] : outs[i - nin];
+        if (b.bytes && !b.ptr)
+            return BASP_ERR_INVALID;
+        if (addr(b.ptr) % p.es)
+            return BASP_ERR_ALIGN;
+    }
+    for (int o = 0; o < nout; ++o) {
+        for (int i = 0; i < nin; ++i)
+            if (overlaps(addr(outs[o].ptr), outs[o].bytes, addr(ins[i].ptr), ins[i].bytes))
+                return BASP_ERR_ALIAS;
+        for (int j = 0; j < o; ++j)
+            if (overlaps(addr(outs[o].ptr), outs[o].bytes, addr(outs[j].ptr), outs[j].bytes))
+                return BASP_ERR_ALIAS;
+    }
+    return BASP_OK;
+}
+
+struct PermSpec {
+    uint64_t src, dst, src_bytes, dst_bytes;
+    uint32_t ext[5];       // digit extents, d0 slowest
+    uint32_t sstride[5];   // source strides in rows
+    uint64_t rows;
+};
+
+int build_perm(const basp_plan &p, const PermSpec *ps, int n, int vw, PermLaunch &L)
+{
+    std::memset(&L, 0, sizeof(L));
+    PermDesc &D = L.D;
+    const uint32_t A = uint32_t(p.row_bytes / vw);
+    D.row = uint32_t(p.row_bytes);
+    D.A = make_fastdiv(A);
+    uint64_t chunks = 0;
+    for (int i = 0; i < 3; ++i) {
+        PermSeg &sg = D.seg[i];
+        if (i >= n) {
+            sg = D.seg[i - 1];
+            sg.chunk_begin = sg.chunk_end;
+            continue;
+        }
+        const uint64_t nvec = ps[i].rows * A;
+        if (nvec > kI31Max || ps[i].src_bytes > kI31Max || ps[i].dst_bytes > kI31Max)
+            return BASP_ERR_UNSUPPORTED;
+        sg.src = ps[i].src;
+        sg.dst = ps[i].dst;
+        sg.src_bytes = ps[i].src_bytes;
+        sg.dst_bytes = ps[i].dst_bytes;
+        for (int j = 0; j < 4; ++j)
+            sg.ext[j] = make_fastdiv(ps[i].ext[j + 1]);
+        for (int j = 0; j < 5; ++j)
+            sg.sstride[j] = ps[i].sstride[j];
+        sg.nvec = uint32_t(nvec);
+        sg.chunk_begin = uint32_t(chunks);
+        chunks += (nvec + kBlock * kPermVpt - 1) / (kBlock * kPermVpt);
+        sg.chunk_end = uint32_t(chunks);
+    }
+    D.nchunks = uint32_t(chunks);
+    L.grid = uint32_t(std::min<uint64_t>(chunks, kGridCap));
+    L.vw = vw;
+    return BASP_OK;
+}
+
+}  // namespace
+
+basp_status check_launch_limits(const basp_plan &p, const basp_tuning &t)
+{
+    if (p.St > int64_t(kI31Max) || p.row_bytes > int64_t(kI31Max) ||
+        int64_t(p.Hq) * p.row_bytes > int64_t(kI31Max))
+        return BASP_ERR_UNSUPPORTED;
+    for (int vw = 16; vw >= p.es; vw /= 2) {
+        if (p.row_bytes % vw)
+            continue;
+        const uint32_t A = uint32_t(p.row_bytes / vw);
+        uint64_t total = 0;
+        const uint32_t heads[3] = {uint32_t(p.Hq), uint32_t(p.Hkv), uint32_t(p.Hkv)};
+        for (int i = 0; i < 3; ++i) {
+            const TileShape ts = tile_shape(p, t, heads[i] / p.P, A);
+            if (!tile_offsets_fit(p, heads[i], ts) || uint64_t(ts.Ts) * ts.Th * A > kI31Max)
+                return BASP_ERR_UNSUPPORTED;
+            total += ts.ntiles;
+        }
+        if (total > kI31Max)
+            return BASP_ERR_UNSUPPORTED;
+    }
+    return BASP_OK;
+}
+
+int prepare_seq_to_head(const basp_plan &p, const void *q, const void *k, const void *v, void *out,
+                        TileLaunch &L)
+{
+    std::memset(&L, 0, sizeof(L));
+    const uint64_t qb = uint64_t(p.q_elems) * p.es, kb = uint64_t(p.kv_elems) * p.es;
+    const Buf ins[3] = {{q, qb}, {k, kb}, {v, kb}};
+    const Buf outs[1] = {{out, qb + 2 * kb}};
+    const int s = check_buffers(p, ins, 3, outs, 1);
+    if (s != BASP_OK || p.S == 0)
+        return s;
+    const uint64_t o = addr(out);
+    const SegSpec segs[3] = {{addr(q), o, uint32_t(p.Hq)},
+                             {addr(k), o + qb, uint32_t(p.Hkv)},
+                             {addr(v), o + qb + kb, uint32_t(p.Hkv)}};
+    return build_tiles(p, segs, 3, true, L);
+}
+
+int prepare_head_to_seq(const basp_plan &p, const void *o, void *out, TileLaunch &L)
+{
+    std::memset(&L, 0, sizeof(L));
+    const uint64_t qb = uint64_t(p.q_elems) * p.es;
+    const Buf ins[1] = {{o, qb}};
+    const Buf outs[1] = {{out, qb}};
+    const int s = check_buffers(p, ins, 1, outs, 1);
+    if (s != BASP_OK || p.S == 0)
+        return s;
+    const SegSpec segs[1] = {{addr(out), addr(o), uint32_t(p.Hq)}};
+    return build_tiles(p, segs, 1, false, L);
+}
+
+int prepare_seq_to_head_o(const basp_plan &p, const void *dout, void *out, TileLaunch &L)
+{
+    std::memset(&L, 0, sizeof(L));
+    const uint64_t qb = uint64_t(p.q_elems) * p.es;
+    const Buf ins[1] = {{dout, qb}};
+    const Buf outs[1] = {{out, qb}};
+    const int s = check_buffers(p, ins, 1, outs, 1);
+    if (s != BASP_OK || p.S == 0)
+        return s;
+    const SegSpec segs[1] = {{addr(dout), addr(out), uint32_t(p.Hq)}};
+    return build_tiles(p, segs, 1, true, L);
+}
+
+int prepare_head_to_seq_qkv(const basp_plan &p, const void *in, void *dq, void *dk, void *dv,
+                            TileLaunch &L)
+{
+    std::memset(&L, 0, sizeof(L));
+    const uint64_t qb = uint64_t(p.q_elems) * p.es, kb = uint64_t(p.kv_elems) * p.es;
+    const Buf ins[1] = {{in, qb + 2 * kb}};
+    const Buf outs[3] = {{dq, qb}, {dk, kb}, {dv, kb}};
+    const int s = check_buffers(p, ins, 1, outs, 3);
+    if (s != BASP_OK || p.S == 0)
+        return s;
+    const uint64_t i = addr(in);
+    const SegSpec segs[3] = {{addr(dq), i, uint32_t(p.Hq)},
+                             {addr(dk), i + qb, uint32_t(p.Hkv)},
+                             {addr(dv), i + qb + kb, uint32_t(p.Hkv)}};
+    return build_tiles(p, segs, 3, false, L);
+}
+
+int prepare_seq_to_head_unfused(const basp_plan &p, const void *q, const void *k, const void *v,
+                                void *out, void *ws, PermLaunch L[3])
+{
+    std::memset(L, 0, 3 * sizeof(PermLaunch));
+    const uint64_t qb = uint64_t(p.q_elems) * p.es, kb = uint64_t(p.kv_elems) * p.es;
+    const uint64_t tot = qb + 2 * kb;
+    const Buf ins[3] = {{q, qb}, {k, kb}, {v, kb}};
+    const Buf outs[2] = {{out, tot}, {ws, 2 * tot}};
+    int s = check_buffers(p, ins, 3, outs, 2);
+    if (s != BASP_OK || p.S == 0)
+        return s;
+
+    const uint64_t w1 = addr(ws), w2 = w1 + tot, o = addr(out);
+    const uint64_t src[3] = {addr(q), addr(k), addr(v)};
+    const uint64_t off[3] = {0, qb, qb + kb};
+    const uint64_t bytes[3] = {qb, kb, kb};
+    const uint32_t heads[3] = {uint32_t(p.Hq), uint32_t(p.Hkv), uint32_t(p.Hkv)};
+    const uint64_t addrs[6] = {src[0], src[1], src[2], o, w1, w2};
+    const int vw = vector_width(p, addrs, 6);
+
+    const uint32_t N = p.N, P = p.P, Bl = p.Bl, St = uint32_t(p.St), G = p.G;
+    PermSpec pack[3], xchg[3], unpack[3];
+    for (int i = 0; i < 3; ++i) {
+        const uint32_t H = heads[i], Hl = H / P;
+        const uint64_t rows = bytes[i] / p.row_bytes;
+        const uint32_t C = Bl * St * Hl;  // rows of one per-peer chunk
+        // (1) pack each rank's shard by destination member:
+        //     [r][Bl][St][P*Hl] -> [r][jh][Bl][St][Hl]
+        pack[i] = {src[i], w1 + off[i], bytes[i], bytes[i],
+                   {N, P, Bl, St, Hl}, {Bl * St * H, Hl, St * H, H, 1}, rows};
+        // (2) exchange: chunk jh of rank (g, js) becomes chunk js of rank (g, jh)
+        xchg[i] = {w1 + off[i], w2 + off[i], bytes[i], bytes[i],
+                   {G, P, P, C, 1}, {P * P * C, C, P * C, 1, 0}, rows};
+        // (3) unpack [r][js][Bl][St][Hl] into the head-sharded layout
+        if (p.layout == BASP_LAYOUT_HEAD_MAJOR)
+            unpack[i] = {w2 + off[i], o + off[i], bytes[i], bytes[i],
+                         {N, Bl, Hl, P, St}, {P * C, St * Hl, 1, C, Hl}, rows};
+        else
+            unpack[i] = {w2 + off[i], o + off[i], bytes[i], bytes[i],
+                         {N, Bl, P, St, Hl}, {P * C, St * Hl, C, Hl, 1}, rows};
+    }
+    if ((s = build_perm(p, pack, 3, vw, L[0])) != BASP_OK)
+        return s;
+    if ((s = build_perm(p, xchg, 3, vw, L[1])) != BASP_OK)
+        return s;
+    return build_perm(p, unpack, 3, vw, L[2]);
+}
+
+}  // namespace basp

@@ -1,0 +1,177 @@
+// launch.hpp -- launch descriptors of the re-layout kernels and the index
+// arithmetic every lane runs, as plain C++ shared by the HIP kernels and the
+// host-side planning code.
+//
+// The exchange at the attention boundary (BASP review page, "Summary";
+// "Scope & Claims") moves (token, head) rows of d*es bytes: member js of
+// group g holds tokens [js*St, (js+1)*St) of every head before attention,
+// member jh holds heads [jh*Hl, (jh+1)*Hl) of every token after it.
+//
+// Tile kernel.  A work tile is the rectangle
+//     tokens [t0, t0+Ts) of source member js  x  heads [hl0, hl0+Th) of
+//     destination member jh,  for one group g and local sequence bl.
+// Inside a tile both layouts are 2-D strided arrays of rows:
+//     sequence-sharded  t*H*row + h*row
+//     head-major        h*S*row + t*row
+//     token-major       t*Hl*row + h*row
+// so a work-group computes the tile's two base addresses once and each lane
+// only adds 32-bit offsets.  Tiles are numbered (g, jh, bl, hb, js, tb) with
+// the token block tb fastest.
+//
+// Perm kernel (unfused baseline).  Writes its destination linearly; row i of
+// the destination has digits (d0..d4), d4 fastest, and is read from source
+// row sum(d_k * sstride_k).
+#pragma once
+
+#include <cstdint>
+
+#include "fastdiv.hpp"
+
+struct basp_plan;
+
+namespace basp {
+
+constexpr int kBlock = 256;               // threads per work-group (4 waves)
+constexpr uint64_t kI31Max = 0x7fffffffull;
+// Buffer descriptors span at most kI31Max bytes and every real offset is
+// below that, so a lane given kOutside touches nothing: its load returns zero
+// and its store is dropped.
+constexpr uint32_t kOutside = 0x80000000u;
+
+// One tensor of a tile launch.
+struct TileSeg {
+    uint64_t seq, head;            // buffer addresses
+    uint64_t seq_bytes, head_bytes;
+    uint64_t seq_rank, seq_bl;     // byte strides of a rank and a local sequence
+    uint64_t head_rank, head_bl;
+    uint64_t head_head;            // byte stride of a head, head-sharded
+    uint32_t seq_tok;              // byte stride of a token, sequence-sharded
+    uint32_t head_tok;             // byte stride of a token, head-sharded
+    uint32_t head_head_lane;       // head stride inside a tile (0 when Th == 1)
+    uint32_t Hl;                   // heads per rank
+    uint32_t Ts, Th;               // tile extent in tokens and heads
+    FastDiv ntb;                   // token blocks per member chunk
+    FastDiv nhb;                   // head blocks per rank
+    FastDiv fast;                  // extent of the lane-fastest tile axis
+    uint32_t tile_begin, tile_end;
+};
+
+struct TileDesc {
+    TileSeg seg[3];
+    uint32_t ntiles;
+    uint32_t St;
+    uint32_t row;                  // bytes per (token, head) row
+    uint32_t s_fast;               // lanes along tokens (1) or heads (0)
+    FastDiv P, Bl, A;              // group size, sequences per group, vectors per row
+};
+
+// Where a tile starts and how much of it is real.
+struct TileOrigin {
+    uint32_t seg;
+    uint64_t seq_off, head_off;    // byte offsets of the tile base
+    uint32_t ns, nh;               // tokens and heads present (ragged tail)
+};
+
+BASP_HD inline TileOrigin tile_origin(const TileDesc &D, uint32_t tile)
+{
+    TileOrigin o;
+    o.seg = (tile >= D.seg[0].tile_end) + (tile >= D.seg[1].tile_end);
+    const TileSeg &sg = D.seg[o.seg];
+    const uint32_t P = D.P.d;
+    const uint32_t local = tile - sg.tile_begin;
+    const uint32_t q1 = fastdiv(local, sg.ntb), tb = local - q1 * sg.ntb.d;
+    const uint32_t q2 = fastdiv(q1, D.P), js = q1 - q2 * P;
+    const uint32_t q3 = fastdiv(q2, sg.nhb), hb = q2 - q3 * sg.nhb.d;
+    const uint32_t q4 = fastdiv(q3, D.Bl), bl = q3 - q4 * D.Bl.d;
+    const uint32_t g = fastdiv(q4, D.P), jh = q4 - g * P;
+    const uint32_t t0 = tb * sg.Ts, hl0 = hb * sg.Th;
+    o.ns = D.St - t0 < sg.Ts ? D.St - t0 : sg.Ts;
+    o.nh = sg.Hl - hl0 < sg.Th ? sg.Hl - hl0 : sg.Th;
+    const uint64_t rs = uint64_t(g) * P + js, rh = uint64_t(g) * P + jh;
+    o.seq_off = rs * sg.seq_rank + bl * sg.seq_bl + uint64_t(t0) * sg.seq_tok +
+                (uint64_t(jh) * sg.Hl + hl0) * D.row;
+    o.head_off = rh * sg.head_rank + bl * sg.head_bl + (uint64_t(js) * D.St + t0) * sg.head_tok +
+                 uint64_t(hl0) * sg.head_head;
+    return o;
+}
+
+// Offsets (from the tile base) of the vw-byte vector v of a tile in the
+// sequence-sharded (so) and head-sharded (ho) buffers.  Returns false for a
+// vector outside the tile's present rows.
+BASP_HD inline bool lane_offsets(const TileDesc &D, const TileSeg &sg, uint32_t ns, uint32_t nh,
+                                 uint32_t v, uint32_t vw, uint32_t &so, uint32_t &ho)
+{
+    const uint32_t nvec = sg.Ts * sg.Th * D.A.d;
+    const uint32_t r = fastdiv(v, D.A), vi = v - r * D.A.d;
+    const uint32_t slow = fastdiv(r, sg.fast), fst = r - slow * sg.fast.d;
+    const uint32_t sl = D.s_fast ? fst : slow, hl = D.s_fast ? slow : fst;
+    so = sl * sg.seq_tok + hl * D.row + vi * vw;
+    ho = sl * sg.head_tok + hl * sg.head_head_lane + vi * vw;
+    return (v < nvec) & (sl < ns) & (hl < nh);
+}
+
+struct PermSeg {
+    uint64_t src, dst;
+    uint64_t src_bytes, dst_bytes;
+    FastDiv ext[4];        // extents of d1..d4
+    uint32_t sstride[5];   // source strides in rows
+    uint32_t nvec;         // vectors in this tensor
+    uint32_t chunk_begin, chunk_end;
+};
+
+struct PermDesc {
+    PermSeg seg[3];
+    uint32_t nchunks;
+    uint32_t row;
+    FastDiv A;
+};
+
+constexpr int kPermVpt = 4;   // vectors per lane in the perm kernel
+
+BASP_HD inline uint32_t perm_segment(const PermDesc &D, uint32_t chunk)
+{
+    return (chunk >= D.seg[0].chunk_end) + (chunk >= D.seg[1].chunk_end);
+}
+
+// Source byte offset of the vw-byte destination vector v of a tensor.
+BASP_HD inline uint32_t perm_source(const PermDesc &D, const PermSeg &sg, uint32_t v, uint32_t vw)
+{
+    const uint32_t r = fastdiv(v, D.A), vi = v - r * D.A.d;
+    uint32_t q = r, src_row = 0;
+    for (int j = 3; j >= 0; --j) {
+        const uint32_t qn = fastdiv(q, sg.ext[j]);
+        src_row += (q - qn * sg.ext[j].d) * sg.sstride[j + 1];
+        q = qn;
+    }
+    src_row += q * sg.sstride[0];
+    return src_row * D.row + vi * vw;
+}
+
+// ------------------------------------------------------------ host side --
+
+// A tile launch ready to go: descriptor, template parameters, grid.
+struct TileLaunch {
+    TileDesc D;
+    int vw, vpt, policy;
+    bool s2h;                 // read sequence-sharded, write head-sharded
+    uint32_t grid;            // 0: nothing to launch
+};
+
+struct PermLaunch {
+    PermDesc D;
+    int vw;
+    uint32_t grid;
+};
+
+// Checks and descriptors of each entry point (basp.h).  They return the
+// status the entry point reports; on BASP_OK the launch(es) are filled.
+int prepare_seq_to_head(const basp_plan &p, const void *q, const void *k, const void *v, void *out,
+                        TileLaunch &L);
+int prepare_head_to_seq(const basp_plan &p, const void *o, void *out, TileLaunch &L);
+int prepare_seq_to_head_o(const basp_plan &p, const void *dout, void *out, TileLaunch &L);
+int prepare_head_to_seq_qkv(const basp_plan &p, const void *in, void *dq, void *dk, void *dv,
+                            TileLaunch &L);
+int prepare_seq_to_head_unfused(const basp_plan &p, const void *q, const void *k, const void *v,
+                                void *out, void *ws, PermLaunch L[3]);
+
+}  // namespace basp

@@ -1,0 +1,266 @@
+// relayout.hip -- gfx950 kernels of libbasp and the C-ABI entry points that
+// launch them (include/basp.h).  Launch planning and the per-lane index
+// arithmetic are in launch.hpp / launch.cpp.
+//
+// Each kernel moves (token, head) rows whole with 16-byte vector accesses
+// (8/4/2 bytes when a row or a pointer is not 16-byte aligned) and never
+// interprets values.  A lane first issues all of its VPT loads, then its
+// stores, with no branch in between, so the loads of a wave overlap.
+//
+// Every access is a raw buffer instruction through a descriptor that covers
+// only what is left of the buffer being accessed: an index error can at worst
+// read zeros or drop a store; it cannot reach memory outside the caller's
+// buffers.  Lanes past a ragged tile edge use an offset outside the
+// descriptor, so they need no branch either.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#define BASP_HD __host__ __device__
+#include "launch.hpp"
+#include "plan_internal.hpp"
+
+namespace basp {
+namespace {
+
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer descriptor word 3: raw access, 32-bit format
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int VW> struct Vec;
+template <> struct Vec<16> { typedef u32x4 type; };
+template <> struct Vec<8> { typedef u32x2 type; };
+template <> struct Vec<4> { typedef uint32_t type; };
+template <> struct Vec<2> { typedef uint16_t type; };
+
+// Cache-policy bits of gfx940-family memory instructions: bit 1 is NT
+// (non-temporal: the line is not expected to be reused).
+constexpr int kNT = 2;
+template <int POL> struct Policy;
+template <> struct Policy<1> { static constexpr int load = 0, store = 0; };
+template <> struct Policy<2> { static constexpr int load = 0, store = kNT; };
+template <> struct Policy<3> { static constexpr int load = kNT, store = kNT; };
+
+// Bytes of a buffer of `bytes` bytes from offset `off` on (0 past the end).
+__device__ inline uint64_t rest(uint64_t bytes, uint64_t off) { return off < bytes ? bytes - off : 0; }
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(uint64_t base, uint64_t bytes)
+{
+    const uint32_t n = static_cast<uint32_t>(bytes > kI31Max ? kI31Max : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(base), 0,
+                                             static_cast<int>(n), kRsrcWord3);
+}
+
+template <int VW, int AUX>
+__device__ inline typename Vec<VW>::type vload(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    if constexpr (VW == 16)
+        return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+    else if constexpr (VW == 8)
+        return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
+    else if constexpr (VW == 4)
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
+    else
+        return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, AUX);
+}
+
+template <int VW, int AUX>
+__device__ inline void vstore(__amdgpu_buffer_rsrc_t r, uint32_t off, typename Vec<VW>::type x)
+{
+    if constexpr (VW == 16)
+        __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, AUX);
+    else if constexpr (VW == 8)
+        __builtin_amdgcn_raw_buffer_store_b64(x, r, off, 0, AUX);
+    else if constexpr (VW == 4)
+        __builtin_amdgcn_raw_buffer_store_b32(x, r, off, 0, AUX);
+    else
+        __builtin_amdgcn_raw_buffer_store_b16(x, r, off, 0, AUX);
+}
+
+// Fused re-layout of up to three tensors: S2H reads the sequence-sharded
+// side and writes the head-sharded side, !S2H the reverse.
+template <int VW, int VPT, int POL, bool S2H>
+__global__ __launch_bounds__(kBlock) void tile_kernel(const TileDesc D)
+{
+    using V = typename Vec<VW>::type;
+    for (uint32_t tile = blockIdx.x; tile < D.ntiles; tile += gridDim.x) {
+        const TileOrigin o = tile_origin(D, tile);
+        const TileSeg &sg = D.seg[o.seg];
+        const __amdgpu_buffer_rsrc_t rseq = make_rsrc(sg.seq + o.seq_off, rest(sg.seq_bytes, o.seq_off));
+        const __amdgpu_buffer_rsrc_t rhead =
+            make_rsrc(sg.head + o.head_off, rest(sg.head_bytes, o.head_off));
+        const uint32_t nvec = sg.Ts * sg.Th * D.A.d;
+        for (uint32_t v0 = 0; v0 < nvec; v0 += kBlock * VPT) {
+            uint32_t src[VPT], dst[VPT];
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                uint32_t so, ho;
+                const bool ok = lane_offsets(D, sg, o.ns, o.nh, v0 + threadIdx.x + k * kBlock, VW, so, ho);
+                src[k] = ok ? (S2H ? so : ho) : kOutside;
+                dst[k] = ok ? (S2H ? ho : so) : kOutside;
+            }
+            V buf[VPT];
+#pragma unroll
+            for (int k = 0; k < VPT; ++k)
+                buf[k] = vload<VW, Policy<POL>::load>(S2H ? rseq : rhead, src[k]);
+#pragma unroll
+            for (int k = 0; k < VPT; ++k)
+                vstore<VW, Policy<POL>::store>(S2H ? rhead : rseq, dst[k], buf[k]);
+        }
+    }
+}
+
+// One pass of the unfused baseline: linear destination, permuted source.
+template <int VW>
+__global__ __launch_bounds__(kBlock) void perm_kernel(const PermDesc D)
+{
+    using V = typename Vec<VW>::type;
+    for (uint32_t chunk = blockIdx.x; chunk < D.nchunks; chunk += gridDim.x) {
+        const PermSeg &sg = D.seg[perm_segment(D, chunk)];
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(sg.src, sg.src_bytes);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(sg.dst, sg.dst_bytes);
+        const uint32_t base = (chunk - sg.chunk_begin) * (kBlock * kPermVpt);
+        uint32_t src[kPermVpt], dst[kPermVpt];
+#pragma unroll
+        for (int k = 0; k < kPermVpt; ++k) {
+            const uint32_t v = base + threadIdx.x + k * kBlock;
+            const bool ok = v < sg.nvec;
+            src[k] = ok ? perm_source(D, sg, v, VW) : kOutside;
+            dst[k] = ok ? v * VW : kOutside;
+        }
+        V buf[kPermVpt];
+#pragma unroll
+        for (int k = 0; k < kPermVpt; ++k)
+            buf[k] = vload<VW, 0>(rs, src[k]);
+#pragma unroll
+        for (int k = 0; k < kPermVpt; ++k)
+            vstore<VW, kNT>(rd, dst[k], buf[k]);
+    }
+}
+
+typedef void (*TileFn)(const TileDesc);
+
+template <int VW, int VPT, int POL>
+TileFn tile_fn_dir(bool s2h)
+{
+    return s2h ? tile_kernel<VW, VPT, POL, true> : tile_kernel<VW, VPT, POL, false>;
+}
+
+template <int VW, int VPT>
+TileFn tile_fn_pol(int pol, bool s2h)
+{
+    switch (pol) {
+    case 1: return tile_fn_dir<VW, VPT, 1>(s2h);
+    case 3: return tile_fn_dir<VW, VPT, 3>(s2h);
+    default: return tile_fn_dir<VW, VPT, 2>(s2h);
+    }
+}
+
+template <int VW>
+TileFn tile_fn_vpt(int vpt, int pol, bool s2h)
+{
+    switch (vpt) {
+    case 1: return tile_fn_pol<VW, 1>(pol, s2h);
+    case 2: return tile_fn_pol<VW, 2>(pol, s2h);
+    case 8: return tile_fn_pol<VW, 8>(pol, s2h);
+    default: return tile_fn_pol<VW, 4>(pol, s2h);
+    }
+}
+
+TileFn tile_fn(int vw, int vpt, int pol, bool s2h)
+{
+    switch (vw) {
+    case 16: return tile_fn_vpt<16>(vpt, pol, s2h);
+    case 8: return tile_fn_vpt<8>(vpt, pol, s2h);
+    case 4: return tile_fn_vpt<4>(vpt, pol, s2h);
+    default: return tile_fn_vpt<2>(vpt, pol, s2h);
+    }
+}
+
+basp_status launch(const TileLaunch &L, void *stream)
+{
+    if (L.grid == 0)
+        return BASP_OK;
+    hipLaunchKernelGGL(tile_fn(L.vw, L.vpt, L.policy, L.s2h), dim3(L.grid), dim3(kBlock), 0,
+                       static_cast<hipStream_t>(stream), L.D);
+    return hipGetLastError() == hipSuccess ? BASP_OK : BASP_ERR_HIP;
+}
+
+basp_status launch(const PermLaunch &L, void *stream)
+{
+    if (L.grid == 0)
+        return BASP_OK;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (L.vw) {
+    case 16: hipLaunchKernelGGL(perm_kernel<16>, dim3(L.grid), dim3(kBlock), 0, st, L.D); break;
+    case 8: hipLaunchKernelGGL(perm_kernel<8>, dim3(L.grid), dim3(kBlock), 0, st, L.D); break;
+    case 4: hipLaunchKernelGGL(perm_kernel<4>, dim3(L.grid), dim3(kBlock), 0, st, L.D); break;
+    default: hipLaunchKernelGGL(perm_kernel<2>, dim3(L.grid), dim3(kBlock), 0, st, L.D); break;
+    }
+    return hipGetLastError() == hipSuccess ? BASP_OK : BASP_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace basp
+
+using basp::record;
+
+extern "C" basp_status basp_seq_to_head(const basp_plan *p, const void *q, const void *k,
+                                        const void *v, void *out, void *stream)
+{
+    if (!p)
+        return record(BASP_ERR_INVALID);
+    basp::TileLaunch L;
+    const int s = basp::prepare_seq_to_head(*p, q, k, v, out, L);
+    return record(s != BASP_OK ? basp_status(s) : basp::launch(L, stream));
+}
+
+extern "C" basp_status basp_head_to_seq(const basp_plan *p, const void *o, void *out, void *stream)
+{
+    if (!p)
+        return record(BASP_ERR_INVALID);
+    basp::TileLaunch L;
+    const int s = basp::prepare_head_to_seq(*p, o, out, L);
+    return record(s != BASP_OK ? basp_status(s) : basp::launch(L, stream));
+}
+
+extern "C" basp_status basp_seq_to_head_o(const basp_plan *p, const void *dout, void *out,
+                                          void *stream)
+{
+    if (!p)
+        return record(BASP_ERR_INVALID);
+    basp::TileLaunch L;
+    const int s = basp::prepare_seq_to_head_o(*p, dout, out, L);
+    return record(s != BASP_OK ? basp_status(s) : basp::launch(L, stream));
+}
+
+extern "C" basp_status basp_head_to_seq_qkv(const basp_plan *p, const void *in, void *dq,
+                                            void *dk, void *dv, void *stream)
+{
+    if (!p)
+        return record(BASP_ERR_INVALID);
+    basp::TileLaunch L;
+    const int s = basp::prepare_head_to_seq_qkv(*p, in, dq, dk, dv, L);
+    return record(s != BASP_OK ? basp_status(s) : basp::launch(L, stream));
+}
+
+extern "C" size_t basp_unfused_workspace_bytes(const basp_plan *p)
+{
+    if (!p)
+        return 0;
+    // packed and exchanged copies of all three tensors
+    return size_t(2) * uint64_t(p->q_elems + 2 * p->kv_elems) * p->es;
+}
+
+extern "C" basp_status basp_seq_to_head_unfused(const basp_plan *p, const void *q, const void *k,
+                                                const void *v, void *out, void *ws, void *stream)
+{
+    if (!p)
+        return record(BASP_ERR_INVALID);
+    basp::PermLaunch L[3];
+    int s = basp::prepare_seq_to_head_unfused(*p, q, k, v, out, ws, L);
+    for (int i = 0; i < 3 && s == BASP_OK; ++i)
+        s = basp::launch(L[i], stream);
+    return record(basp_status(s));
+}

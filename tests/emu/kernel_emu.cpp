@@ -1,0 +1,140 @@
+// CPU emulation of libbasp's kernels, for tests without a GPU.
+//
+// It compiles the library's own launch planning (launch.cpp), plan code
+// (plan.cpp) and per-lane index arithmetic (launch.hpp) with g++, then runs
+// every launch on the host: each work-group's tile loop, each lane's vector
+// offsets, and each vector access as a memcpy under the rule of the raw
+// buffer descriptors (an access is performed only when it lies inside the
+// descriptor's range).  A lane that the kernel treats as present but whose
+// access falls outside its descriptor is counted in *bad: a correct plan
+// never has one.
+#include <cstdint>
+#include <cstring>
+
+#include "launch.hpp"
+#include "plan_internal.hpp"
+
+using namespace basp;
+
+namespace {
+
+uint64_t rest(uint64_t bytes, uint64_t off) { return off < bytes ? bytes - off : 0; }
+uint64_t range(uint64_t bytes) { return bytes > kI31Max ? kI31Max : bytes; }
+bool inside(uint32_t off, uint32_t vw, uint64_t n) { return uint64_t(off) + vw <= n; }
+
+void copy(uint64_t dst, uint64_t src, uint32_t vw)
+{
+    std::memcpy(reinterpret_cast<void *>(dst), reinterpret_cast<const void *>(src), vw);
+}
+
+void run(const TileLaunch &L, uint64_t *bad)
+{
+    const TileDesc &D = L.D;
+    for (uint32_t block = 0; block < L.grid; ++block) {
+        for (uint32_t tile = block; tile < D.ntiles; tile += L.grid) {
+            const TileOrigin o = tile_origin(D, tile);
+            const TileSeg &sg = D.seg[o.seg];
+            const uint64_t seq = sg.seq + o.seq_off, head = sg.head + o.head_off;
+            const uint64_t nseq = range(rest(sg.seq_bytes, o.seq_off));
+            const uint64_t nhead = range(rest(sg.head_bytes, o.head_off));
+            const uint32_t nvec = sg.Ts * sg.Th * D.A.d;
+            const uint32_t step = kBlock * L.vpt;
+            const uint32_t vend = (nvec + step - 1) / step * step;
+            for (uint32_t v = 0; v < vend; ++v) {
+                uint32_t so, ho;
+                if (!lane_offsets(D, sg, o.ns, o.nh, v, L.vw, so, ho))
+                    continue;
+                if (!inside(so, L.vw, nseq) || !inside(ho, L.vw, nhead)) {
+                    ++*bad;
+                    continue;
+                }
+                if (L.s2h)
+                    copy(head + ho, seq + so, L.vw);
+                else
+                    copy(seq + so, head + ho, L.vw);
+            }
+        }
+    }
+}
+
+void run(const PermLaunch &L, uint64_t *bad)
+{
+    const PermDesc &D = L.D;
+    for (uint32_t block = 0; block < L.grid; ++block) {
+        for (uint32_t chunk = block; chunk < D.nchunks; chunk += L.grid) {
+            const PermSeg &sg = D.seg[perm_segment(D, chunk)];
+            const uint32_t base = (chunk - sg.chunk_begin) * (kBlock * kPermVpt);
+            for (uint32_t i = 0; i < uint32_t(kBlock * kPermVpt); ++i) {
+                const uint32_t v = base + i;
+                if (v >= sg.nvec)
+                    continue;
+                const uint32_t src = perm_source(D, sg, v, L.vw), dst = v * L.vw;
+                if (!inside(src, L.vw, range(sg.src_bytes)) || !inside(dst, L.vw, range(sg.dst_bytes))) {
+                    ++*bad;
+                    continue;
+                }
+                copy(sg.dst + dst, sg.src + src, L.vw);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int emu_seq_to_head(const basp_plan *p, const void *q, const void *k, const void *v, void *out,
+                    uint64_t *bad, int *vw)
+{
+    TileLaunch L;
+    const int s = prepare_seq_to_head(*p, q, k, v, out, L);
+    *vw = L.vw;
+    if (s == BASP_OK)
+        run(L, bad);
+    return s;
+}
+
+int emu_head_to_seq(const basp_plan *p, const void *o, void *out, uint64_t *bad, int *vw)
+{
+    TileLaunch L;
+    const int s = prepare_head_to_seq(*p, o, out, L);
+    *vw = L.vw;
+    if (s == BASP_OK)
+        run(L, bad);
+    return s;
+}
+
+int emu_seq_to_head_o(const basp_plan *p, const void *dout, void *out, uint64_t *bad, int *vw)
+{
+    TileLaunch L;
+    const int s = prepare_seq_to_head_o(*p, dout, out, L);
+    *vw = L.vw;
+    if (s == BASP_OK)
+        run(L, bad);
+    return s;
+}
+
+int emu_head_to_seq_qkv(const basp_plan *p, const void *in, void *dq, void *dk, void *dv,
+                        uint64_t *bad, int *vw)
+{
+    TileLaunch L;
+    const int s = prepare_head_to_seq_qkv(*p, in, dq, dk, dv, L);
+    *vw = L.vw;
+    if (s == BASP_OK)
+        run(L, bad);
+    return s;
+}
+
+int emu_seq_to_head_unfused(const basp_plan *p, const void *q, const void *k, const void *v,
+                            void *out, void *ws, uint64_t *bad, int *vw)
+{
+    PermLaunch L[3];
+    const int s = prepare_seq_to_head_unfused(*p, q, k, v, out, ws, L);
+    *vw = L[0].vw;
+    if (s == BASP_OK)
+        for (int i = 0; i < 3; ++i)
+            run(L[i], bad);
+    return s;
+}
+
+}  // extern "C"

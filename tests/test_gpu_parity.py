@@ -1,0 +1,338 @@
+"""GPU parity: every entry point of libbasp against the CPU oracle, bit for
+bit, on the same seeded bytes (MI355X only).
+
+Coverage:
+* every named workload at full size, both modes, seq->head (fused Q/K/V) and
+  head->seq (O), compared element by element with the oracle;
+* ragged shapes spanning several tiles with partial tiles at the end, odd row
+  sizes (narrow vector paths), several launch shapes (tuning) and a capped
+  grid (work-groups looping over tiles);
+* edge cases: empty sequences, B = 1, K = 1, the data-parallel fallback
+  (B > N), N = 1, unaligned (2-byte) views, all bf16 bit patterns;
+* guard bands around the output and a sentinel fill (each destination written
+  exactly once, nothing outside written);
+* the backward entry points, the token-major layout and the unfused baseline.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sequence_re_layout_amd import inputs, workloads
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from sequence_re_layout_amd import binding as b
+else:  # collected off the GPU machine: every test here is skipped
+    b = None
+
+MODE = {"basp": 1, "ulysses": 0}
+GUARD = 4096  # bytes of canary on each side of an output
+
+
+def needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def bits(t):
+    return inputs.raw_bits(t.cpu())
+
+
+def seq_inputs(B, S, Hq, Hkv, d, dtype):
+    """Q, K, V as flat CPU tensors: N(0,1) bf16 from seeds 0/1/2, or int32 tags
+    numbering the three tensors consecutively."""
+    nq, nkv = B * S * Hq * d, B * S * Hkv * d
+    if dtype == "int32":
+        return (inputs.tags_int32(nq, 0), inputs.tags_int32(nkv, nq), inputs.tags_int32(nkv, nq + nkv))
+    return (inputs.normal_bf16(nq, inputs.SEED_Q), inputs.normal_bf16(nkv, inputs.SEED_K),
+            inputs.normal_bf16(nkv, inputs.SEED_V))
+
+
+def guarded(numel, dtype):
+    """Device buffer with GUARD bytes of canary on both sides; returns
+    (whole, view).  The view is sentinel-filled: all-ones bits, a NaN for
+    bf16 that N(0,1) never produces and -1 for int32, which tags never are."""
+    es = torch.tensor([], dtype=dtype).element_size()
+    g = GUARD // es
+    whole = torch.empty(numel + 2 * g, dtype=dtype, device="cuda")
+    raw = whole.view(torch.int16 if es == 2 else torch.int32)
+    raw.fill_(-1)
+    raw[:g] = 0x5A5A
+    raw[g + numel:] = 0x5A5A
+    return whole, whole[g:g + numel]
+
+
+def check_guards(whole, numel):
+    es = whole.element_size()
+    g = GUARD // es
+    raw = bits(whole)
+    assert np.all(raw[:g] == 0x5A5A) and np.all(raw[g + numel:] == 0x5A5A), "guard band written"
+    body = raw[g:g + numel]
+    assert not np.any(body == np.iinfo(body.dtype).max), "a destination was never written"
+
+
+TDT = {"bf16": (torch.bfloat16, 0), "int32": (torch.int32, 3), "fp16": (torch.float16, 1),
+       "fp32": (torch.float32, 2)}
+
+
+def run_s2h(shape, mode, dtype="bf16", layout=0, tuning=None, cpu=None):
+    """Fused seq->head on the GPU and in the oracle; asserts bit equality."""
+    N, B, S, Hq, Hkv, d = shape
+    tdt, code = TDT[dtype]
+    plan = b.basp_plan_create_ex(N, B, S, Hq, Hkv, d, code, MODE[mode], layout)
+    if tuning:
+        b.basp_plan_set_tuning(plan, **tuning)
+    q, k, v = cpu or seq_inputs(B, S, Hq, Hkv, d, "int32" if dtype == "int32" else "bf16")
+    q, k, v = (x.view(tdt) if x.element_size() == tdt.itemsize else x.to(tdt) for x in (q, k, v))
+    whole, out = guarded(plan.info["qkv_elems"], tdt)
+    b.basp_seq_to_head(plan, q.cuda(), k.cuda(), v.cuda(), out)
+    torch.cuda.synchronize()
+    check_guards(whole, plan.info["qkv_elems"])
+    want = oracle.seq_to_head_qkv(inputs.raw_bits(q), inputs.raw_bits(k), inputs.raw_bits(v),
+                                  MODE[mode], N, B, S, Hq, Hkv, d, layout)
+    got = bits(out)
+    assert got.shape == want.shape
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, "first mismatches at %s" % bad[:8]
+    return plan, out
+
+
+def run_h2s(shape, mode, dtype="bf16", layout=0, tuning=None):
+    N, B, S, Hq, Hkv, d = shape
+    tdt, code = TDT[dtype]
+    plan = b.basp_plan_create_ex(N, B, S, Hq, Hkv, d, code, MODE[mode], layout)
+    if tuning:
+        b.basp_plan_set_tuning(plan, **tuning)
+    nq = plan.info["q_elems"]
+    o = inputs.tags_int32(nq) if dtype == "int32" else inputs.normal_bf16(nq, inputs.SEED_O)
+    o = o.view(tdt) if o.element_size() == tdt.itemsize else o.to(tdt)
+    whole, out = guarded(nq, tdt)
+    b.basp_head_to_seq(plan, o.cuda(), out)
+    torch.cuda.synchronize()
+    check_guards(whole, nq)
+    want = oracle.head_to_seq(inputs.raw_bits(o), MODE[mode], N, B, S, Hq, d, layout)
+    bad = np.flatnonzero(bits(out) != want)
+    assert bad.size == 0, "first mismatches at %s" % bad[:8]
+
+
+# ------------------------------------------------------- named workloads ---
+
+@pytest.mark.parametrize("mode", ["basp", "ulysses"])
+@pytest.mark.parametrize("w", workloads.ALL, ids=[w[0] for w in workloads.ALL])
+def test_workload_full_size(w, mode):
+    needs_gpu()
+    print("workload", w, mode, flush=True)
+    shape = w[1:]
+    run_s2h(shape, mode)
+    run_h2s(shape, mode)
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode", ["basp", "ulysses"])
+def test_tiny_int32_tagged(mode):
+    needs_gpu()
+    shape = workloads.TINY[1:]
+    run_s2h(shape, mode, dtype="int32")
+    run_h2s(shape, mode, dtype="int32")
+
+
+# -------------------------------------------------- ragged, tunings, dtypes --
+
+RAGGED = [  # N, B, S, Hq, Hkv, d
+    (6, 3, 6 * 37, 12, 6, 40),     # St = 37 tokens, 80-byte rows (5 vectors)
+    (4, 2, 4 * 203, 8, 4, 64),     # St = 203 > one tile
+    (8, 2, 8 * 129, 24, 8, 128),   # Hl_q = 6 (BASP) / 3 (Ulysses)
+    (3, 3, 3 * 11, 6, 3, 3),       # 6-byte rows: 2-byte vectors
+    (2, 4, 2 * 50, 4, 2, 12),      # 24-byte rows: 8-byte vectors
+]
+
+
+@pytest.mark.parametrize("mode", ["basp", "ulysses"])
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
+def test_ragged(shape, mode):
+    needs_gpu()
+    for dtype in ("bf16", "int32"):
+        for layout in (0, 1):
+            run_s2h(shape, mode, dtype, layout)
+            run_h2s(shape, mode, dtype, layout)
+
+
+TUNINGS = [dict(vectors_per_thread=1), dict(vectors_per_thread=2), dict(vectors_per_thread=8),
+           dict(tile_tokens=1), dict(tile_tokens=3, tile_heads=2), dict(tile_tokens=100, tile_heads=3),
+           dict(cache_policy=1), dict(cache_policy=3), dict(max_grid=7),
+           dict(vectors_per_thread=8, tile_tokens=5, tile_heads=1, cache_policy=3, max_grid=3)]
+
+
+@pytest.mark.parametrize("tuning", TUNINGS, ids=lambda t: ",".join("%s=%s" % kv for kv in t.items()))
+def test_tunings(tuning):
+    needs_gpu()
+    for shape, mode in (((8, 2, 8 * 129, 24, 8, 128), "basp"), ((6, 3, 6 * 37, 12, 6, 40), "ulysses")):
+        for layout in (0, 1):
+            run_s2h(shape, mode, "int32", layout, tuning)
+            run_h2s(shape, mode, "int32", layout, tuning)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "fp32"])
+def test_other_dtypes(dtype):
+    needs_gpu()
+    run_s2h((4, 2, 4 * 33, 8, 4, 64), "basp", dtype)
+    run_h2s((4, 2, 4 * 33, 8, 4, 64), "ulysses", dtype)
+
+
+# ------------------------------------------------------------- edge cases --
+
+def test_empty_sequence():
+    needs_gpu()
+    plan = b.basp_plan_create(8, 2, 0, 32, 8, 64)
+    z = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+    b.basp_seq_to_head(plan, z, z, z, z)
+    b.basp_head_to_seq(plan, z, z)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("shape,mode", [
+    ((8, 1, 8 * 16, 8, 8, 64), "basp"),       # B = 1: one group of N
+    ((8, 8, 8 * 16, 8, 8, 64), "basp"),       # K = 1: purely local
+    ((4, 16, 32, 8, 4, 64), "basp"),          # B > N: data-parallel fallback
+    ((1, 3, 40, 4, 2, 64), "ulysses"),        # one rank
+    ((1, 3, 40, 4, 2, 64), "basp"),
+    ((8, 3, 8 * 5, 8, 8, 64), "ulysses"),     # Ulysses needs no N % B
+])
+def test_degenerate(shape, mode):
+    needs_gpu()
+    for layout in (0, 1):
+        run_s2h(shape, mode, "int32", layout)
+        run_h2s(shape, mode, "int32", layout)
+
+
+def test_b1_basp_equals_ulysses():
+    needs_gpu()
+    shape = (8, 1, 8192, 32, 8, 64)
+    _, a = run_s2h(shape, "basp")
+    _, u = run_s2h(shape, "ulysses")
+    assert torch.equal(a.view(torch.int16), u.view(torch.int16))
+
+
+def test_unaligned_views():
+    """Tensors that start 2 bytes past a 16-byte boundary take the narrow
+    vector path and give the same bits."""
+    needs_gpu()
+    N, B, S, Hq, Hkv, d = 4, 2, 4 * 20, 8, 4, 64
+    plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, 1)
+    q, k, v = seq_inputs(B, S, Hq, Hkv, d, "bf16")
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+        buf[1:].copy_(t.cuda())
+        return buf[1:]
+    out_buf = torch.empty(plan.info["qkv_elems"] + 1, dtype=torch.bfloat16, device="cuda")
+    out = out_buf[1:]
+    b.basp_seq_to_head(plan, shifted(q), shifted(k), shifted(v), out)
+    torch.cuda.synchronize()
+    want = oracle.seq_to_head_qkv(inputs.raw_bits(q), inputs.raw_bits(k), inputs.raw_bits(v),
+                                  1, N, B, S, Hq, Hkv, d)
+    assert np.array_equal(bits(out), want)
+
+
+def test_all_bf16_patterns_round_trip():
+    needs_gpu()
+    pats = inputs.all_bf16_patterns()
+    N, B, S, H, d = 4, 2, 16, 16, 128   # B*S*H*d = 65536
+    for mode in (0, 1):
+        plan = b.basp_plan_create(N, B, S, H, H, d, b.BASP_BF16, mode)
+        x = pats.cuda()
+        out = torch.empty(3 * x.numel(), dtype=torch.bfloat16, device="cuda")
+        b.basp_seq_to_head(plan, x, x, x, out)
+        back = torch.empty_like(x)
+        b.basp_head_to_seq(plan, out[:x.numel()], back)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(back), inputs.raw_bits(pats))
+        want = oracle.seq_to_head(inputs.raw_bits(pats), mode, N, B, S, H, d)
+        assert np.array_equal(bits(out[2 * x.numel():]), want)
+
+
+def test_device_round_trip():
+    needs_gpu()
+    N, B, S, Hq, Hkv, d = workloads.LLAMA_1B[1:]
+    for mode in (0, 1):
+        plan = b.basp_plan_create(N, B, S, Hq, Hq, d, b.BASP_BF16, mode)  # Hkv := Hq
+        q = inputs.normal_bf16(plan.info["q_elems"], 11).cuda()
+        out = torch.empty(plan.info["qkv_elems"], dtype=torch.bfloat16, device="cuda")
+        b.basp_seq_to_head(plan, q, q, q, out)
+        back = torch.empty_like(q)
+        b.basp_head_to_seq(plan, out[plan.info["qkv_offset_v"]:], back)
+        torch.cuda.synchronize()
+        assert torch.equal(back.view(torch.int16), q.view(torch.int16))
+
+
+# ----------------------------------------- backward, layout, unfused paths --
+
+@pytest.mark.parametrize("mode", ["basp", "ulysses"])
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("shape", [workloads.LLAMA_1B[1:], (6, 3, 6 * 37, 12, 6, 40)],
+                         ids=["llama1b", "ragged"])
+def test_backward_entries(shape, layout, mode):
+    needs_gpu()
+    N, B, S, Hq, Hkv, d = shape
+    m = MODE[mode]
+    plan = b.basp_plan_create_ex(N, B, S, Hq, Hkv, d, b.BASP_BF16, m, layout)
+    i = plan.info
+    # dO: seq -> head
+    do = inputs.normal_bf16(i["q_elems"], 21)
+    out = torch.empty(i["q_elems"], dtype=torch.bfloat16, device="cuda")
+    b.basp_seq_to_head_o(plan, do.cuda(), out)
+    # fused dQ/dK/dV: head -> seq
+    g = inputs.normal_bf16(i["qkv_elems"], 22)
+    dq = torch.empty(i["q_elems"], dtype=torch.bfloat16, device="cuda")
+    dk = torch.empty(i["kv_elems"], dtype=torch.bfloat16, device="cuda")
+    dv = torch.empty(i["kv_elems"], dtype=torch.bfloat16, device="cuda")
+    b.basp_head_to_seq_qkv(plan, g.cuda(), dq, dk, dv)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), oracle.seq_to_head(inputs.raw_bits(do), m, N, B, S, Hq, d, layout))
+    wq, wk, wv = oracle.head_to_seq_qkv(inputs.raw_bits(g), m, N, B, S, Hq, Hkv, d, layout)
+    assert np.array_equal(bits(dq), wq) and np.array_equal(bits(dk), wk) and np.array_equal(bits(dv), wv)
+
+
+@pytest.mark.parametrize("mode", ["basp", "ulysses"])
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("shape", [workloads.LLAMA_1B[1:], workloads.QWEN_1_8B[1:],
+                                   (6, 3, 6 * 37, 12, 6, 40), (3, 3, 3 * 11, 6, 3, 3)],
+                         ids=["llama1b", "qwen", "ragged", "narrow"])
+def test_unfused_matches_oracle(shape, layout, mode):
+    needs_gpu()
+    N, B, S, Hq, Hkv, d = shape
+    m = MODE[mode]
+    plan = b.basp_plan_create_ex(N, B, S, Hq, Hkv, d, b.BASP_BF16, m, layout)
+    q, k, v = seq_inputs(B, S, Hq, Hkv, d, "bf16")
+    ws = torch.empty(b.basp_unfused_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
+    whole, out = guarded(plan.info["qkv_elems"], torch.bfloat16)
+    b.basp_seq_to_head_unfused(plan, q.cuda(), k.cuda(), v.cuda(), out, ws)
+    torch.cuda.synchronize()
+    check_guards(whole, plan.info["qkv_elems"])
+    want = oracle.seq_to_head_qkv(inputs.raw_bits(q), inputs.raw_bits(k), inputs.raw_bits(v),
+                                  m, N, B, S, Hq, Hkv, d, layout)
+    assert np.array_equal(bits(out), want)
+
+
+# ------------------------------------------------------------ error paths --
+
+def test_device_error_paths():
+    needs_gpu()
+    plan = b.basp_plan_create(4, 2, 64, 8, 8, 64)
+    i = plan.info
+    q = torch.zeros(i["q_elems"], dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros(i["qkv_elems"], dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(b.BaspError) as e:
+        b.basp_seq_to_head(plan, q, q, q, out.data_ptr() + 1)
+    assert e.value.status == b.BASP_ERR_ALIGN
+    with pytest.raises(b.BaspError) as e:
+        b.basp_seq_to_head(plan, q, q, q, q.data_ptr())
+    assert e.value.status == b.BASP_ERR_ALIAS
+    with pytest.raises(TypeError):
+        b.basp_seq_to_head(plan, q.float(), q, q, out)
+    with pytest.raises(ValueError):
+        b.basp_seq_to_head(plan, q[:-1], q, q, out)
+    # q, k and v may share one buffer
+    b.basp_seq_to_head(plan, q, q, q, out)
+    torch.cuda.synchronize()

@@ -1,0 +1,210 @@
+"""The kernels' index arithmetic and the library's launch planning, run on the
+CPU and compared with the oracle (no GPU).
+
+``tests/emu/kernel_emu.cpp`` compiles the library's own plan.cpp, launch.cpp
+and launch.hpp with g++ and executes every launch on the host (see its
+header).  These tests drive it over ragged shapes, all launch shapes, both
+layouts, both element sizes, narrow vector widths (misaligned pointers) and
+the degenerate cases, and require (a) the oracle's result bit for bit, with
+every destination written, and (b) no in-tile access outside the kernels'
+buffer descriptors.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from sequence_re_layout_amd import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "sequence_re_layout_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def emu(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("emu") / "libbasp_emu.so")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-DBASP_HD=",
+                    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+                    os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "launch.cpp"),
+                    os.path.join(ROOT, "tests", "emu", "kernel_emu.cpp"), "-o", out], check=True)
+    lib = ctypes.CDLL(out)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.basp_plan_create_ex.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32]
+    lib.basp_plan_create_ex.restype = vp
+    lib.basp_plan_destroy.argtypes = [vp]
+    lib.basp_plan_set_tuning.argtypes = [vp, ctypes.POINTER(ctypes.c_int32 * 5)]
+    lib.basp_plan_set_tuning.restype = i32
+    tail = [ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_int)]
+    lib.emu_seq_to_head.argtypes = [vp, vp, vp, vp, vp] + tail
+    lib.emu_head_to_seq.argtypes = [vp, vp, vp] + tail
+    lib.emu_seq_to_head_o.argtypes = [vp, vp, vp] + tail
+    lib.emu_head_to_seq_qkv.argtypes = [vp, vp, vp, vp, vp] + tail
+    lib.emu_seq_to_head_unfused.argtypes = [vp, vp, vp, vp, vp, vp] + tail
+    return lib
+
+
+class Run:
+    """One emulated call: checks status, the descriptor bound count and
+    records the vector width used."""
+
+    def __init__(self, lib, shape, mode, layout, es, tuning=None):
+        N, B, S, Hq, Hkv, d = shape
+        self.lib = lib
+        dtype = {2: 0, 4: 3}[es]
+        self.plan = lib.basp_plan_create_ex(N, B, S, Hq, Hkv, d, dtype, mode, layout)
+        assert self.plan, "plan rejected"
+        if tuning:
+            t = (ctypes.c_int32 * 5)(*[tuning.get(k, 0) for k in (
+                "vectors_per_thread", "tile_tokens", "tile_heads", "cache_policy", "max_grid")])
+            assert lib.basp_plan_set_tuning(self.plan, ctypes.byref(t)) == 0
+
+    def __call__(self, fn, *arrays):
+        bad, vw = ctypes.c_uint64(0), ctypes.c_int(0)
+        ptrs = [a.ctypes.data if a is not None else None for a in arrays]
+        st = getattr(self.lib, fn)(self.plan, *ptrs, ctypes.byref(bad), ctypes.byref(vw))
+        assert st == 0, "%s returned status %d" % (fn, st)
+        assert bad.value == 0, "%d accesses outside a descriptor" % bad.value
+        return vw.value
+
+    def __del__(self):
+        self.lib.basp_plan_destroy(self.plan)
+
+
+def _rand(n, es, rng):
+    dt = np.uint16 if es == 2 else np.uint32
+    # values below the all-ones sentinel, so an unwritten destination shows
+    return rng.integers(0, np.iinfo(dt).max, size=n, dtype=dt)
+
+
+def _empty(n, es, offset=0):
+    """Sentinel-filled array whose data pointer sits `offset` elements past an
+    allocation start (a misaligned view when offset > 0)."""
+    dt = np.uint16 if es == 2 else np.uint32
+    buf = np.full(n + offset + 8, np.iinfo(dt).max, dtype=dt)
+    return buf[offset:offset + n]
+
+
+def _shifted(a, offset):
+    b = _empty(a.size, a.itemsize, offset)
+    b[:] = a
+    return b
+
+
+def check_s2h(emu, shape, mode, layout, es, tuning=None, offset=0, seed=0):
+    N, B, S, Hq, Hkv, d = shape
+    rng = np.random.default_rng(seed)
+    q, k, v = (_rand(B * S * H * d, es, rng) for H in (Hq, Hkv, Hkv))
+    run = Run(emu, shape, mode, layout, es, tuning)
+    out = _empty(q.size + 2 * k.size, es, offset)
+    vw = run("emu_seq_to_head", _shifted(q, offset), _shifted(k, offset), _shifted(v, offset), out)
+    want = oracle.seq_to_head_qkv(q, k, v, mode, N, B, S, Hq, Hkv, d, layout)
+    assert np.array_equal(out, want)
+    return vw
+
+
+def check_h2s(emu, shape, mode, layout, es, tuning=None, offset=0, seed=1):
+    N, B, S, Hq, Hkv, d = shape
+    rng = np.random.default_rng(seed)
+    o = _rand(B * S * Hq * d, es, rng)
+    run = Run(emu, shape, mode, layout, es, tuning)
+    out = _empty(o.size, es, offset)
+    vw = run("emu_head_to_seq", _shifted(o, offset), out)
+    assert np.array_equal(out, oracle.head_to_seq(o, mode, N, B, S, Hq, d, layout))
+    return vw
+
+
+RAGGED = [  # N, B, S, Hq, Hkv, d
+    (6, 3, 6 * 37, 12, 6, 40),
+    (4, 2, 4 * 203, 8, 4, 64),
+    (8, 2, 8 * 129, 24, 8, 128),
+    (3, 3, 3 * 11, 6, 3, 3),
+    (2, 4, 2 * 50, 4, 2, 12),
+    (8, 4, 8 * 3, 16, 8, 8),
+]
+
+
+@pytest.mark.parametrize("mode", [1, 0], ids=["basp", "ulysses"])
+@pytest.mark.parametrize("layout", [0, 1], ids=["head_major", "token_major"])
+@pytest.mark.parametrize("es", [2, 4])
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
+def test_ragged(emu, shape, es, layout, mode):
+    check_s2h(emu, shape, mode, layout, es)
+    check_h2s(emu, shape, mode, layout, es)
+
+
+TUNINGS = [dict(vectors_per_thread=1), dict(vectors_per_thread=2), dict(vectors_per_thread=8),
+           dict(tile_tokens=1), dict(tile_tokens=3, tile_heads=2), dict(tile_tokens=100, tile_heads=3),
+           dict(tile_heads=4), dict(max_grid=7), dict(max_grid=1),
+           dict(vectors_per_thread=8, tile_tokens=5, tile_heads=1, cache_policy=3, max_grid=3)]
+
+
+@pytest.mark.parametrize("tuning", TUNINGS, ids=lambda t: ",".join("%s=%s" % kv for kv in t.items()))
+def test_tunings(emu, tuning):
+    for shape, mode in (((8, 2, 8 * 129, 24, 8, 128), 1), ((6, 3, 6 * 37, 12, 6, 40), 0)):
+        for layout in (0, 1):
+            check_s2h(emu, shape, mode, layout, 2, tuning)
+            check_h2s(emu, shape, mode, layout, 4, tuning)
+
+
+@pytest.mark.parametrize("offset,es,expect_vw", [(0, 2, 16), (1, 2, 2), (2, 2, 4), (4, 2, 8),
+                                                  (1, 4, 4), (2, 4, 8)])
+def test_vector_width_follows_alignment(emu, offset, es, expect_vw):
+    shape = (4, 2, 4 * 21, 8, 4, 64)
+    assert check_s2h(emu, shape, 1, 0, es, offset=offset) == expect_vw
+    assert check_h2s(emu, shape, 0, 1, es, offset=offset) == expect_vw
+
+
+@pytest.mark.parametrize("shape,mode", [
+    ((8, 1, 8 * 16, 8, 8, 64), 1), ((8, 8, 8 * 16, 8, 8, 64), 1), ((4, 16, 32, 8, 4, 64), 1),
+    ((1, 3, 40, 4, 2, 64), 0), ((1, 3, 40, 4, 2, 64), 1), ((8, 3, 8 * 5, 8, 8, 64), 0),
+    ((2, 2, 2, 2, 2, 1), 1), ((8, 2, 8, 8, 8, 2), 0),
+])
+def test_degenerate(emu, shape, mode):
+    for layout in (0, 1):
+        for es in (2, 4):
+            check_s2h(emu, shape, mode, layout, es)
+            check_h2s(emu, shape, mode, layout, es)
+
+
+SCALED = [(w[0], w[1], w[2], max(w[3] // 16, w[1]), w[4], w[5], w[6]) for w in workloads.ALL]
+
+
+@pytest.mark.parametrize("mode", [1, 0], ids=["basp", "ulysses"])
+@pytest.mark.parametrize("w", SCALED, ids=[w[0] + "_S/16" for w in SCALED])
+def test_workloads_scaled(emu, w, mode):
+    check_s2h(emu, w[1:], mode, 0, 2)
+    check_h2s(emu, w[1:], mode, 0, 2)
+
+
+@pytest.mark.parametrize("mode", [1, 0], ids=["basp", "ulysses"])
+def test_llama1b_full_size(emu, mode):
+    check_s2h(emu, workloads.LLAMA_1B[1:], mode, 0, 2)
+    check_h2s(emu, workloads.LLAMA_1B[1:], mode, 0, 2)
+
+
+@pytest.mark.parametrize("mode", [1, 0], ids=["basp", "ulysses"])
+@pytest.mark.parametrize("layout", [0, 1], ids=["head_major", "token_major"])
+@pytest.mark.parametrize("shape", [(8, 2, 8 * 16, 32, 8, 64), (6, 3, 6 * 37, 12, 6, 40), (3, 3, 33, 6, 3, 3)],
+                         ids=["llama1b_small", "ragged", "narrow"])
+def test_backward_and_unfused(emu, shape, layout, mode):
+    N, B, S, Hq, Hkv, d = shape
+    rng = np.random.default_rng(9)
+    run = Run(emu, shape, mode, layout, 2)
+    nq, nkv = B * S * Hq * d, B * S * Hkv * d
+    do = _rand(nq, 2, rng)
+    out = _empty(nq, 2)
+    run("emu_seq_to_head_o", do, out)
+    assert np.array_equal(out, oracle.seq_to_head(do, mode, N, B, S, Hq, d, layout))
+    g = _rand(nq + 2 * nkv, 2, rng)
+    dq, dk, dv = _empty(nq, 2), _empty(nkv, 2), _empty(nkv, 2)
+    run("emu_head_to_seq_qkv", g, dq, dk, dv)
+    wq, wk, wv = oracle.head_to_seq_qkv(g, mode, N, B, S, Hq, Hkv, d, layout)
+    assert np.array_equal(dq, wq) and np.array_equal(dk, wk) and np.array_equal(dv, wv)
+    q, k, v = (_rand(n, 2, rng) for n in (nq, nkv, nkv))
+    out = _empty(nq + 2 * nkv, 2)
+    ws = _empty(2 * (nq + 2 * nkv), 2)
+    run("emu_seq_to_head_unfused", q, k, v, out, ws)
+    assert np.array_equal(out, oracle.seq_to_head_qkv(q, k, v, mode, N, B, S, Hq, Hkv, d, layout))
