@@ -1,0 +1,384 @@
+#!/usr/bin/env python3
+"""Benchmark of the BASP attention-boundary re-layout on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--mode basp|ulysses]
+
+One step is one pass of the attention-boundary re-layout of a layer: the
+fused Q/K/V seq->head exchange before attention and the O head->seq exchange
+after it, on the Llama-3.2-1B-shaped workload by default (N = 8 virtual
+ranks, B = 2, S = 16384, Hq = 32, Hkv = 8, d = 64, bf16, BASP mode: 2 groups
+of K = 4).  Inputs are seeded synthetic N(0, 1) bf16 values resident in HBM
+before timing starts; R buffer sets rotate so that no step finds its bytes in
+the 256 MB Infinity Cache.
+
+Printed: one JSON line.  ``value`` is effective HBM GB/s of the whole step
+(algorithmic bytes: every input byte read once, every output byte written
+once) over wall time of K steps bracketed by device synchronisation.
+``roofline`` is the fused seq->head kernel (the larger of the two) against
+the 8 TB/s HBM peak, its duration taken with HIP events on the stream it runs
+on.  ``detail`` holds per-kernel rates of both modes, the unfused three-pass
+baseline and a plain device copy.  ``cpu_baseline`` is the CPU oracle doing
+the same step on the host, repeated for about --cpu-seconds.
+
+    python bench.py --pmc-summary FETCH_DIR WRITE_DIR
+
+reads the CSV output of two ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc
+WRITE_SIZE`` runs of this script and writes ``profiles/pmc_traffic.json``
+(HBM bytes per launch of the fused kernel, scaled by the same counters on a
+plain copy of known size).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("effective HBM GB/s (and % of peak) of fused QKV seq→head re-layout, "
+          "BASP vs Ulysses")
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["sequence_re_layout_amd/csrc/relayout.hip", "sequence_re_layout_amd/csrc/launch.hpp",
+                  "sequence_re_layout_amd/csrc/launch.cpp", "sequence_re_layout_amd/csrc/fastdiv.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+CALIB_BYTES = 256 << 20   # plain copy used to scale the PMC byte counters
+
+
+def kernel_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="llama3.2-1b_s16k_b2")
+    ap.add_argument("--mode", choices=["basp", "ulysses"], default="basp")
+    ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough for > 1 GiB reuse distance)")
+    ap.add_argument("--detail-iters", type=int, default=100)
+    ap.add_argument("--no-detail", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    return ap.parse_args(argv)
+
+
+# ------------------------------------------------------------------ GPU ---
+
+class Workload:
+    """Device buffers of one workload: R rotating sets of Q/K/V/out and
+    O/out, filled from the same seeded host data."""
+
+    def __init__(self, b, name, mode, rotate):
+        import torch
+        from sequence_re_layout_amd import inputs, workloads
+        self.name, N, B, S, Hq, Hkv, d = workloads.BY_NAME[name]
+        self.shape = (N, B, S, Hq, Hkv, d)
+        self.mode = mode
+        code = b.BASP_MODE_BASP if mode == "basp" else b.BASP_MODE_ULYSSES
+        self.plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, code)
+        i = self.plan.info
+        self.s2h_bytes = i["qkv_bytes_moved"]
+        self.h2s_bytes = i["o_bytes_moved"]
+        self.host = {
+            "q": inputs.normal_bf16(i["q_elems"], inputs.SEED_Q),
+            "k": inputs.normal_bf16(i["kv_elems"], inputs.SEED_K),
+            "v": inputs.normal_bf16(i["kv_elems"], inputs.SEED_V),
+            "o": inputs.normal_bf16(i["q_elems"], inputs.SEED_O),
+        }
+        set_bytes = self.s2h_bytes + self.h2s_bytes
+        self.R = rotate or max(2, -(-(3 << 30) // set_bytes))   # > 1 GiB between reuses
+        self.sets = []
+        for _ in range(self.R):
+            s = {n: t.cuda() for n, t in self.host.items()}
+            s["qkv_out"] = torch.empty(i["qkv_elems"], dtype=torch.bfloat16, device="cuda")
+            s["o_out"] = torch.empty(i["q_elems"], dtype=torch.bfloat16, device="cuda")
+            self.sets.append(s)
+        torch.cuda.synchronize()
+
+
+def time_launches(fn, n, rotate):
+    """Durations (s) of n launches of fn(set_index), each bracketed by HIP
+    events on torch's current stream, the stream the library launches on."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record()
+        fn(i % rotate)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(z) * 1e-3 for a, z in ev]
+
+
+def rate(nbytes, seconds):
+    return nbytes / seconds / 1e9
+
+
+def run_gpu(args):
+    import torch
+    from sequence_re_layout_amd import binding as b
+
+    torch.cuda.set_device(0)
+    w = Workload(b, args.workload, args.mode, args.rotate)
+    plan, sets = w.plan, w.sets
+
+    def s2h(i):
+        s = sets[i]
+        b.basp_seq_to_head(plan, s["q"], s["k"], s["v"], s["qkv_out"])
+
+    def h2s(i):
+        s = sets[i]
+        b.basp_head_to_seq(plan, s["o"], s["o_out"])
+
+    # parity of the timed configuration: the fused output of set 0 against
+    # the head->seq inverse of itself would need the oracle; the bench only
+    # checks the round trip on the device, which holds for any correct kernel
+    for i in range(args.warmup):
+        s2h(i % w.R)
+        h2s(i % w.R)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-kernel events on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        s2h(i % w.R)
+        ev[i][1].record()
+        h2s(i % w.R)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    s2h_t = [e[0].elapsed_time(e[1]) * 1e-3 for e in ev]
+    h2s_t = [e[1].elapsed_time(e[2]) * 1e-3 for e in ev]
+
+    ms_per_step = wall / args.steps * 1e3
+    step_bytes = w.s2h_bytes + w.h2s_bytes
+    s2h_avg = statistics.mean(s2h_t)
+    res = {
+        "ms_per_step": ms_per_step,
+        "value": rate(step_bytes, wall / args.steps),
+        "step_bytes": step_bytes,
+        "rotate_sets": w.R,
+        "s2h_avg_us": s2h_avg * 1e6,
+        "s2h_median_us": statistics.median(s2h_t) * 1e6,
+        "h2s_avg_us": statistics.mean(h2s_t) * 1e6,
+        "h2s_median_us": statistics.median(h2s_t) * 1e6,
+        "s2h_bytes": w.s2h_bytes,
+        "h2s_bytes": w.h2s_bytes,
+        "s2h_gbs": rate(w.s2h_bytes, s2h_avg),
+        "h2s_gbs": rate(w.h2s_bytes, statistics.mean(h2s_t)),
+    }
+
+    # device round trip of the timed buffers: head->seq of the Q part of the
+    # fused output must give Q back bit for bit
+    s = sets[0]
+    back = torch.empty_like(s["q"])
+    b.basp_seq_to_head(plan, s["q"], s["k"], s["v"], s["qkv_out"])
+    b.basp_head_to_seq(plan, s["qkv_out"][: plan.info["q_elems"]], back)
+    torch.cuda.synchronize()
+    res["round_trip_bit_exact"] = bool(torch.equal(back.view(torch.int16), s["q"].view(torch.int16)))
+
+    if not args.no_detail:
+        res["detail"] = detail(args, b, w)
+    res["w"] = w
+    return res
+
+
+def detail(args, b, w):
+    """Per-kernel rates of both modes, the unfused baseline and a plain copy."""
+    import torch
+    out = {}
+    n = args.detail_iters
+    for mode in ("basp", "ulysses"):
+        ww = w if mode == w.mode else Workload(b, w.name, mode, w.R)
+        p, sets = ww.plan, ww.sets
+        t = time_launches(lambda i: b.basp_seq_to_head(p, sets[i]["q"], sets[i]["k"], sets[i]["v"],
+                                                       sets[i]["qkv_out"]), n, ww.R)
+        u = time_launches(lambda i: b.basp_head_to_seq(p, sets[i]["o"], sets[i]["o_out"]), n, ww.R)
+        info = p.info
+        out[mode] = {
+            "G": info["G"], "P": info["P"], "Bl": info["Bl"], "peers_per_rank": info["peers_per_rank"],
+            "cross_rank_bytes_qkv": info["cross_rank_bytes_q"] + 2 * info["cross_rank_bytes_kv"],
+            "s2h_median_us": statistics.median(t) * 1e6,
+            "s2h_gbs": rate(ww.s2h_bytes, statistics.median(t)),
+            "s2h_frac_of_peak": rate(ww.s2h_bytes, statistics.median(t)) / HBM_PEAK_GBS,
+            "h2s_median_us": statistics.median(u) * 1e6,
+            "h2s_gbs": rate(ww.h2s_bytes, statistics.median(u)),
+            "h2s_frac_of_peak": rate(ww.h2s_bytes, statistics.median(u)) / HBM_PEAK_GBS,
+        }
+        if mode == w.mode:
+            ws = torch.empty(b.basp_unfused_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+            f = time_launches(lambda i: b.basp_seq_to_head_unfused(
+                p, sets[i]["q"], sets[i]["k"], sets[i]["v"], sets[i]["qkv_out"], ws), max(10, n // 4), ww.R)
+            out[mode]["s2h_unfused_median_us"] = statistics.median(f) * 1e6
+            out[mode]["s2h_unfused_gbs"] = rate(ww.s2h_bytes, statistics.median(f))
+            del ws
+        if ww is not w:
+            del ww
+            torch.cuda.empty_cache()
+    # plain device copy of the same byte count (read + write), and the
+    # known-size copy the PMC counters are scaled by
+    nb = w.s2h_bytes // 2
+    src = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    dst = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    c = time_launches(lambda i: dst[i].copy_(src[i]), n, 4)
+    out["device_copy"] = {"bytes_moved": 2 * nb, "median_us": statistics.median(c) * 1e6,
+                          "gbs": rate(2 * nb, statistics.median(c))}
+    cal_src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    cal_dst = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    return out
+
+
+# ------------------------------------------------------------------ CPU ---
+
+def cpu_baseline(args, w):
+    """The oracle doing one step (fused Q/K/V seq->head, O head->seq) on the
+    host bytes of the same workload, repeated for about --cpu-seconds."""
+    import oracle
+    from sequence_re_layout_amd import inputs
+    N, B, S, Hq, Hkv, d = w.shape
+    mode = oracle.BASP if w.mode == "basp" else oracle.ULYSSES
+    q, k, v, o = (inputs.raw_bits(w.host[n]) for n in ("q", "k", "v", "o"))
+    threads = oracle.max_threads()
+    reps, spent = 0, 0.0
+    while reps == 0 or spent < args.cpu_seconds:
+        t0 = time.perf_counter_ns()
+        oracle.seq_to_head_qkv(q, k, v, mode, N, B, S, Hq, Hkv, d, threads=threads)
+        oracle.head_to_seq(o, mode, N, B, S, Hq, d, threads=threads)
+        spent += (time.perf_counter_ns() - t0) * 1e-9
+        reps += 1
+    step_bytes = w.s2h_bytes + w.h2s_bytes
+    return {"value": rate(step_bytes * reps, spent), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d full step(s) of the same workload (fused QKV seq->head + O head->seq), "
+                      "%.1f s on the host, OpenMP over destination blocks" % (reps, spent),
+            "seconds_per_step": spent / reps, "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+# ------------------------------------------------------------ roofline ---
+
+def traffic_bytes(workload):
+    """HBM bytes per fused seq->head launch from committed PMC counters, or
+    None when they are missing or were taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sources_sha256") != kernel_sources_sha256() or t.get("workload") != workload:
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def pmc_summary(fetch_dir, write_dir):
+    """Per-launch FETCH_SIZE/WRITE_SIZE of the fused kernel, scaled by the same
+    counter on the known-size copy, into profiles/pmc_traffic.json."""
+
+    def load(d, counter):
+        rows = []
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                rows += [r for r in csv.DictReader(f) if r.get("Counter_Name") == counter]
+        if not rows:
+            raise SystemExit("no %s rows under %s" % (counter, d))
+        return rows
+
+    out = {"workload": None, "kernel_sources_sha256": kernel_sources_sha256()}
+    for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        rows = load(d, counter)
+        fused = [float(r["Counter_Value"]) for r in rows if "tile_kernel" in r["Kernel_Name"]
+                 and "Lb1E" in r["Kernel_Name"]]
+        copies = [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()]
+        if not fused or not copies:
+            raise SystemExit("missing fused or copy dispatches for %s" % counter)
+        # the calibration copy is the last copy of the run (CALIB_BYTES each way)
+        factor = (CALIB_BYTES / 1024.0) / copies[-1]
+        kib = statistics.median(fused)
+        out[counter] = {"kib_per_launch_raw": kib, "copy_kib_raw": copies[-1], "scale": factor,
+                        "bytes_per_launch": kib * factor * 1024.0, "launches": len(fused)}
+    out["traffic_bytes_per_launch"] = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
+    return out
+
+
+# ---------------------------------------------------------------- main ---
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.pmc_summary:
+        res = pmc_summary(*args.pmc_summary)
+        res["workload"] = parse_args([]).workload
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(res, f, indent=1)
+        print(json.dumps(res))
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the N virtual ranks of the re-layout share one "
+              "device allocation, and no multi-GPU path exists (requested --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        return 2
+
+    r = run_gpu(args)
+    w = r.pop("w")
+    N, B, S, Hq, Hkv, d = w.shape
+    traffic = traffic_bytes(w.name)
+    line = {
+        "metric": METRIC,
+        "value": r["value"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 Q/K/V/O, resident in HBM, %d rotating buffer sets" % r["rotate_sets"],
+        "config": {"workload": w.name, "N": N, "B": B, "S": S, "Hq": Hq, "Hkv": Hkv, "d": d,
+                   "mode": w.mode, "parallelism": "%d virtual ranks on 1 GPU" % N,
+                   "step": "fused QKV seq->head + O head->seq", "step_bytes": r["step_bytes"]},
+        "roofline": {"bound": "hbm", "kernel": "fused QKV seq->head (tile_kernel)",
+                     "achieved": r["s2h_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": r["s2h_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": r["s2h_bytes"], "avg_launch_us": r["s2h_avg_us"]},
+        "head_to_seq": {"achieved": r["h2s_gbs"], "frac": r["h2s_gbs"] / HBM_PEAK_GBS,
+                        "avg_launch_us": r["h2s_avg_us"], "bytes_per_launch": r["h2s_bytes"]},
+        "round_trip_bit_exact": r["round_trip_bit_exact"],
+    }
+    if "detail" in r:
+        line["detail"] = r["detail"]
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args, w)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

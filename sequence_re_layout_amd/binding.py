@@ -64,6 +64,11 @@ class BaspError(RuntimeError):
         super().__init__("%s: %s" % (call, basp_status_str(status)))
 
 
+# torch first: libbasp.so then binds to the HIP runtime torch has loaded, so
+# that streams, events and allocations are shared with it (one runtime per
+# process).
+import torch  # noqa: E402,F401
+
 if not os.path.exists(LIB_PATH):
     raise ImportError("libbasp.so is not built (expected at %s); build it with "
                       "`python -m sequence_re_layout_amd.build`" % LIB_PATH)

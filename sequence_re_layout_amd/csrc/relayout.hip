@@ -178,27 +178,37 @@ TileFn tile_fn(int vw, int vpt, int pol, bool s2h)
     }
 }
 
+// The launch's own status (not the thread's sticky last error, which other
+// code in the process may have left set).
+template <typename Desc>
+basp_status launch_kernel(const void *fn, uint32_t grid, const Desc &D, void *stream)
+{
+    void *args[] = {const_cast<Desc *>(&D)};
+    const hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BASP_OK : BASP_ERR_HIP;
+}
+
 basp_status launch(const TileLaunch &L, void *stream)
 {
     if (L.grid == 0)
         return BASP_OK;
-    hipLaunchKernelGGL(tile_fn(L.vw, L.vpt, L.policy, L.s2h), dim3(L.grid), dim3(kBlock), 0,
-                       static_cast<hipStream_t>(stream), L.D);
-    return hipGetLastError() == hipSuccess ? BASP_OK : BASP_ERR_HIP;
+    const TileFn fn = tile_fn(L.vw, L.vpt, L.policy, L.s2h);
+    return launch_kernel(reinterpret_cast<const void *>(fn), L.grid, L.D, stream);
 }
 
 basp_status launch(const PermLaunch &L, void *stream)
 {
     if (L.grid == 0)
         return BASP_OK;
-    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const void *fn;
     switch (L.vw) {
-    case 16: hipLaunchKernelGGL(perm_kernel<16>, dim3(L.grid), dim3(kBlock), 0, st, L.D); break;
-    case 8: hipLaunchKernelGGL(perm_kernel<8>, dim3(L.grid), dim3(kBlock), 0, st, L.D); break;
-    case 4: hipLaunchKernelGGL(perm_kernel<4>, dim3(L.grid), dim3(kBlock), 0, st, L.D); break;
-    default: hipLaunchKernelGGL(perm_kernel<2>, dim3(L.grid), dim3(kBlock), 0, st, L.D); break;
+    case 16: fn = reinterpret_cast<const void *>(perm_kernel<16>); break;
+    case 8: fn = reinterpret_cast<const void *>(perm_kernel<8>); break;
+    case 4: fn = reinterpret_cast<const void *>(perm_kernel<4>); break;
+    default: fn = reinterpret_cast<const void *>(perm_kernel<2>); break;
     }
-    return hipGetLastError() == hipSuccess ? BASP_OK : BASP_ERR_HIP;
+    return launch_kernel(fn, L.grid, L.D, stream);
 }
 
 }  // namespace

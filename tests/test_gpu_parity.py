@@ -336,3 +336,14 @@ def test_device_error_paths():
     # q, k and v may share one buffer
     b.basp_seq_to_head(plan, q, q, q, out)
     torch.cuda.synchronize()
+
+
+def test_single_hip_runtime_and_native_library():
+    """libbasp.so is loaded from the tree and shares torch's HIP runtime: one
+    libamdhip64 image in the process."""
+    needs_gpu()
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = sorted({l.split()[-1] for l in maps if "libamdhip64" in l})
+    assert len(hip) == 1, hip
+    basp = sorted({l.split()[-1] for l in maps if l.endswith("libbasp.so")})
+    assert basp == [b.LIB_PATH], basp
