@@ -15,8 +15,9 @@ Printed: one JSON line.  ``value`` is effective HBM GB/s of the whole step
 (algorithmic bytes: every input byte read once, every output byte written
 once) over wall time of K steps bracketed by device synchronisation.
 ``roofline`` is the fused seq->head kernel (the larger of the two) against
-the 8 TB/s HBM peak, its duration taken with HIP events on the stream it runs
-on.  ``detail`` holds per-kernel rates of both modes, the unfused three-pass
+the 8 TB/s HBM peak, its duration taken from HIP events that its own launch
+records (hipExtLaunchKernel start/stop timestamps, via basp_time_next_call) on
+the stream it runs on.  ``detail`` holds per-kernel rates of both modes, the unfused three-pass
 baseline and a plain device copy.  ``cpu_baseline`` is the CPU oracle doing
 the same step on the host, repeated for about --cpu-seconds.
 
@@ -110,9 +111,31 @@ class Workload:
         torch.cuda.synchronize()
 
 
-def time_launches(fn, n, rotate):
-    """Durations (s) of n launches of fn(set_index), each bracketed by HIP
-    events on torch's current stream, the stream the library launches on."""
+def make_events(n):
+    """n timing events whose handles exist (torch creates them on first record)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    return ev
+
+
+def time_launches(b, fn, n, rotate):
+    """Durations (s) of n calls of fn(set_index), each timed from its kernels'
+    own dispatch timestamps (basp_time_next_call) on the launch stream."""
+    import torch
+    ev = make_events(2 * n)
+    for i in range(n):
+        b.basp_time_next_call(ev[2 * i], ev[2 * i + 1])
+        fn(i % rotate)
+    torch.cuda.synchronize()
+    return [ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e-3 for i in range(n)]
+
+
+def time_torch(fn, n, rotate):
+    """Durations (s) of n calls of a torch op, bracketed by events on torch's
+    current stream."""
     import torch
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     for i in range(n):
@@ -143,28 +166,25 @@ def run_gpu(args):
         s = sets[i]
         b.basp_head_to_seq(plan, s["o"], s["o_out"])
 
-    # parity of the timed configuration: the fused output of set 0 against
-    # the head->seq inverse of itself would need the oracle; the bench only
-    # checks the round trip on the device, which holds for any correct kernel
     for i in range(args.warmup):
         s2h(i % w.R)
         h2s(i % w.R)
     torch.cuda.synchronize()
 
-    # timed region: K steps, per-kernel events on the launch stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # timed region: K steps; each kernel carries its own start/stop events
+    # (dispatch timestamps), so nothing extra is queued between the kernels
+    ev = make_events(4 * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        ev[i][0].record()
+        b.basp_time_next_call(ev[4 * i], ev[4 * i + 1])
         s2h(i % w.R)
-        ev[i][1].record()
+        b.basp_time_next_call(ev[4 * i + 2], ev[4 * i + 3])
         h2s(i % w.R)
-        ev[i][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    s2h_t = [e[0].elapsed_time(e[1]) * 1e-3 for e in ev]
-    h2s_t = [e[1].elapsed_time(e[2]) * 1e-3 for e in ev]
+    s2h_t = [ev[4 * i].elapsed_time(ev[4 * i + 1]) * 1e-3 for i in range(args.steps)]
+    h2s_t = [ev[4 * i + 2].elapsed_time(ev[4 * i + 3]) * 1e-3 for i in range(args.steps)]
 
     ms_per_step = wall / args.steps * 1e3
     step_bytes = w.s2h_bytes + w.h2s_bytes
@@ -207,9 +227,9 @@ def detail(args, b, w):
     for mode in ("basp", "ulysses"):
         ww = w if mode == w.mode else Workload(b, w.name, mode, w.R)
         p, sets = ww.plan, ww.sets
-        t = time_launches(lambda i: b.basp_seq_to_head(p, sets[i]["q"], sets[i]["k"], sets[i]["v"],
-                                                       sets[i]["qkv_out"]), n, ww.R)
-        u = time_launches(lambda i: b.basp_head_to_seq(p, sets[i]["o"], sets[i]["o_out"]), n, ww.R)
+        t = time_launches(b, lambda i: b.basp_seq_to_head(p, sets[i]["q"], sets[i]["k"], sets[i]["v"],
+                                                          sets[i]["qkv_out"]), n, ww.R)
+        u = time_launches(b, lambda i: b.basp_head_to_seq(p, sets[i]["o"], sets[i]["o_out"]), n, ww.R)
         info = p.info
         out[mode] = {
             "G": info["G"], "P": info["P"], "Bl": info["Bl"], "peers_per_rank": info["peers_per_rank"],
@@ -223,7 +243,7 @@ def detail(args, b, w):
         }
         if mode == w.mode:
             ws = torch.empty(b.basp_unfused_workspace_bytes(p), dtype=torch.uint8, device="cuda")
-            f = time_launches(lambda i: b.basp_seq_to_head_unfused(
+            f = time_launches(b, lambda i: b.basp_seq_to_head_unfused(
                 p, sets[i]["q"], sets[i]["k"], sets[i]["v"], sets[i]["qkv_out"], ws), max(10, n // 4), ww.R)
             out[mode]["s2h_unfused_median_us"] = statistics.median(f) * 1e6
             out[mode]["s2h_unfused_gbs"] = rate(ww.s2h_bytes, statistics.median(f))
@@ -236,7 +256,7 @@ def detail(args, b, w):
     nb = w.s2h_bytes // 2
     src = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(4)]
     dst = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(4)]
-    c = time_launches(lambda i: dst[i].copy_(src[i]), n, 4)
+    c = time_torch(lambda i: dst[i].copy_(src[i]), n, 4)
     out["device_copy"] = {"bytes_moved": 2 * nb, "median_us": statistics.median(c) * 1e6,
                           "gbs": rate(2 * nb, statistics.median(c))}
     cal_src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
@@ -308,20 +328,23 @@ def pmc_summary(fetch_dir, write_dir):
                 rows += [r for r in csv.DictReader(f) if r.get("Counter_Name") == counter]
         if not rows:
             raise SystemExit("no %s rows under %s" % (counter, d))
-        return rows
+        return sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
 
     out = {"workload": None, "kernel_sources_sha256": kernel_sources_sha256()}
     for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
         rows = load(d, counter)
-        fused = [float(r["Counter_Value"]) for r in rows if "tile_kernel" in r["Kernel_Name"]
-                 and "Lb1E" in r["Kernel_Name"]]
-        copies = [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()]
+        # the fused seq->head kernel: tile_kernel<VW, VPT, POLICY, true>
+        fused = [r for r in rows if "tile_kernel<" in r["Kernel_Name"] and "true>" in r["Kernel_Name"]]
+        copies = [r for r in rows if "copy" in r["Kernel_Name"].lower()]
         if not fused or not copies:
             raise SystemExit("missing fused or copy dispatches for %s" % counter)
         # the calibration copy is the last copy of the run (CALIB_BYTES each way)
-        factor = (CALIB_BYTES / 1024.0) / copies[-1]
-        kib = statistics.median(fused)
-        out[counter] = {"kib_per_launch_raw": kib, "copy_kib_raw": copies[-1], "scale": factor,
+        cal = float(copies[-1]["Counter_Value"])
+        factor = (CALIB_BYTES / 1024.0) / cal
+        kib = statistics.median(float(r["Counter_Value"]) for r in fused)
+        out["kernel"] = fused[0]["Kernel_Name"]
+        out[counter] = {"kib_per_launch_raw": kib, "copy_kernel": copies[-1]["Kernel_Name"],
+                        "copy_kib_raw": cal, "scale": factor,
                         "bytes_per_launch": kib * factor * 1024.0, "launches": len(fused)}
     out["traffic_bytes_per_launch"] = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
     return out

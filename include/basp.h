@@ -18,11 +18,11 @@
  *   BASP:     N = K*B ranks in B disjoint groups of K = N/B, each group owns
  *             one sequence and exchanges K-way; every rank keeps B*S/N tokens
  *                                             [review, Summary; Key claims]
- *             G = B, P = K, Bl = 1.  With B > N the method falls back to data
- *             parallelism [review, Frequently asked questions]: G = N, P = 1,
- *             Bl = B/N (B must then be a multiple of N).
+ *             G = B, P = K, Bl = 1.  With more sequences than ranks (B > N)
+ *             the method reverts to data parallelism [review, Frequently asked
+ *             questions]: G = N, P = 1, Bl = B/N (B a multiple of N).
  *
- * Rank r is member j = r % P of group g = r / P (contiguous rank assignment,
+ * Rank r is member j = r % P of group g = r / P (groups of consecutive ranks,
  * [review, Summary]); group g owns sequences [g*Bl, (g+1)*Bl).  Member j holds
  * the tokens [j*St, (j+1)*St), St = S/P, before attention and the heads
  * [j*Hl, (j+1)*Hl), Hl = H/P, after it (heads split evenly over the members,
@@ -36,7 +36,7 @@
  * For BASP with B <= N the sequence-sharded buffer is exactly the global
  * [B][S][H][d] tensor.
  *
- * The re-layout copies elements bit for bit ("identical model accuracy",
+ * The re-layout copies elements bit for bit (model accuracy is unchanged,
  * [abstract, Abstract]): only the element size matters, values are never
  * interpreted, so NaN payloads, signed zeros and subnormals pass unchanged.
  *
@@ -205,15 +205,22 @@ basp_status basp_seq_to_head_unfused(const basp_plan *plan, const void *q, const
 
 /*
  * Launch shape of a plan, for tuning sweeps.  Zero fields keep the built-in
- * choice.  Results never depend on these values, only the speed does.
+ * choice, which depends on the direction and on the row size d*elem_size
+ * (measured on MI355X over the Llama/Qwen attention shapes).  Results never
+ * depend on these values, only the speed does.
  *   vectors_per_thread   1, 2, 4 or 8 (16-byte vectors held in flight per lane)
  *   tile_tokens          tokens per work tile (>= 1)
  *   tile_heads           heads per work tile (>= 1, clamped to H/P)
  *   cache_policy         1 = plain loads and stores, 2 = non-temporal stores,
- *                        3 = non-temporal loads and stores
+ *                        3 = non-temporal loads and stores (built-in)
  *   max_grid             cap on work-groups per launch (tiles loop beyond it)
- * BASP_ERR_INVALID on a NULL plan or an out-of-range value.  Not thread-safe
- * against concurrent launches with the same plan.
+ *   lane_order           1 = lanes run along tokens first, 2 = along heads
+ *                        first (built-in)
+ *   xcd_remap            1 = tiles in work-group order, 2 = each of the 8 XCDs
+ *                        takes one contiguous eighth of the tiles (built-in)
+ * BASP_ERR_INVALID on a NULL plan or an out-of-range value,
+ * BASP_ERR_UNSUPPORTED when the shape exceeds the index limits.  Not
+ * thread-safe against concurrent launches with the same plan.
  */
 typedef struct basp_tuning {
     int32_t vectors_per_thread;
@@ -221,9 +228,22 @@ typedef struct basp_tuning {
     int32_t tile_heads;
     int32_t cache_policy;
     int32_t max_grid;
+    int32_t lane_order;
+    int32_t xcd_remap;
 } basp_tuning;
 basp_status basp_plan_set_tuning(basp_plan *plan, const basp_tuning *tuning);
 basp_status basp_plan_get_tuning(const basp_plan *plan, basp_tuning *tuning);
+
+/*
+ * Kernel timing without extra work on the stream.  The next call of this
+ * thread that launches kernels records start_event when its first kernel
+ * begins and stop_event when its last kernel ends, from the kernels' own
+ * dispatch timestamps (hipExtLaunchKernel).  The events are hipEvent_t
+ * handles passed as void*, created by the caller on the current device; either
+ * may be NULL.  The request applies to exactly one call (also one that fails
+ * or launches nothing) and is then cleared.  Returns BASP_OK.
+ */
+basp_status basp_time_next_call(void *start_event, void *stop_event);
 
 /* Status of the last call made by this thread, and a static description. */
 basp_status basp_last_error(void);

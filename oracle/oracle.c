@@ -21,10 +21,10 @@
  *   - BASP: N = K*B; the N GPUs form B disjoint groups of K = N/B, each
  *     group owns one sequence and runs its own K-way all-to-all; every GPU
  *     still holds B*S/N tokens [review, Summary; Key claims].
- *   - Contiguous rank assignment [review, Summary].
- *   - N must be a multiple of B; heads must split evenly across the members
- *     of a group; B > N falls back to data parallelism
- *     [review, Frequently asked questions].
+ *   - The ranks of a group are consecutive [review, Summary].
+ *   - N must be a multiple of B; the heads must split equally over the
+ *     members of a group; with more sequences than GPUs the method reverts to
+ *     data parallelism [review, Frequently asked questions].
  *
  * What the pages leave open, and the reading taken here (each is also
  * listed with the other readings of this project):
@@ -46,8 +46,8 @@
  *   BASP, B <= N:     G = B, P = N/B, Bl = 1
  *   BASP, B >  N:     G = N, P = 1,   Bl = B/N
  *
- * The re-layout moves elements without changing them ("identical model
- * accuracy", [abs, Abstract]), so the oracle copies raw bytes of es bytes
+ * The re-layout moves elements without changing them (model accuracy is
+ * unchanged, [abs, Abstract]), so the oracle copies raw bytes of es bytes
  * each; no floating point is involved anywhere.
  *
  * Every function walks the destination buffer element by element and reads

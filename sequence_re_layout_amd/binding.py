@@ -53,7 +53,8 @@ class basp_plan_info(ctypes.Structure):
 
 class basp_tuning(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "vectors_per_thread", "tile_tokens", "tile_heads", "cache_policy", "max_grid")]
+        "vectors_per_thread", "tile_tokens", "tile_heads", "cache_policy", "max_grid",
+        "lane_order", "xcd_remap")]
 
 
 class BaspError(RuntimeError):
@@ -100,6 +101,8 @@ _lib.basp_plan_set_tuning.argtypes = [_plan_p, ctypes.POINTER(basp_tuning)]
 _lib.basp_plan_set_tuning.restype = _i32
 _lib.basp_plan_get_tuning.argtypes = [_plan_p, ctypes.POINTER(basp_tuning)]
 _lib.basp_plan_get_tuning.restype = _i32
+_lib.basp_time_next_call.argtypes = [_vp, _vp]
+_lib.basp_time_next_call.restype = _i32
 _lib.basp_last_error.argtypes = []
 _lib.basp_last_error.restype = _i32
 _lib.basp_status_str.argtypes = [_i32]
@@ -121,7 +124,7 @@ class Plan:
 
     def __del__(self):
         h, self.handle = getattr(self, "handle", None), None
-        if h:
+        if h and _lib is not None:   # _lib is None during interpreter shutdown
             _lib.basp_plan_destroy(h)
 
     @property
@@ -169,8 +172,9 @@ def basp_plan_query(plan: Plan) -> dict:
 
 
 def basp_plan_set_tuning(plan: Plan, vectors_per_thread=0, tile_tokens=0, tile_heads=0,
-                         cache_policy=0, max_grid=0) -> None:
-    t = basp_tuning(vectors_per_thread, tile_tokens, tile_heads, cache_policy, max_grid)
+                         cache_policy=0, max_grid=0, lane_order=0, xcd_remap=0) -> None:
+    t = basp_tuning(vectors_per_thread, tile_tokens, tile_heads, cache_policy, max_grid,
+                    lane_order, xcd_remap)
     _check(_lib.basp_plan_set_tuning(plan.handle, ctypes.byref(t)), "basp_plan_set_tuning")
 
 
@@ -178,6 +182,17 @@ def basp_plan_get_tuning(plan: Plan) -> dict:
     t = basp_tuning()
     _check(_lib.basp_plan_get_tuning(plan.handle, ctypes.byref(t)), "basp_plan_get_tuning")
     return {name: getattr(t, name) for name, _ in t._fields_}
+
+
+def basp_time_next_call(start_event, stop_event) -> None:
+    """Time the next call of this thread from its kernels' own dispatch
+    timestamps.  Takes torch.cuda.Event objects (already recorded once, so
+    that their handles exist) or raw hipEvent_t addresses."""
+    def handle(e):
+        if e is None or isinstance(e, int):
+            return e
+        return e.cuda_event
+    _check(_lib.basp_time_next_call(handle(start_event), handle(stop_event)), "basp_time_next_call")
 
 
 def basp_unfused_workspace_bytes(plan: Plan) -> int:

@@ -13,12 +13,40 @@
 namespace basp {
 namespace {
 
-constexpr int kDefaultVpt = 4;           // 16-byte vectors in flight per lane
-constexpr int kDefaultPolicy = 2;        // non-temporal stores
 constexpr uint32_t kGridCap = 1u << 22;  // work-groups per launch at most
 
-int resolved_vpt(const basp_tuning &t) { return t.vectors_per_thread ? t.vectors_per_thread : kDefaultVpt; }
-int resolved_policy(const basp_tuning &t) { return t.cache_policy ? t.cache_policy : kDefaultPolicy; }
+// Launch shape of one tile launch: the plan's tuning where set, else the
+// defaults below.  The defaults come from sweeps on MI355X over every named
+// workload (Llama/Qwen shapes, 128- and 256-byte rows, both modes):
+//   - non-temporal loads and stores: each byte is touched exactly once;
+//   - XCD-contiguous tile order: each XCD streams one contiguous eighth;
+//   - about 4 KiB per tile for seq->head (one 16-byte vector per lane), with
+//     4 heads per tile for 128-byte rows and 1 for longer rows;
+//   - 8 KiB per tile for head->seq with 4 heads per tile, and a grid capped
+//     at 8192 work-groups for 128-byte rows.
+struct Shape {
+    int vpt, policy;
+    uint32_t tile_tokens, tile_heads;   // tile_tokens 0: derived
+    bool heads_given;                   // tile_heads set by the tuning
+    bool s_fast;
+    uint32_t grid_cap;
+    bool xcd;
+};
+
+Shape resolve(const basp_plan &p, const basp_tuning &t, bool s2h)
+{
+    const bool short_rows = p.row_bytes <= 128;
+    Shape s;
+    s.vpt = t.vectors_per_thread ? t.vectors_per_thread : (s2h ? 1 : 2);
+    s.policy = t.cache_policy ? t.cache_policy : 3;
+    s.tile_tokens = uint32_t(t.tile_tokens);
+    s.tile_heads = t.tile_heads ? uint32_t(t.tile_heads) : (s2h && !short_rows ? 1 : 4);
+    s.heads_given = t.tile_heads != 0;
+    s.s_fast = t.lane_order ? t.lane_order == 1 : false;
+    s.grid_cap = t.max_grid ? uint32_t(t.max_grid) : (!s2h && short_rows ? 8192u : kGridCap);
+    s.xcd = t.xcd_remap ? t.xcd_remap == 2 : true;
+    return s;
+}
 
 uint64_t addr(const void *p) { return reinterpret_cast<uint64_t>(p); }
 
@@ -44,14 +72,12 @@ struct TileShape {
 };
 
 // Tile of one tensor with Hl heads per rank and A vectors per row: about
-// kBlock*vpt vectors, lanes along the head-sharded layout's contiguous axis.
-TileShape tile_shape(const basp_plan &p, const basp_tuning &t, uint32_t Hl, uint32_t A)
+// kBlock*vpt vectors unless the tile extent is given.
+TileShape tile_shape(const basp_plan &p, const Shape &sh, uint32_t Hl, uint32_t A)
 {
-    const bool s_fast = p.layout == BASP_LAYOUT_HEAD_MAJOR;
-    const uint64_t rows = std::max<uint64_t>(1, uint64_t(kBlock) * resolved_vpt(t) / A);
-    uint64_t th = t.tile_heads ? uint64_t(t.tile_heads) : (s_fast ? 1 : std::min<uint64_t>(Hl, rows));
-    th = std::min<uint64_t>(th, Hl);
-    uint64_t ts = t.tile_tokens ? uint64_t(t.tile_tokens) : std::max<uint64_t>(1, rows / th);
+    const uint64_t rows = std::max<uint64_t>(1, uint64_t(kBlock) * sh.vpt / A);
+    uint64_t th = std::min<uint64_t>(sh.tile_heads, Hl);
+    uint64_t ts = sh.tile_tokens ? uint64_t(sh.tile_tokens) : std::max<uint64_t>(1, rows / th);
     ts = std::min<uint64_t>(ts, uint64_t(std::max<int64_t>(p.St, 1)));
     TileShape s;
     s.Ts = uint32_t(ts);
@@ -98,6 +124,21 @@ bool tile_offsets_fit(const basp_plan &p, uint32_t H, const TileShape &ts)
            s.head_tok <= kI31Max && (ts.Th == 1 || s.head_head <= kI31Max);
 }
 
+// Tile shape of a tensor of H heads whose in-tile offsets fit; a built-in
+// multi-head tile falls back to one head per tile (the head stride of a very
+// long head-major sequence is too large for 31-bit offsets).
+bool fitted_shape(const basp_plan &p, Shape sh, uint32_t H, uint32_t A, TileShape &ts)
+{
+    ts = tile_shape(p, sh, H / p.P, A);
+    if (tile_offsets_fit(p, H, ts) && uint64_t(ts.Ts) * ts.Th * A <= kI31Max)
+        return true;
+    if (sh.heads_given || ts.Th == 1)
+        return false;
+    sh.tile_heads = 1;
+    ts = tile_shape(p, sh, H / p.P, A);
+    return tile_offsets_fit(p, H, ts) && uint64_t(ts.Ts) * ts.Th * A <= kI31Max;
+}
+
 struct SegSpec {
     uint64_t seq, head;   // addresses
     uint32_t H;           // heads of this tensor
@@ -113,10 +154,11 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
     }
     const int vw = vector_width(p, addrs, 2 * nseg);
     const uint32_t A = uint32_t(p.row_bytes / vw);
+    const Shape sh = resolve(p, p.tuning, s2h);
     TileDesc &D = L.D;
     D.St = uint32_t(p.St);
     D.row = uint32_t(p.row_bytes);
-    D.s_fast = p.layout == BASP_LAYOUT_HEAD_MAJOR;
+    D.s_fast = sh.s_fast;
     D.P = make_fastdiv(p.P);
     D.Bl = make_fastdiv(p.Bl);
     D.A = make_fastdiv(A);
@@ -129,8 +171,8 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
             continue;
         }
         const uint32_t H = segs[i].H, Hl = H / p.P;
-        const TileShape ts = tile_shape(p, p.tuning, Hl, A);
-        if (!tile_offsets_fit(p, H, ts))
+        TileShape ts;
+        if (!fitted_shape(p, sh, H, A, ts))
             return BASP_ERR_UNSUPPORTED;
         const Strides st = strides(p, H);
         sg.seq = segs[i].seq;
@@ -153,16 +195,16 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
         sg.fast = make_fastdiv(D.s_fast ? ts.Ts : ts.Th);
         sg.tile_begin = uint32_t(total);
         total += ts.ntiles;
-        if (total > kI31Max || uint64_t(ts.Ts) * ts.Th * A > kI31Max)
+        if (total > kI31Max)
             return BASP_ERR_UNSUPPORTED;
         sg.tile_end = uint32_t(total);
     }
     D.ntiles = uint32_t(total);
-    const uint32_t cap = p.tuning.max_grid ? uint32_t(p.tuning.max_grid) : kGridCap;
-    L.grid = uint32_t(std::min<uint64_t>(total, cap));
+    D.xcd_span = sh.xcd ? uint32_t(total / kXcds) : 0;
+    L.grid = uint32_t(std::min<uint64_t>(total, sh.grid_cap));
     L.vw = vw;
-    L.vpt = resolved_vpt(p.tuning);
-    L.policy = resolved_policy(p.tuning);
+    L.vpt = sh.vpt;
+    L.policy = sh.policy;
     L.s2h = s2h;
     return BASP_OK;
 }
@@ -253,16 +295,19 @@ basp_status check_launch_limits(const basp_plan &p, const basp_tuning &t)
         if (p.row_bytes % vw)
             continue;
         const uint32_t A = uint32_t(p.row_bytes / vw);
-        uint64_t total = 0;
         const uint32_t heads[3] = {uint32_t(p.Hq), uint32_t(p.Hkv), uint32_t(p.Hkv)};
-        for (int i = 0; i < 3; ++i) {
-            const TileShape ts = tile_shape(p, t, heads[i] / p.P, A);
-            if (!tile_offsets_fit(p, heads[i], ts) || uint64_t(ts.Ts) * ts.Th * A > kI31Max)
+        for (const bool s2h : {true, false}) {
+            const Shape sh = resolve(p, t, s2h);
+            uint64_t total = 0;
+            for (int i = 0; i < 3; ++i) {
+                TileShape ts;
+                if (!fitted_shape(p, sh, heads[i], A, ts))
+                    return BASP_ERR_UNSUPPORTED;
+                total += ts.ntiles;
+            }
+            if (total > kI31Max)
                 return BASP_ERR_UNSUPPORTED;
-            total += ts.ntiles;
         }
-        if (total > kI31Max)
-            return BASP_ERR_UNSUPPORTED;
     }
     return BASP_OK;
 }

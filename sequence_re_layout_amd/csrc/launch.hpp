@@ -62,8 +62,20 @@ struct TileDesc {
     uint32_t St;
     uint32_t row;                  // bytes per (token, head) row
     uint32_t s_fast;               // lanes along tokens (1) or heads (0)
+    uint32_t xcd_span;             // tiles per XCD when remapped, else 0
     FastDiv P, Bl, A;              // group size, sequences per group, vectors per row
 };
+
+// Work-groups are dispatched round-robin over the 8 XCDs (work-group i runs
+// on XCD i % 8).  With xcd_span = n/8 > 0 the i-th tile in launch order is
+// renumbered so that each XCD walks one contiguous eighth of the first
+// 8*xcd_span tiles; the remaining tiles keep their number.  A bijection.
+constexpr uint32_t kXcds = 8;
+
+BASP_HD inline uint32_t xcd_tile(uint32_t x, uint32_t span)
+{
+    return x < kXcds * span ? (x % kXcds) * span + x / kXcds : x;
+}
 
 // Where a tile starts and how much of it is real.
 struct TileOrigin {
@@ -72,8 +84,9 @@ struct TileOrigin {
     uint32_t ns, nh;               // tokens and heads present (ragged tail)
 };
 
-BASP_HD inline TileOrigin tile_origin(const TileDesc &D, uint32_t tile)
+BASP_HD inline TileOrigin tile_origin(const TileDesc &D, uint32_t x)
 {
+    const uint32_t tile = xcd_tile(x, D.xcd_span);
     TileOrigin o;
     o.seg = (tile >= D.seg[0].tile_end) + (tile >= D.seg[1].tile_end);
     const TileSeg &sg = D.seg[o.seg];

@@ -202,7 +202,8 @@ extern "C" basp_status basp_plan_set_tuning(basp_plan *p, const basp_tuning *t)
         return record(BASP_ERR_INVALID);
     const int v = t->vectors_per_thread;
     if ((v != 0 && v != 1 && v != 2 && v != 4 && v != 8) || t->tile_tokens < 0 ||
-        t->tile_heads < 0 || t->cache_policy < 0 || t->cache_policy > 3 || t->max_grid < 0)
+        t->tile_heads < 0 || t->cache_policy < 0 || t->cache_policy > 3 || t->max_grid < 0 ||
+        t->lane_order < 0 || t->lane_order > 2 || t->xcd_remap < 0 || t->xcd_remap > 2)
         return record(BASP_ERR_INVALID);
     const basp_status lim = basp::check_launch_limits(*p, *t);
     if (lim != BASP_OK)

@@ -14,6 +14,8 @@
 // descriptor, so they need no branch either.
 #include <hip/hip_runtime.h>
 
+#include <hip/hip_ext.h>
+
 #include <cstdint>
 
 #define BASP_HD __host__ __device__
@@ -178,14 +180,27 @@ TileFn tile_fn(int vw, int vpt, int pol, bool s2h)
     }
 }
 
+// Events set by basp_time_next_call for the next call of this thread.
+struct Timing {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local Timing t_timing;
+
 // The launch's own status (not the thread's sticky last error, which other
-// code in the process may have left set).
+// code in the process may have left set).  first/last: this launch opens or
+// closes the current entry-point call, for the timing events.
 template <typename Desc>
-basp_status launch_kernel(const void *fn, uint32_t grid, const Desc &D, void *stream)
+basp_status launch_kernel(const void *fn, uint32_t grid, const Desc &D, void *stream, bool first,
+                          bool last)
 {
     void *args[] = {const_cast<Desc *>(&D)};
-    const hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0,
-                                         static_cast<hipStream_t>(stream));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (t_timing.start || t_timing.stop)
+        e = hipExtLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, st,
+                               first ? t_timing.start : nullptr, last ? t_timing.stop : nullptr, 0);
+    else
+        e = hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, st);
     return e == hipSuccess ? BASP_OK : BASP_ERR_HIP;
 }
 
@@ -194,10 +209,10 @@ basp_status launch(const TileLaunch &L, void *stream)
     if (L.grid == 0)
         return BASP_OK;
     const TileFn fn = tile_fn(L.vw, L.vpt, L.policy, L.s2h);
-    return launch_kernel(reinterpret_cast<const void *>(fn), L.grid, L.D, stream);
+    return launch_kernel(reinterpret_cast<const void *>(fn), L.grid, L.D, stream, true, true);
 }
 
-basp_status launch(const PermLaunch &L, void *stream)
+basp_status launch(const PermLaunch &L, void *stream, bool first, bool last)
 {
     if (L.grid == 0)
         return BASP_OK;
@@ -208,7 +223,16 @@ basp_status launch(const PermLaunch &L, void *stream)
     case 4: fn = reinterpret_cast<const void *>(perm_kernel<4>); break;
     default: fn = reinterpret_cast<const void *>(perm_kernel<2>); break;
     }
-    return launch_kernel(fn, L.grid, L.D, stream);
+    return launch_kernel(fn, L.grid, L.D, stream, first, last);
+}
+
+// Runs f, the body of an entry point, and clears the timing request after it.
+template <typename F>
+basp_status timed_call(F f)
+{
+    const basp_status s = f();
+    t_timing = Timing();
+    return record(s);
 }
 
 }  // namespace
@@ -216,43 +240,58 @@ basp_status launch(const PermLaunch &L, void *stream)
 
 using basp::record;
 
+extern "C" basp_status basp_time_next_call(void *start_event, void *stop_event)
+{
+    basp::t_timing.start = static_cast<hipEvent_t>(start_event);
+    basp::t_timing.stop = static_cast<hipEvent_t>(stop_event);
+    return record(BASP_OK);
+}
+
 extern "C" basp_status basp_seq_to_head(const basp_plan *p, const void *q, const void *k,
                                         const void *v, void *out, void *stream)
 {
-    if (!p)
-        return record(BASP_ERR_INVALID);
-    basp::TileLaunch L;
-    const int s = basp::prepare_seq_to_head(*p, q, k, v, out, L);
-    return record(s != BASP_OK ? basp_status(s) : basp::launch(L, stream));
+    return basp::timed_call([&]() -> basp_status {
+        if (!p)
+            return BASP_ERR_INVALID;
+        basp::TileLaunch L;
+        const int s = basp::prepare_seq_to_head(*p, q, k, v, out, L);
+        return s != BASP_OK ? basp_status(s) : basp::launch(L, stream);
+    });
 }
 
 extern "C" basp_status basp_head_to_seq(const basp_plan *p, const void *o, void *out, void *stream)
 {
-    if (!p)
-        return record(BASP_ERR_INVALID);
-    basp::TileLaunch L;
-    const int s = basp::prepare_head_to_seq(*p, o, out, L);
-    return record(s != BASP_OK ? basp_status(s) : basp::launch(L, stream));
+    return basp::timed_call([&]() -> basp_status {
+        if (!p)
+            return BASP_ERR_INVALID;
+        basp::TileLaunch L;
+        const int s = basp::prepare_head_to_seq(*p, o, out, L);
+        return s != BASP_OK ? basp_status(s) : basp::launch(L, stream);
+    });
 }
 
 extern "C" basp_status basp_seq_to_head_o(const basp_plan *p, const void *dout, void *out,
                                           void *stream)
 {
-    if (!p)
-        return record(BASP_ERR_INVALID);
-    basp::TileLaunch L;
-    const int s = basp::prepare_seq_to_head_o(*p, dout, out, L);
-    return record(s != BASP_OK ? basp_status(s) : basp::launch(L, stream));
+    return basp::timed_call([&]() -> basp_status {
+        if (!p)
+            return BASP_ERR_INVALID;
+        basp::TileLaunch L;
+        const int s = basp::prepare_seq_to_head_o(*p, dout, out, L);
+        return s != BASP_OK ? basp_status(s) : basp::launch(L, stream);
+    });
 }
 
 extern "C" basp_status basp_head_to_seq_qkv(const basp_plan *p, const void *in, void *dq,
                                             void *dk, void *dv, void *stream)
 {
-    if (!p)
-        return record(BASP_ERR_INVALID);
-    basp::TileLaunch L;
-    const int s = basp::prepare_head_to_seq_qkv(*p, in, dq, dk, dv, L);
-    return record(s != BASP_OK ? basp_status(s) : basp::launch(L, stream));
+    return basp::timed_call([&]() -> basp_status {
+        if (!p)
+            return BASP_ERR_INVALID;
+        basp::TileLaunch L;
+        const int s = basp::prepare_head_to_seq_qkv(*p, in, dq, dk, dv, L);
+        return s != BASP_OK ? basp_status(s) : basp::launch(L, stream);
+    });
 }
 
 extern "C" size_t basp_unfused_workspace_bytes(const basp_plan *p)
@@ -266,11 +305,13 @@ extern "C" size_t basp_unfused_workspace_bytes(const basp_plan *p)
 extern "C" basp_status basp_seq_to_head_unfused(const basp_plan *p, const void *q, const void *k,
                                                 const void *v, void *out, void *ws, void *stream)
 {
-    if (!p)
-        return record(BASP_ERR_INVALID);
-    basp::PermLaunch L[3];
-    int s = basp::prepare_seq_to_head_unfused(*p, q, k, v, out, ws, L);
-    for (int i = 0; i < 3 && s == BASP_OK; ++i)
-        s = basp::launch(L[i], stream);
-    return record(basp_status(s));
+    return basp::timed_call([&]() -> basp_status {
+        if (!p)
+            return BASP_ERR_INVALID;
+        basp::PermLaunch L[3];
+        int s = basp::prepare_seq_to_head_unfused(*p, q, k, v, out, ws, L);
+        for (int i = 0; i < 3 && s == BASP_OK; ++i)
+            s = basp::launch(L[i], stream, i == 0, i == 2);
+        return basp_status(s);
+    });
 }

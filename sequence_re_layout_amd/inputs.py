@@ -6,7 +6,8 @@ bytes, so the generator cannot affect parity.
 
 * ``normal_bf16``: N(0, 1) drawn in float32 from a seeded CPU generator, then
   rounded to bfloat16 (round-to-nearest-even), as the attention activations
-  of the Llama/Qwen models the pages train are bf16 under mixed precision.
+  of the Llama/Qwen models the pages train are bf16 when training in mixed
+  precision.
 * ``tags_int32``: consecutive int32 tags ``base, base+1, ...``.  Every element
   is unique, so an output element names the input element it came from.
 

@@ -162,7 +162,9 @@ def test_ragged(shape, mode):
 TUNINGS = [dict(vectors_per_thread=1), dict(vectors_per_thread=2), dict(vectors_per_thread=8),
            dict(tile_tokens=1), dict(tile_tokens=3, tile_heads=2), dict(tile_tokens=100, tile_heads=3),
            dict(cache_policy=1), dict(cache_policy=3), dict(max_grid=7),
-           dict(vectors_per_thread=8, tile_tokens=5, tile_heads=1, cache_policy=3, max_grid=3)]
+           dict(vectors_per_thread=8, tile_tokens=5, tile_heads=1, cache_policy=3, max_grid=3),
+           dict(lane_order=2, tile_heads=3, tile_tokens=7), dict(xcd_remap=2, max_grid=24),
+           dict(xcd_remap=2, max_grid=13, lane_order=2)]
 
 
 @pytest.mark.parametrize("tuning", TUNINGS, ids=lambda t: ",".join("%s=%s" % kv for kv in t.items()))
@@ -347,3 +349,38 @@ def test_single_hip_runtime_and_native_library():
     assert len(hip) == 1, hip
     basp = sorted({l.split()[-1] for l in maps if l.endswith("libbasp.so")})
     assert basp == [b.LIB_PATH], basp
+
+
+def test_timed_call_records_kernel_time_and_keeps_results():
+    """basp_time_next_call: the events get the kernel's start and end, the
+    result is unchanged, and the request applies to one call only."""
+    needs_gpu()
+    shape = (8, 2, 8 * 129, 24, 8, 128)
+    N, B, S, Hq, Hkv, d = shape
+    plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, 1)
+    q, k, v = (x.cuda() for x in seq_inputs(B, S, Hq, Hkv, d, "bf16"))
+    ref = torch.empty(plan.info["qkv_elems"], dtype=torch.bfloat16, device="cuda")
+    b.basp_seq_to_head(plan, q, k, v, ref)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    out = torch.empty_like(ref)
+    b.basp_time_next_call(ev[0], ev[1])
+    b.basp_seq_to_head(plan, q, k, v, out)
+    torch.cuda.synchronize()
+    t = ev[0].elapsed_time(ev[1])
+    assert 0 < t < 1000.0
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    # the request was consumed: a second call leaves ev[2]/ev[3] as recorded
+    before = ev[2].elapsed_time(ev[3])
+    b.basp_seq_to_head(plan, q, k, v, out)
+    torch.cuda.synchronize()
+    assert ev[2].elapsed_time(ev[3]) == before
+    # the unfused path: start at its first kernel, stop at its last
+    ws = torch.empty(b.basp_unfused_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
+    b.basp_time_next_call(ev[0], ev[1])
+    b.basp_seq_to_head_unfused(plan, q, k, v, out, ws)
+    torch.cuda.synchronize()
+    assert ev[0].elapsed_time(ev[1]) > 0
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))

@@ -35,7 +35,7 @@ def emu(tmp_path_factory):
     lib.basp_plan_create_ex.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32]
     lib.basp_plan_create_ex.restype = vp
     lib.basp_plan_destroy.argtypes = [vp]
-    lib.basp_plan_set_tuning.argtypes = [vp, ctypes.POINTER(ctypes.c_int32 * 5)]
+    lib.basp_plan_set_tuning.argtypes = [vp, ctypes.POINTER(ctypes.c_int32 * 7)]
     lib.basp_plan_set_tuning.restype = i32
     tail = [ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_int)]
     lib.emu_seq_to_head.argtypes = [vp, vp, vp, vp, vp] + tail
@@ -57,8 +57,9 @@ class Run:
         self.plan = lib.basp_plan_create_ex(N, B, S, Hq, Hkv, d, dtype, mode, layout)
         assert self.plan, "plan rejected"
         if tuning:
-            t = (ctypes.c_int32 * 5)(*[tuning.get(k, 0) for k in (
-                "vectors_per_thread", "tile_tokens", "tile_heads", "cache_policy", "max_grid")])
+            t = (ctypes.c_int32 * 7)(*[tuning.get(k, 0) for k in (
+                "vectors_per_thread", "tile_tokens", "tile_heads", "cache_policy", "max_grid",
+                "lane_order", "xcd_remap")])
             assert lib.basp_plan_set_tuning(self.plan, ctypes.byref(t)) == 0
 
     def __call__(self, fn, *arrays):
@@ -138,7 +139,10 @@ def test_ragged(emu, shape, es, layout, mode):
 TUNINGS = [dict(vectors_per_thread=1), dict(vectors_per_thread=2), dict(vectors_per_thread=8),
            dict(tile_tokens=1), dict(tile_tokens=3, tile_heads=2), dict(tile_tokens=100, tile_heads=3),
            dict(tile_heads=4), dict(max_grid=7), dict(max_grid=1),
-           dict(vectors_per_thread=8, tile_tokens=5, tile_heads=1, cache_policy=3, max_grid=3)]
+           dict(vectors_per_thread=8, tile_tokens=5, tile_heads=1, cache_policy=3, max_grid=3),
+           dict(lane_order=1), dict(lane_order=2), dict(lane_order=2, tile_heads=3, tile_tokens=7),
+           dict(xcd_remap=2), dict(xcd_remap=2, max_grid=24), dict(xcd_remap=2, max_grid=13, lane_order=2),
+           dict(xcd_remap=1, lane_order=1, vectors_per_thread=1)]
 
 
 @pytest.mark.parametrize("tuning", TUNINGS, ids=lambda t: ",".join("%s=%s" % kv for kv in t.items()))
