@@ -9,16 +9,20 @@ after it, on the Llama-3.2-1B-shaped workload by default (N = 8 virtual
 ranks, B = 2, S = 16384, Hq = 32, Hkv = 8, d = 64, bf16, BASP mode: 2 groups
 of K = 4).  Inputs are seeded synthetic N(0, 1) bf16 values resident in HBM
 before timing starts; R buffer sets rotate so that no step finds its bytes in
-the 256 MB Infinity Cache.
+the 256 MB Infinity Cache.  Each plan's launch shapes are chosen by
+basp_plan_autotune before anything is timed (--no-autotune keeps the
+built-in ones).
 
 Printed: one JSON line.  ``value`` is effective HBM GB/s of the whole step
 (algorithmic bytes: every input byte read once, every output byte written
 once) over wall time of K steps bracketed by device synchronisation.
 ``roofline`` is the fused seq->head kernel (the larger of the two) against
 the 8 TB/s HBM peak, its duration taken from HIP events that its own launch
-records (hipExtLaunchKernel start/stop timestamps, via basp_time_next_call) on
-the stream it runs on.  ``detail`` holds per-kernel rates of both modes, the unfused three-pass
-baseline and a plain device copy.  ``cpu_baseline`` is the CPU oracle doing
+records (hipExtLaunchKernel start/stop timestamps, via basp_time_next_call)
+on the stream it runs on.  ``detail`` holds per-kernel rates of both modes,
+the unfused three-pass baseline, the backward entry points, the token-major
+layout and a plain device copy; ``workloads`` the fused seq->head and
+head->seq rates of every named workload in both modes.  ``cpu_baseline`` is the CPU oracle doing
 the same step on the host, repeated for about --cpu-seconds.
 
     python bench.py --pmc-summary FETCH_DIR WRITE_DIR
@@ -51,6 +55,7 @@ KERNEL_SOURCES = ["sequence_re_layout_amd/csrc/relayout.hip", "sequence_re_layou
                   "sequence_re_layout_amd/csrc/launch.cpp", "sequence_re_layout_amd/csrc/fastdiv.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 CALIB_BYTES = 256 << 20   # plain copy used to scale the PMC byte counters
+MARKER_CYCLES = 1000      # torch's spin kernel, brackets the timed region
 
 
 def kernel_sources_sha256() -> str:
@@ -70,7 +75,11 @@ def parse_args(argv=None):
     ap.add_argument("--mode", choices=["basp", "ulysses"], default="basp")
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough for > 1 GiB reuse distance)")
     ap.add_argument("--detail-iters", type=int, default=100)
+    ap.add_argument("--no-autotune", action="store_true",
+                    help="keep the built-in launch shapes instead of measuring them per plan")
     ap.add_argument("--no-detail", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the table of every named workload")
+    ap.add_argument("--workload-iters", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -83,7 +92,7 @@ class Workload:
     """Device buffers of one workload: R rotating sets of Q/K/V/out and
     O/out, filled from the same seeded host data."""
 
-    def __init__(self, b, name, mode, rotate):
+    def __init__(self, b, name, mode, rotate, autotune=True):
         import torch
         from sequence_re_layout_amd import inputs, workloads
         self.name, N, B, S, Hq, Hkv, d = workloads.BY_NAME[name]
@@ -109,6 +118,10 @@ class Workload:
             s["o_out"] = torch.empty(i["q_elems"], dtype=torch.bfloat16, device="cuda")
             self.sets.append(s)
         torch.cuda.synchronize()
+        if autotune:   # plan-time measurement, before anything is timed
+            s = self.sets[0]
+            b.basp_plan_autotune(self.plan, s["q"], s["k"], s["v"], s["qkv_out"], s["o"], s["o_out"])
+            torch.cuda.synchronize()
 
 
 def make_events(n):
@@ -155,7 +168,7 @@ def run_gpu(args):
     from sequence_re_layout_amd import binding as b
 
     torch.cuda.set_device(0)
-    w = Workload(b, args.workload, args.mode, args.rotate)
+    w = Workload(b, args.workload, args.mode, args.rotate, not args.no_autotune)
     plan, sets = w.plan, w.sets
 
     def s2h(i):
@@ -172,8 +185,11 @@ def run_gpu(args):
     torch.cuda.synchronize()
 
     # timed region: K steps; each kernel carries its own start/stop events
-    # (dispatch timestamps), so nothing extra is queued between the kernels
+    # (dispatch timestamps), so nothing extra is queued between the kernels.
+    # A tiny marker kernel before and after it lets a profiler trace find the
+    # timed launches among the plan-time measurements.
     ev = make_events(4 * args.steps)
+    torch.cuda._sleep(MARKER_CYCLES)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -183,6 +199,7 @@ def run_gpu(args):
         h2s(i % w.R)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    torch.cuda._sleep(MARKER_CYCLES)
     s2h_t = [ev[4 * i].elapsed_time(ev[4 * i + 1]) * 1e-3 for i in range(args.steps)]
     h2s_t = [ev[4 * i + 2].elapsed_time(ev[4 * i + 3]) * 1e-3 for i in range(args.steps)]
 
@@ -213,19 +230,33 @@ def run_gpu(args):
     torch.cuda.synchronize()
     res["round_trip_bit_exact"] = bool(torch.equal(back.view(torch.int16), s["q"].view(torch.int16)))
 
+    # a plain copy of known size: the PMC byte counters are scaled by it
+    cal_src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    cal_dst = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+
     if not args.no_detail:
         res["detail"] = detail(args, b, w)
+    if not args.no_workloads:
+        res["workloads"] = workload_table(b, args.workload_iters, not args.no_autotune)
+    res["tuning"] = {"seq_to_head": b.basp_plan_get_tuning(plan, b.BASP_SEQ_TO_HEAD),
+                     "head_to_seq": b.basp_plan_get_tuning(plan, b.BASP_HEAD_TO_SEQ),
+                     "autotuned": not args.no_autotune}
     res["w"] = w
     return res
 
 
 def detail(args, b, w):
-    """Per-kernel rates of both modes, the unfused baseline and a plain copy."""
+    """Per-kernel rates of both modes, the unfused baseline, the backward
+    entry points, the token-major layout and a plain device copy."""
     import torch
     out = {}
     n = args.detail_iters
+    med = statistics.median
     for mode in ("basp", "ulysses"):
-        ww = w if mode == w.mode else Workload(b, w.name, mode, w.R)
+        ww = w if mode == w.mode else Workload(b, w.name, mode, w.R, not args.no_autotune)
         p, sets = ww.plan, ww.sets
         t = time_launches(b, lambda i: b.basp_seq_to_head(p, sets[i]["q"], sets[i]["k"], sets[i]["v"],
                                                           sets[i]["qkv_out"]), n, ww.R)
@@ -234,20 +265,44 @@ def detail(args, b, w):
         out[mode] = {
             "G": info["G"], "P": info["P"], "Bl": info["Bl"], "peers_per_rank": info["peers_per_rank"],
             "cross_rank_bytes_qkv": info["cross_rank_bytes_q"] + 2 * info["cross_rank_bytes_kv"],
-            "s2h_median_us": statistics.median(t) * 1e6,
-            "s2h_gbs": rate(ww.s2h_bytes, statistics.median(t)),
-            "s2h_frac_of_peak": rate(ww.s2h_bytes, statistics.median(t)) / HBM_PEAK_GBS,
-            "h2s_median_us": statistics.median(u) * 1e6,
-            "h2s_gbs": rate(ww.h2s_bytes, statistics.median(u)),
-            "h2s_frac_of_peak": rate(ww.h2s_bytes, statistics.median(u)) / HBM_PEAK_GBS,
+            "s2h_median_us": med(t) * 1e6,
+            "s2h_gbs": rate(ww.s2h_bytes, med(t)),
+            "s2h_frac_of_peak": rate(ww.s2h_bytes, med(t)) / HBM_PEAK_GBS,
+            "h2s_median_us": med(u) * 1e6,
+            "h2s_gbs": rate(ww.h2s_bytes, med(u)),
+            "h2s_frac_of_peak": rate(ww.h2s_bytes, med(u)) / HBM_PEAK_GBS,
         }
         if mode == w.mode:
             ws = torch.empty(b.basp_unfused_workspace_bytes(p), dtype=torch.uint8, device="cuda")
             f = time_launches(b, lambda i: b.basp_seq_to_head_unfused(
                 p, sets[i]["q"], sets[i]["k"], sets[i]["v"], sets[i]["qkv_out"], ws), max(10, n // 4), ww.R)
-            out[mode]["s2h_unfused_median_us"] = statistics.median(f) * 1e6
-            out[mode]["s2h_unfused_gbs"] = rate(ww.s2h_bytes, statistics.median(f))
+            out[mode]["s2h_unfused_median_us"] = med(f) * 1e6
+            out[mode]["s2h_unfused_gbs"] = rate(ww.s2h_bytes, med(f))
             del ws
+            # backward: dO seq->head (O-shaped, reuses the O buffers) and the
+            # fused dQ/dK/dV head->seq (reads the fused buffer, writes q/k/v-shaped)
+            grads = [{"dq": torch.empty_like(s["q"]), "dk": torch.empty_like(s["k"]),
+                      "dv": torch.empty_like(s["v"])} for s in sets]
+            bo = time_launches(b, lambda i: b.basp_seq_to_head_o(p, sets[i]["o"], sets[i]["o_out"]), n, ww.R)
+            bq = time_launches(b, lambda i: b.basp_head_to_seq_qkv(
+                p, sets[i]["qkv_out"], grads[i]["dq"], grads[i]["dk"], grads[i]["dv"]), n, ww.R)
+            out[mode]["backward"] = {
+                "do_s2h_gbs": rate(ww.h2s_bytes, med(bo)), "do_s2h_median_us": med(bo) * 1e6,
+                "dqkv_h2s_gbs": rate(ww.s2h_bytes, med(bq)), "dqkv_h2s_median_us": med(bq) * 1e6}
+            del grads
+            # head shards in token-major order ([Bl][S][Hl][d])
+            N, B, S, Hq, Hkv, d = ww.shape
+            pt = b.basp_plan_create_ex(N, B, S, Hq, Hkv, d, b.BASP_BF16,
+                                       b.BASP_MODE_BASP if mode == "basp" else b.BASP_MODE_ULYSSES,
+                                       b.BASP_LAYOUT_TOKEN_MAJOR)
+            if not args.no_autotune:
+                s0 = sets[0]
+                b.basp_plan_autotune(pt, s0["q"], s0["k"], s0["v"], s0["qkv_out"], s0["o"], s0["o_out"])
+            tt = time_launches(b, lambda i: b.basp_seq_to_head(pt, sets[i]["q"], sets[i]["k"], sets[i]["v"],
+                                                               sets[i]["qkv_out"]), n, ww.R)
+            tu = time_launches(b, lambda i: b.basp_head_to_seq(pt, sets[i]["o"], sets[i]["o_out"]), n, ww.R)
+            out[mode]["token_major"] = {"s2h_gbs": rate(ww.s2h_bytes, med(tt)),
+                                        "h2s_gbs": rate(ww.h2s_bytes, med(tu))}
         if ww is not w:
             del ww
             torch.cuda.empty_cache()
@@ -257,12 +312,47 @@ def detail(args, b, w):
     src = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(4)]
     dst = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(4)]
     c = time_torch(lambda i: dst[i].copy_(src[i]), n, 4)
-    out["device_copy"] = {"bytes_moved": 2 * nb, "median_us": statistics.median(c) * 1e6,
-                          "gbs": rate(2 * nb, statistics.median(c))}
-    cal_src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
-    cal_dst = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
-    cal_dst.copy_(cal_src)
-    torch.cuda.synchronize()
+    out["device_copy"] = {"bytes_moved": 2 * nb, "median_us": med(c) * 1e6,
+                          "gbs": rate(2 * nb, med(c))}
+    del src, dst
+    return out
+
+
+def workload_table(b, iters, autotune):
+    """Fused seq->head and head->seq rates of every named workload in both
+    modes (device-filled random bf16: the rate does not depend on values)."""
+    import torch
+    from sequence_re_layout_amd import workloads
+    out = {}
+    for (name, N, B, S, Hq, Hkv, d) in workloads.ALL + workloads.EXTRA:
+        out[name] = {}
+        for mode, code in (("basp", b.BASP_MODE_BASP), ("ulysses", b.BASP_MODE_ULYSSES)):
+            p = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, code)
+            i = p.info
+            R = max(2, -(-(3 << 30) // (i["qkv_bytes_moved"] + i["o_bytes_moved"])))
+            sets = []
+            for _ in range(R):
+                x = torch.empty(2 * i["q_elems"] + 2 * i["kv_elems"], dtype=torch.bfloat16, device="cuda").normal_()
+                sets.append({"q": x[:i["q_elems"]], "k": x[i["q_elems"]:i["q_elems"] + i["kv_elems"]],
+                             "v": x[i["q_elems"] + i["kv_elems"]:i["q_elems"] + 2 * i["kv_elems"]],
+                             "o": x[i["q_elems"] + 2 * i["kv_elems"]:],
+                             "out": torch.empty(i["qkv_elems"], dtype=torch.bfloat16, device="cuda"),
+                             "o_out": torch.empty(i["q_elems"], dtype=torch.bfloat16, device="cuda")})
+            if autotune:
+                b.basp_plan_autotune(p, sets[0]["q"], sets[0]["k"], sets[0]["v"], sets[0]["out"],
+                                     sets[0]["o"], sets[0]["o_out"])
+            t = statistics.median(time_launches(b, lambda j: b.basp_seq_to_head(
+                p, sets[j]["q"], sets[j]["k"], sets[j]["v"], sets[j]["out"]), iters, R))
+            u = statistics.median(time_launches(b, lambda j: b.basp_head_to_seq(
+                p, sets[j]["o"], sets[j]["o_out"]), iters, R))
+            out[name][mode] = {
+                "G": i["G"], "P": i["P"], "Bl": i["Bl"], "peers_per_rank": i["peers_per_rank"],
+                "s2h_bytes": i["qkv_bytes_moved"], "s2h_us": t * 1e6,
+                "s2h_gbs": rate(i["qkv_bytes_moved"], t), "s2h_frac": rate(i["qkv_bytes_moved"], t) / HBM_PEAK_GBS,
+                "h2s_bytes": i["o_bytes_moved"], "h2s_us": u * 1e6,
+                "h2s_gbs": rate(i["o_bytes_moved"], u), "h2s_frac": rate(i["o_bytes_moved"], u) / HBM_PEAK_GBS}
+            del sets
+            torch.cuda.empty_cache()
     return out
 
 
@@ -333,17 +423,22 @@ def pmc_summary(fetch_dir, write_dir):
     out = {"workload": None, "kernel_sources_sha256": kernel_sources_sha256()}
     for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
         rows = load(d, counter)
+        # the timed launches: between the two marker kernels of the run
+        marks = [i for i, r in enumerate(rows) if "spin_kernel" in r["Kernel_Name"]]
+        if len(marks) < 2:
+            raise SystemExit("no timed-region markers for %s" % counter)
+        timed = rows[marks[0] + 1:marks[1]]
         # the fused seq->head kernel: tile_kernel<VW, VPT, POLICY, true>
-        fused = [r for r in rows if "tile_kernel<" in r["Kernel_Name"] and "true>" in r["Kernel_Name"]]
-        copies = [r for r in rows if "copy" in r["Kernel_Name"].lower()]
+        fused = [r for r in timed if "tile_kernel<" in r["Kernel_Name"] and "true>" in r["Kernel_Name"]]
+        copies = [r for r in rows[marks[1]:] if "copy" in r["Kernel_Name"].lower()]
         if not fused or not copies:
             raise SystemExit("missing fused or copy dispatches for %s" % counter)
-        # the calibration copy is the last copy of the run (CALIB_BYTES each way)
-        cal = float(copies[-1]["Counter_Value"])
+        # the calibration copy is the first copy after the timed region
+        cal = float(copies[0]["Counter_Value"])
         factor = (CALIB_BYTES / 1024.0) / cal
         kib = statistics.median(float(r["Counter_Value"]) for r in fused)
         out["kernel"] = fused[0]["Kernel_Name"]
-        out[counter] = {"kib_per_launch_raw": kib, "copy_kernel": copies[-1]["Kernel_Name"],
+        out[counter] = {"kib_per_launch_raw": kib, "copy_kernel": copies[0]["Kernel_Name"],
                         "copy_kib_raw": cal, "scale": factor,
                         "bytes_per_launch": kib * factor * 1024.0, "launches": len(fused)}
     out["traffic_bytes_per_launch"] = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
@@ -386,7 +481,8 @@ def main(argv=None):
         "data": "synthetic: seeded N(0,1) bf16 Q/K/V/O, resident in HBM, %d rotating buffer sets" % r["rotate_sets"],
         "config": {"workload": w.name, "N": N, "B": B, "S": S, "Hq": Hq, "Hkv": Hkv, "d": d,
                    "mode": w.mode, "parallelism": "%d virtual ranks on 1 GPU" % N,
-                   "step": "fused QKV seq->head + O head->seq", "step_bytes": r["step_bytes"]},
+                   "step": "fused QKV seq->head + O head->seq", "step_bytes": r["step_bytes"],
+                   "launch_shape": r["tuning"]},
         "roofline": {"bound": "hbm", "kernel": "fused QKV seq->head (tile_kernel)",
                      "achieved": r["s2h_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": r["s2h_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
@@ -397,6 +493,8 @@ def main(argv=None):
     }
     if "detail" in r:
         line["detail"] = r["detail"]
+    if "workloads" in r:
+        line["workloads"] = r["workloads"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, w)
     print(json.dumps(line), flush=True)

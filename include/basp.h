@@ -204,24 +204,36 @@ basp_status basp_seq_to_head_unfused(const basp_plan *plan, const void *q, const
                                      const void *v, void *out, void *ws, void *stream);
 
 /*
- * Launch shape of a plan, for tuning sweeps.  Zero fields keep the built-in
- * choice, which depends on the direction and on the row size d*elem_size
- * (measured on MI355X over the Llama/Qwen attention shapes).  Results never
- * depend on these values, only the speed does.
+ * Launch shape of a plan, per direction: BASP_SEQ_TO_HEAD applies to
+ * basp_seq_to_head and basp_seq_to_head_o, BASP_HEAD_TO_SEQ to
+ * basp_head_to_seq and basp_head_to_seq_qkv (the unfused baseline has a
+ * fixed shape).  Zero fields keep the built-in choice, which depends on the
+ * direction and on the row size d*elem_size (measured on MI355X over the
+ * Llama/Qwen attention shapes).  Results never depend on these values, only
+ * the speed does.
  *   vectors_per_thread   1, 2, 4 or 8 (16-byte vectors held in flight per lane)
  *   tile_tokens          tokens per work tile (>= 1)
  *   tile_heads           heads per work tile (>= 1, clamped to H/P)
  *   cache_policy         1 = plain loads and stores, 2 = non-temporal stores,
  *                        3 = non-temporal loads and stores (built-in)
  *   max_grid             cap on work-groups per launch (tiles loop beyond it)
- *   lane_order           1 = lanes run along tokens first, 2 = along heads
- *                        first (built-in)
+ *   lane_order           1 = lanes run along tokens first, 2 = along heads first
  *   xcd_remap            1 = tiles in work-group order, 2 = each of the 8 XCDs
- *                        takes one contiguous eighth of the tiles (built-in)
- * BASP_ERR_INVALID on a NULL plan or an out-of-range value,
- * BASP_ERR_UNSUPPORTED when the shape exceeds the index limits.  Not
- * thread-safe against concurrent launches with the same plan.
+ *                        takes one contiguous eighth of the tiles
+ *   tile_order           1 = token blocks fastest (the head-sharded side's
+ *                        order), 2 = head blocks fastest (the sequence-sharded
+ *                        side's order)
+ * basp_plan_set_tuning sets both directions, basp_plan_set_direction_tuning
+ * one; basp_plan_get_tuning reads one.  Errors: BASP_ERR_INVALID on a NULL
+ * argument, an unknown direction or an out-of-range field;
+ * BASP_ERR_UNSUPPORTED when the shape exceeds the index limits.  A plan's
+ * tuning must not change while another thread launches with it.
  */
+typedef enum basp_direction {
+    BASP_SEQ_TO_HEAD = 0,
+    BASP_HEAD_TO_SEQ = 1
+} basp_direction;
+
 typedef struct basp_tuning {
     int32_t vectors_per_thread;
     int32_t tile_tokens;
@@ -230,9 +242,27 @@ typedef struct basp_tuning {
     int32_t max_grid;
     int32_t lane_order;
     int32_t xcd_remap;
+    int32_t tile_order;
 } basp_tuning;
 basp_status basp_plan_set_tuning(basp_plan *plan, const basp_tuning *tuning);
-basp_status basp_plan_get_tuning(const basp_plan *plan, basp_tuning *tuning);
+basp_status basp_plan_set_direction_tuning(basp_plan *plan, basp_direction dir,
+                                           const basp_tuning *tuning);
+basp_status basp_plan_get_tuning(const basp_plan *plan, basp_direction dir, basp_tuning *tuning);
+
+/*
+ * Choose the launch shape of both directions by measurement on the caller's
+ * buffers (as a planner that times candidates): a fixed set of launch shapes
+ * is timed for seq->head on (q, k, v -> qkv) and for head->seq on
+ * (o -> o_out), and the fastest of each is stored in the plan, replacing its
+ * tuning.  The buffers are those of basp_seq_to_head and basp_head_to_seq,
+ * with the same checks; qkv and o_out are overwritten.  Runs on stream and
+ * waits for it; creates and destroys HIP events but allocates no device
+ * memory.  A pending basp_time_next_call request is dropped.  Errors as for
+ * the two calls; on BASP_ERR_HIP the plan keeps its previous tuning.  The
+ * plan must not be used by another thread meanwhile.
+ */
+basp_status basp_plan_autotune(basp_plan *plan, const void *q, const void *k, const void *v,
+                               void *qkv, const void *o, void *o_out, void *stream);
 
 /*
  * Kernel timing without extra work on the stream.  The next call of this

@@ -35,6 +35,9 @@ BASP_MODE_BASP = 1
 BASP_LAYOUT_HEAD_MAJOR = 0
 BASP_LAYOUT_TOKEN_MAJOR = 1
 
+BASP_SEQ_TO_HEAD = 0
+BASP_HEAD_TO_SEQ = 1
+
 
 class basp_plan_info(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("N", "B", "Hq", "Hkv", "d", "elem_size")] + [
@@ -54,7 +57,7 @@ class basp_plan_info(ctypes.Structure):
 class basp_tuning(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "vectors_per_thread", "tile_tokens", "tile_heads", "cache_policy", "max_grid",
-        "lane_order", "xcd_remap")]
+        "lane_order", "xcd_remap", "tile_order")]
 
 
 class BaspError(RuntimeError):
@@ -99,8 +102,12 @@ _lib.basp_seq_to_head_unfused.argtypes = [_plan_p, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.basp_seq_to_head_unfused.restype = _i32
 _lib.basp_plan_set_tuning.argtypes = [_plan_p, ctypes.POINTER(basp_tuning)]
 _lib.basp_plan_set_tuning.restype = _i32
-_lib.basp_plan_get_tuning.argtypes = [_plan_p, ctypes.POINTER(basp_tuning)]
+_lib.basp_plan_set_direction_tuning.argtypes = [_plan_p, _i32, ctypes.POINTER(basp_tuning)]
+_lib.basp_plan_set_direction_tuning.restype = _i32
+_lib.basp_plan_get_tuning.argtypes = [_plan_p, _i32, ctypes.POINTER(basp_tuning)]
 _lib.basp_plan_get_tuning.restype = _i32
+_lib.basp_plan_autotune.argtypes = [_plan_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.basp_plan_autotune.restype = _i32
 _lib.basp_time_next_call.argtypes = [_vp, _vp]
 _lib.basp_time_next_call.restype = _i32
 _lib.basp_last_error.argtypes = []
@@ -171,17 +178,44 @@ def basp_plan_query(plan: Plan) -> dict:
     return info.as_dict()
 
 
-def basp_plan_set_tuning(plan: Plan, vectors_per_thread=0, tile_tokens=0, tile_heads=0,
-                         cache_policy=0, max_grid=0, lane_order=0, xcd_remap=0) -> None:
-    t = basp_tuning(vectors_per_thread, tile_tokens, tile_heads, cache_policy, max_grid,
-                    lane_order, xcd_remap)
+_TUNING_FIELDS = ("vectors_per_thread", "tile_tokens", "tile_heads", "cache_policy", "max_grid",
+                  "lane_order", "xcd_remap", "tile_order")
+
+
+def _tuning(fields) -> basp_tuning:
+    unknown = set(fields) - set(_TUNING_FIELDS)
+    if unknown:
+        raise TypeError("unknown tuning fields %s" % sorted(unknown))
+    return basp_tuning(*[int(fields.get(n, 0)) for n in _TUNING_FIELDS])
+
+
+def basp_plan_set_tuning(plan: Plan, **fields) -> None:
+    """Launch shape of both directions (fields of basp_tuning; unset = 0)."""
+    t = _tuning(fields)
     _check(_lib.basp_plan_set_tuning(plan.handle, ctypes.byref(t)), "basp_plan_set_tuning")
 
 
-def basp_plan_get_tuning(plan: Plan) -> dict:
+def basp_plan_set_direction_tuning(plan: Plan, direction: int, **fields) -> None:
+    t = _tuning(fields)
+    _check(_lib.basp_plan_set_direction_tuning(plan.handle, direction, ctypes.byref(t)),
+           "basp_plan_set_direction_tuning")
+
+
+def basp_plan_get_tuning(plan: Plan, direction: int = BASP_SEQ_TO_HEAD) -> dict:
     t = basp_tuning()
-    _check(_lib.basp_plan_get_tuning(plan.handle, ctypes.byref(t)), "basp_plan_get_tuning")
+    _check(_lib.basp_plan_get_tuning(plan.handle, direction, ctypes.byref(t)), "basp_plan_get_tuning")
     return {name: getattr(t, name) for name, _ in t._fields_}
+
+
+def basp_plan_autotune(plan: Plan, q, k, v, qkv, o, o_out, stream=None) -> None:
+    """Measure launch shapes on these buffers and keep the fastest per
+    direction (qkv and o_out are overwritten)."""
+    i = plan.info
+    _check(_lib.basp_plan_autotune(
+        plan.handle, _ptr(q, plan, i["q_elems"], "q"), _ptr(k, plan, i["kv_elems"], "k"),
+        _ptr(v, plan, i["kv_elems"], "v"), _ptr(qkv, plan, i["qkv_elems"], "qkv"),
+        _ptr(o, plan, i["q_elems"], "o"), _ptr(o_out, plan, i["q_elems"], "o_out"),
+        _stream(stream)), "basp_plan_autotune")
 
 
 def basp_time_next_call(start_event, stop_event) -> None:

@@ -16,19 +16,24 @@ namespace {
 constexpr uint32_t kGridCap = 1u << 22;  // work-groups per launch at most
 
 // Launch shape of one tile launch: the plan's tuning where set, else the
-// defaults below.  The defaults come from sweeps on MI355X over every named
-// workload (Llama/Qwen shapes, 128- and 256-byte rows, both modes):
-//   - non-temporal loads and stores: each byte is touched exactly once;
-//   - XCD-contiguous tile order: each XCD streams one contiguous eighth;
-//   - about 4 KiB per tile for seq->head (one 16-byte vector per lane), with
-//     4 heads per tile for 128-byte rows and 1 for longer rows;
-//   - 8 KiB per tile for head->seq with 4 heads per tile, and a grid capped
-//     at 8192 work-groups for 128-byte rows.
+// defaults below, chosen on MI355X over every named workload (Llama/Qwen
+// shapes, 128- and 256-byte rows, both modes) as the launch shape whose worst
+// ratio to each workload's best was highest.  Common to all: non-temporal
+// loads and stores.  seq->head walks tiles token block first (the
+// head-sharded destination's order) with 4 heads per tile for 128-byte rows
+// (2 vectors per lane, 8 KiB tiles) and 1 head for longer rows (1 vector per
+// lane); head->seq walks them head block first (the sequence-sharded
+// destination's order) with 4 heads per tile and 4 vectors per lane for
+// 128-byte rows, 8 heads and 2 vectors for longer rows.  Lanes run along
+// heads first, except for head->seq with long rows; each XCD takes one
+// contiguous eighth of the tiles, except for head->seq with long rows.
+// basp_plan_autotune replaces these by measurement.
 struct Shape {
     int vpt, policy;
     uint32_t tile_tokens, tile_heads;   // tile_tokens 0: derived
     bool heads_given;                   // tile_heads set by the tuning
     bool s_fast;
+    bool heads_first;
     uint32_t grid_cap;
     bool xcd;
 };
@@ -37,14 +42,15 @@ Shape resolve(const basp_plan &p, const basp_tuning &t, bool s2h)
 {
     const bool short_rows = p.row_bytes <= 128;
     Shape s;
-    s.vpt = t.vectors_per_thread ? t.vectors_per_thread : (s2h ? 1 : 2);
+    s.vpt = t.vectors_per_thread ? t.vectors_per_thread : (s2h ? (short_rows ? 2 : 1) : (short_rows ? 4 : 2));
     s.policy = t.cache_policy ? t.cache_policy : 3;
     s.tile_tokens = uint32_t(t.tile_tokens);
-    s.tile_heads = t.tile_heads ? uint32_t(t.tile_heads) : (s2h && !short_rows ? 1 : 4);
+    s.tile_heads = t.tile_heads ? uint32_t(t.tile_heads) : (s2h ? (short_rows ? 4 : 1) : (short_rows ? 4 : 8));
     s.heads_given = t.tile_heads != 0;
-    s.s_fast = t.lane_order ? t.lane_order == 1 : false;
-    s.grid_cap = t.max_grid ? uint32_t(t.max_grid) : (!s2h && short_rows ? 8192u : kGridCap);
-    s.xcd = t.xcd_remap ? t.xcd_remap == 2 : true;
+    s.s_fast = t.lane_order ? t.lane_order == 1 : (!s2h && !short_rows);
+    s.heads_first = t.tile_order ? t.tile_order == 2 : !s2h;
+    s.grid_cap = t.max_grid ? uint32_t(t.max_grid) : kGridCap;
+    s.xcd = t.xcd_remap ? t.xcd_remap == 2 : (s2h || short_rows);
     return s;
 }
 
@@ -154,11 +160,12 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
     }
     const int vw = vector_width(p, addrs, 2 * nseg);
     const uint32_t A = uint32_t(p.row_bytes / vw);
-    const Shape sh = resolve(p, p.tuning, s2h);
+    const Shape sh = resolve(p, p.tuning[s2h ? BASP_SEQ_TO_HEAD : BASP_HEAD_TO_SEQ], s2h);
     TileDesc &D = L.D;
     D.St = uint32_t(p.St);
     D.row = uint32_t(p.row_bytes);
     D.s_fast = sh.s_fast;
+    D.heads_first = sh.heads_first;
     D.P = make_fastdiv(p.P);
     D.Bl = make_fastdiv(p.Bl);
     D.A = make_fastdiv(A);
@@ -286,28 +293,26 @@ int build_perm(const basp_plan &p, const PermSpec *ps, int n, int vw, PermLaunch
 
 }  // namespace
 
-basp_status check_launch_limits(const basp_plan &p, const basp_tuning &t)
+basp_status check_launch_limits(const basp_plan &p, const basp_tuning &t, bool s2h)
 {
     if (p.St > int64_t(kI31Max) || p.row_bytes > int64_t(kI31Max) ||
         int64_t(p.Hq) * p.row_bytes > int64_t(kI31Max))
         return BASP_ERR_UNSUPPORTED;
+    const Shape sh = resolve(p, t, s2h);
+    const uint32_t heads[3] = {uint32_t(p.Hq), uint32_t(p.Hkv), uint32_t(p.Hkv)};
     for (int vw = 16; vw >= p.es; vw /= 2) {
         if (p.row_bytes % vw)
             continue;
         const uint32_t A = uint32_t(p.row_bytes / vw);
-        const uint32_t heads[3] = {uint32_t(p.Hq), uint32_t(p.Hkv), uint32_t(p.Hkv)};
-        for (const bool s2h : {true, false}) {
-            const Shape sh = resolve(p, t, s2h);
-            uint64_t total = 0;
-            for (int i = 0; i < 3; ++i) {
-                TileShape ts;
-                if (!fitted_shape(p, sh, heads[i], A, ts))
-                    return BASP_ERR_UNSUPPORTED;
-                total += ts.ntiles;
-            }
-            if (total > kI31Max)
+        uint64_t total = 0;
+        for (int i = 0; i < 3; ++i) {
+            TileShape ts;
+            if (!fitted_shape(p, sh, heads[i], A, ts))
                 return BASP_ERR_UNSUPPORTED;
+            total += ts.ntiles;
         }
+        if (total > kI31Max)
+            return BASP_ERR_UNSUPPORTED;
     }
     return BASP_OK;
 }

@@ -15,8 +15,11 @@
 //     head-major        h*S*row + t*row
 //     token-major       t*Hl*row + h*row
 // so a work-group computes the tile's two base addresses once and each lane
-// only adds 32-bit offsets.  Tiles are numbered (g, jh, bl, hb, js, tb) with
-// the token block tb fastest.
+// only adds 32-bit offsets.  Tiles are numbered either (g, jh, bl, hb, js, tb),
+// token block tb fastest, the order of the head-sharded layout, or
+// (g, js, bl, tb, jh, hb), head block hb fastest, the order of the
+// sequence-sharded layout: neighbouring tiles, which run at the same time,
+// then share the DRAM pages of one side.
 //
 // Perm kernel (unfused baseline).  Writes its destination linearly; row i of
 // the destination has digits (d0..d4), d4 fastest, and is read from source
@@ -62,6 +65,7 @@ struct TileDesc {
     uint32_t St;
     uint32_t row;                  // bytes per (token, head) row
     uint32_t s_fast;               // lanes along tokens (1) or heads (0)
+    uint32_t heads_first;          // tile order: head block fastest (1) or token block (0)
     uint32_t xcd_span;             // tiles per XCD when remapped, else 0
     FastDiv P, Bl, A;              // group size, sequences per group, vectors per row
 };
@@ -92,11 +96,30 @@ BASP_HD inline TileOrigin tile_origin(const TileDesc &D, uint32_t x)
     const TileSeg &sg = D.seg[o.seg];
     const uint32_t P = D.P.d;
     const uint32_t local = tile - sg.tile_begin;
-    const uint32_t q1 = fastdiv(local, sg.ntb), tb = local - q1 * sg.ntb.d;
-    const uint32_t q2 = fastdiv(q1, D.P), js = q1 - q2 * P;
-    const uint32_t q3 = fastdiv(q2, sg.nhb), hb = q2 - q3 * sg.nhb.d;
-    const uint32_t q4 = fastdiv(q3, D.Bl), bl = q3 - q4 * D.Bl.d;
-    const uint32_t g = fastdiv(q4, D.P), jh = q4 - g * P;
+    uint32_t tb, js, hb, bl, g, jh;
+    if (D.heads_first) {   // (g, js, bl, tb, jh, hb)
+        const uint32_t q1 = fastdiv(local, sg.nhb);
+        hb = local - q1 * sg.nhb.d;
+        const uint32_t q2 = fastdiv(q1, D.P);
+        jh = q1 - q2 * P;
+        const uint32_t q3 = fastdiv(q2, sg.ntb);
+        tb = q2 - q3 * sg.ntb.d;
+        const uint32_t q4 = fastdiv(q3, D.Bl);
+        bl = q3 - q4 * D.Bl.d;
+        g = fastdiv(q4, D.P);
+        js = q4 - g * P;
+    } else {               // (g, jh, bl, hb, js, tb)
+        const uint32_t q1 = fastdiv(local, sg.ntb);
+        tb = local - q1 * sg.ntb.d;
+        const uint32_t q2 = fastdiv(q1, D.P);
+        js = q1 - q2 * P;
+        const uint32_t q3 = fastdiv(q2, sg.nhb);
+        hb = q2 - q3 * sg.nhb.d;
+        const uint32_t q4 = fastdiv(q3, D.Bl);
+        bl = q3 - q4 * D.Bl.d;
+        g = fastdiv(q4, D.P);
+        jh = q4 - g * P;
+    }
     const uint32_t t0 = tb * sg.Ts, hl0 = hb * sg.Th;
     o.ns = D.St - t0 < sg.Ts ? D.St - t0 : sg.Ts;
     o.nh = sg.Hl - hl0 < sg.Th ? sg.Hl - hl0 : sg.Th;

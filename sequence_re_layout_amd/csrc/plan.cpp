@@ -128,9 +128,11 @@ extern "C" basp_plan *basp_plan_create_ex(int N, int B, int64_t S, int Hq, int H
     p->row_bytes = row;
     p->q_elems = q_elems;
     p->kv_elems = kv_elems;
-    std::memset(&p->tuning, 0, sizeof(p->tuning));
+    std::memset(p->tuning, 0, sizeof(p->tuning));
 
-    const basp_status lim = basp::check_launch_limits(*p, p->tuning);
+    basp_status lim = basp::check_launch_limits(*p, p->tuning[0], true);
+    if (lim == BASP_OK)
+        lim = basp::check_launch_limits(*p, p->tuning[1], false);
     if (lim != BASP_OK) {
         delete p;
         record(lim);
@@ -196,27 +198,49 @@ extern "C" basp_status basp_plan_query(const basp_plan *p, basp_plan_info *info)
     return record(BASP_OK);
 }
 
-extern "C" basp_status basp_plan_set_tuning(basp_plan *p, const basp_tuning *t)
+namespace basp {
+
+bool tuning_in_range(const basp_tuning &t)
 {
-    if (!p || !t)
+    const int v = t.vectors_per_thread;
+    return (v == 0 || v == 1 || v == 2 || v == 4 || v == 8) && t.tile_tokens >= 0 &&
+           t.tile_heads >= 0 && t.cache_policy >= 0 && t.cache_policy <= 3 && t.max_grid >= 0 &&
+           t.lane_order >= 0 && t.lane_order <= 2 && t.xcd_remap >= 0 && t.xcd_remap <= 2 &&
+           t.tile_order >= 0 && t.tile_order <= 2;
+}
+
+}  // namespace basp
+
+extern "C" basp_status basp_plan_set_direction_tuning(basp_plan *p, basp_direction dir,
+                                                      const basp_tuning *t)
+{
+    if (!p || !t || (dir != BASP_SEQ_TO_HEAD && dir != BASP_HEAD_TO_SEQ) || !basp::tuning_in_range(*t))
         return record(BASP_ERR_INVALID);
-    const int v = t->vectors_per_thread;
-    if ((v != 0 && v != 1 && v != 2 && v != 4 && v != 8) || t->tile_tokens < 0 ||
-        t->tile_heads < 0 || t->cache_policy < 0 || t->cache_policy > 3 || t->max_grid < 0 ||
-        t->lane_order < 0 || t->lane_order > 2 || t->xcd_remap < 0 || t->xcd_remap > 2)
-        return record(BASP_ERR_INVALID);
-    const basp_status lim = basp::check_launch_limits(*p, *t);
+    const basp_status lim = basp::check_launch_limits(*p, *t, dir == BASP_SEQ_TO_HEAD);
     if (lim != BASP_OK)
         return record(lim);
-    p->tuning = *t;
+    p->tuning[dir] = *t;
     return record(BASP_OK);
 }
 
-extern "C" basp_status basp_plan_get_tuning(const basp_plan *p, basp_tuning *t)
+extern "C" basp_status basp_plan_set_tuning(basp_plan *p, const basp_tuning *t)
 {
-    if (!p || !t)
+    if (!p || !t || !basp::tuning_in_range(*t))
         return record(BASP_ERR_INVALID);
-    *t = p->tuning;
+    basp_status lim = basp::check_launch_limits(*p, *t, true);
+    if (lim == BASP_OK)
+        lim = basp::check_launch_limits(*p, *t, false);
+    if (lim != BASP_OK)
+        return record(lim);
+    p->tuning[0] = p->tuning[1] = *t;
+    return record(BASP_OK);
+}
+
+extern "C" basp_status basp_plan_get_tuning(const basp_plan *p, basp_direction dir, basp_tuning *t)
+{
+    if (!p || !t || (dir != BASP_SEQ_TO_HEAD && dir != BASP_HEAD_TO_SEQ))
+        return record(BASP_ERR_INVALID);
+    *t = p->tuning[dir];
     return record(BASP_OK);
 }
 

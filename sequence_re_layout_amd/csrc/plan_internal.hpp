@@ -19,8 +19,9 @@ struct basp_plan {
     int32_t Hl_q, Hl_kv;
     int64_t row_bytes;   // d * es: one (token, head) row, the unit every exchange moves whole
     int64_t q_elems, kv_elems;
-    // launch shape; zero fields mean "choose per launch"
-    basp_tuning tuning;
+    // launch shape per direction ([BASP_SEQ_TO_HEAD], [BASP_HEAD_TO_SEQ]);
+    // zero fields mean "choose per launch"
+    basp_tuning tuning[2];
 };
 
 namespace basp {
@@ -28,8 +29,11 @@ namespace basp {
 // Store s as the calling thread's last status and return it.
 basp_status record(basp_status s);
 
-// Check that every launch of this plan fits the kernels' 31/32-bit index
-// arithmetic with the given tuning.  Defined beside the kernels.
-basp_status check_launch_limits(const basp_plan &p, const basp_tuning &t);
+// Fields of a tuning within their documented ranges.
+bool tuning_in_range(const basp_tuning &t);
+
+// Check that every launch of this plan in one direction fits the kernels'
+// 31-bit index arithmetic with the given tuning.
+basp_status check_launch_limits(const basp_plan &p, const basp_tuning &t, bool s2h);
 
 }  // namespace basp

@@ -16,7 +16,9 @@
 
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <cstdint>
+#include <vector>
 
 #define BASP_HD __host__ __device__
 #include "launch.hpp"
@@ -235,10 +237,127 @@ basp_status timed_call(F f)
     return record(s);
 }
 
+// ---------------------------------------------------------------- autotune --
+
+// Launch shapes a plan is measured with: tile order x vectors per lane x
+// heads per tile x lane order x XCD order x grid cap, non-temporal loads and
+// stores (the policy every sweep preferred).
+std::vector<basp_tuning> autotune_candidates()
+{
+    std::vector<basp_tuning> c;
+    for (int to : {1, 2})
+        for (int vpt : {1, 2, 4})
+            for (int th : {1, 2, 4, 8})
+                for (int lo : {1, 2})
+                    for (int xcd : {1, 2})
+                        for (int grid : {0, 8192}) {
+                            basp_tuning t = {};
+                            t.vectors_per_thread = vpt;
+                            t.tile_heads = th;
+                            t.cache_policy = 3;
+                            t.max_grid = grid;
+                            t.lane_order = lo;
+                            t.xcd_remap = xcd;
+                            t.tile_order = to;
+                            c.push_back(t);
+                        }
+    return c;
+}
+
+// Median kernel time (ms) of `reps` launches of one tile launch, each timed
+// from its own dispatch timestamps; after one untimed launch.  -1 on error.
+float time_tile_launch(const TileLaunch &L, void *stream, hipEvent_t *ev, int reps)
+{
+    if (launch(L, stream) != BASP_OK)
+        return -1.f;
+    std::vector<float> ms(reps);
+    for (int r = 0; r < reps; ++r) {
+        t_timing.start = ev[2 * r];
+        t_timing.stop = ev[2 * r + 1];
+        const basp_status s = launch(L, stream);
+        t_timing = Timing();
+        if (s != BASP_OK)
+            return -1.f;
+    }
+    if (hipEventSynchronize(ev[2 * reps - 1]) != hipSuccess)
+        return -1.f;
+    for (int r = 0; r < reps; ++r)
+        if (hipEventElapsedTime(&ms[r], ev[2 * r], ev[2 * r + 1]) != hipSuccess)
+            return -1.f;
+    std::nth_element(ms.begin(), ms.begin() + reps / 2, ms.end());
+    return ms[reps / 2];
+}
+
 }  // namespace
 }  // namespace basp
 
 using basp::record;
+
+extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const void *k,
+                                          const void *v, void *qkv, const void *o, void *o_out,
+                                          void *stream)
+{
+    basp::t_timing = basp::Timing();
+    if (!p)
+        return record(BASP_ERR_INVALID);
+    basp::TileLaunch L;
+    int s = basp::prepare_seq_to_head(*p, q, k, v, qkv, L);
+    if (s == BASP_OK)
+        s = basp::prepare_head_to_seq(*p, o, o_out, L);
+    if (s != BASP_OK || p->S == 0)
+        return record(basp_status(s));
+
+    constexpr int kCoarse = 3, kFine = 9, kKeep = 4;
+    hipEvent_t ev[2 * kFine];
+    int made = 0;
+    for (; made < 2 * kFine; ++made)
+        if (hipEventCreate(&ev[made]) != hipSuccess)
+            break;
+    const basp_tuning saved[2] = {p->tuning[0], p->tuning[1]};
+    basp_status status = made == 2 * kFine ? BASP_OK : BASP_ERR_HIP;
+    const std::vector<basp_tuning> cands = basp::autotune_candidates();
+    for (int dir = 0; dir < 2 && status == BASP_OK; ++dir) {
+        const bool s2h = dir == BASP_SEQ_TO_HEAD;
+        auto measure = [&](const basp_tuning &t, int reps) -> float {
+            p->tuning[dir] = t;
+            const int st = s2h ? basp::prepare_seq_to_head(*p, q, k, v, qkv, L)
+                               : basp::prepare_head_to_seq(*p, o, o_out, L);
+            return st == BASP_OK ? basp::time_tile_launch(L, stream, ev, reps) : -2.f;
+        };
+        std::vector<std::pair<float, int>> coarse;
+        for (int i = 0; i < int(cands.size()) && status == BASP_OK; ++i) {
+            if (basp::check_launch_limits(*p, cands[i], s2h) != BASP_OK)
+                continue;
+            const float ms = measure(cands[i], kCoarse);
+            if (ms == -1.f)
+                status = BASP_ERR_HIP;
+            else if (ms >= 0.f)
+                coarse.push_back({ms, i});
+        }
+        if (status != BASP_OK || coarse.empty())
+            break;
+        std::sort(coarse.begin(), coarse.end());
+        float best = -1.f;
+        basp_tuning pick = cands[coarse[0].second];
+        for (int j = 0; j < int(coarse.size()) && j < kKeep && status == BASP_OK; ++j) {
+            const float ms = measure(cands[coarse[j].second], kFine);
+            if (ms == -1.f)
+                status = BASP_ERR_HIP;
+            else if (ms >= 0.f && (best < 0.f || ms < best)) {
+                best = ms;
+                pick = cands[coarse[j].second];
+            }
+        }
+        p->tuning[dir] = pick;
+    }
+    for (int i = 0; i < made; ++i)
+        (void)hipEventDestroy(ev[i]);
+    if (status != BASP_OK) {
+        p->tuning[0] = saved[0];
+        p->tuning[1] = saved[1];
+    }
+    return record(status);
+}
 
 extern "C" basp_status basp_time_next_call(void *start_event, void *stop_event)
 {

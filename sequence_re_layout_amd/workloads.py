@@ -17,4 +17,10 @@ LONG_CONTEXT = [("llama3.2-3b_s%dk_b2" % (S // 1024), 8, 2, S, 24, 8, 128)
 LLAMA_8B = ("llama3.1-8b_s16k_b2", 8, 2, 16384, 32, 8, 128)
 
 ALL = [TINY, LLAMA_1B, QWEN_1_8B] + BATCH_SWEEP + LONG_CONTEXT + [LLAMA_8B]
-BY_NAME = {w[0]: w for w in ALL}
+
+# More sequences than ranks: BASP reverts to data parallelism (each rank takes
+# B/N whole sequences); the batch-sweep shape continued to B = 16.
+DP_FALLBACK = ("llama3.2-1b_s8k_b16", 8, 16, 8192, 32, 8, 64)
+EXTRA = [DP_FALLBACK]
+
+BY_NAME = {w[0]: w for w in ALL + EXTRA}

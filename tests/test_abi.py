@@ -126,7 +126,19 @@ def test_status_strings_and_null_plan():
 def test_tuning_validation():
     p = b.basp_plan_create(8, 2, 16384, 32, 8, 64)
     b.basp_plan_set_tuning(p, vectors_per_thread=8, tile_tokens=64, tile_heads=2, cache_policy=3)
-    assert b.basp_plan_get_tuning(p)["tile_heads"] == 2
+    assert b.basp_plan_get_tuning(p, b.BASP_SEQ_TO_HEAD)["tile_heads"] == 2
+    assert b.basp_plan_get_tuning(p, b.BASP_HEAD_TO_SEQ)["tile_heads"] == 2
+    b.basp_plan_set_direction_tuning(p, b.BASP_HEAD_TO_SEQ, tile_heads=8, tile_order=2)
+    assert b.basp_plan_get_tuning(p, b.BASP_SEQ_TO_HEAD)["tile_heads"] == 2
+    assert b.basp_plan_get_tuning(p, b.BASP_HEAD_TO_SEQ)["tile_order"] == 2
+    with pytest.raises(b.BaspError) as e:
+        b.basp_plan_set_direction_tuning(p, 2, tile_heads=1)
+    assert e.value.status == b.BASP_ERR_INVALID
+    with pytest.raises(b.BaspError) as e:
+        b.basp_plan_set_tuning(p, tile_order=3)
+    assert e.value.status == b.BASP_ERR_INVALID
+    with pytest.raises(TypeError):
+        b.basp_plan_set_tuning(p, tile_size=3)
     for bad in (dict(vectors_per_thread=3), dict(cache_policy=4), dict(tile_tokens=-1)):
         with pytest.raises(b.BaspError) as e:
             b.basp_plan_set_tuning(p, **bad)
@@ -155,6 +167,10 @@ def test_pointer_checks_before_launch():
     ws = out + 4 * qb
     assert lib.basp_seq_to_head_unfused(p.handle, q, k, v, out, out + 8, None) == b.BASP_ERR_ALIAS
     assert lib.basp_seq_to_head_unfused(p.handle, q, k, v, out, ws + 1, None) == b.BASP_ERR_ALIGN
+    # autotune checks both calls' buffers before touching the device
+    assert lib.basp_plan_autotune(p.handle, q, k, v, q + 64, q, out, None) == b.BASP_ERR_ALIAS
+    assert lib.basp_plan_autotune(p.handle, q, k, v, out, q + 1, ws, None) == b.BASP_ERR_ALIGN
+    assert lib.basp_plan_autotune(None, q, k, v, out, q, ws, None) == b.BASP_ERR_INVALID
     # q, k and v may alias each other (inputs only)
     e = b.basp_plan_create(4, 2, 0, 8, 8, 64)
     assert lib.basp_seq_to_head(e.handle, None, None, None, None, None) == b.BASP_OK

@@ -120,7 +120,7 @@ def run_h2s(shape, mode, dtype="bf16", layout=0, tuning=None):
 # ------------------------------------------------------- named workloads ---
 
 @pytest.mark.parametrize("mode", ["basp", "ulysses"])
-@pytest.mark.parametrize("w", workloads.ALL, ids=[w[0] for w in workloads.ALL])
+@pytest.mark.parametrize("w", workloads.ALL + workloads.EXTRA, ids=[w[0] for w in workloads.ALL + workloads.EXTRA])
 def test_workload_full_size(w, mode):
     needs_gpu()
     print("workload", w, mode, flush=True)
@@ -164,7 +164,8 @@ TUNINGS = [dict(vectors_per_thread=1), dict(vectors_per_thread=2), dict(vectors_
            dict(cache_policy=1), dict(cache_policy=3), dict(max_grid=7),
            dict(vectors_per_thread=8, tile_tokens=5, tile_heads=1, cache_policy=3, max_grid=3),
            dict(lane_order=2, tile_heads=3, tile_tokens=7), dict(xcd_remap=2, max_grid=24),
-           dict(xcd_remap=2, max_grid=13, lane_order=2)]
+           dict(xcd_remap=2, max_grid=13, lane_order=2),
+           dict(tile_order=1), dict(tile_order=2, tile_heads=3, tile_tokens=5, max_grid=11)]
 
 
 @pytest.mark.parametrize("tuning", TUNINGS, ids=lambda t: ",".join("%s=%s" % kv for kv in t.items()))
@@ -384,3 +385,30 @@ def test_timed_call_records_kernel_time_and_keeps_results():
     torch.cuda.synchronize()
     assert ev[0].elapsed_time(ev[1]) > 0
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("shape,mode", [(workloads.LLAMA_1B[1:], 1), ((6, 3, 6 * 37, 12, 6, 40), 0)],
+                         ids=["llama1b-basp", "ragged-ulysses"])
+def test_autotune_keeps_results(shape, mode):
+    """basp_plan_autotune stores a valid launch shape per direction and the
+    re-layout stays bit-exact with it."""
+    needs_gpu()
+    N, B, S, Hq, Hkv, d = shape
+    plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, mode)
+    i = plan.info
+    q, k, v = (x.cuda() for x in seq_inputs(B, S, Hq, Hkv, d, "bf16"))
+    o = inputs.normal_bf16(i["q_elems"], inputs.SEED_O).cuda()
+    qkv = torch.empty(i["qkv_elems"], dtype=torch.bfloat16, device="cuda")
+    o_out = torch.empty(i["q_elems"], dtype=torch.bfloat16, device="cuda")
+    b.basp_plan_autotune(plan, q, k, v, qkv, o, o_out)
+    for direction in (b.BASP_SEQ_TO_HEAD, b.BASP_HEAD_TO_SEQ):
+        t = b.basp_plan_get_tuning(plan, direction)
+        assert t["vectors_per_thread"] in (1, 2, 4) and t["cache_policy"] == 3
+    qkv.fill_(0)
+    o_out.fill_(0)
+    b.basp_seq_to_head(plan, q, k, v, qkv)
+    b.basp_head_to_seq(plan, o, o_out)
+    torch.cuda.synchronize()
+    want = oracle.seq_to_head_qkv(bits(q), bits(k), bits(v), mode, N, B, S, Hq, Hkv, d)
+    assert np.array_equal(bits(qkv), want)
+    assert np.array_equal(bits(o_out), oracle.head_to_seq(bits(o), mode, N, B, S, Hq, d))

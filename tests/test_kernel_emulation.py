@@ -35,7 +35,7 @@ def emu(tmp_path_factory):
     lib.basp_plan_create_ex.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32]
     lib.basp_plan_create_ex.restype = vp
     lib.basp_plan_destroy.argtypes = [vp]
-    lib.basp_plan_set_tuning.argtypes = [vp, ctypes.POINTER(ctypes.c_int32 * 7)]
+    lib.basp_plan_set_tuning.argtypes = [vp, ctypes.POINTER(ctypes.c_int32 * 8)]
     lib.basp_plan_set_tuning.restype = i32
     tail = [ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_int)]
     lib.emu_seq_to_head.argtypes = [vp, vp, vp, vp, vp] + tail
@@ -57,9 +57,9 @@ class Run:
         self.plan = lib.basp_plan_create_ex(N, B, S, Hq, Hkv, d, dtype, mode, layout)
         assert self.plan, "plan rejected"
         if tuning:
-            t = (ctypes.c_int32 * 7)(*[tuning.get(k, 0) for k in (
+            t = (ctypes.c_int32 * 8)(*[tuning.get(k, 0) for k in (
                 "vectors_per_thread", "tile_tokens", "tile_heads", "cache_policy", "max_grid",
-                "lane_order", "xcd_remap")])
+                "lane_order", "xcd_remap", "tile_order")])
             assert lib.basp_plan_set_tuning(self.plan, ctypes.byref(t)) == 0
 
     def __call__(self, fn, *arrays):
@@ -142,7 +142,9 @@ TUNINGS = [dict(vectors_per_thread=1), dict(vectors_per_thread=2), dict(vectors_
            dict(vectors_per_thread=8, tile_tokens=5, tile_heads=1, cache_policy=3, max_grid=3),
            dict(lane_order=1), dict(lane_order=2), dict(lane_order=2, tile_heads=3, tile_tokens=7),
            dict(xcd_remap=2), dict(xcd_remap=2, max_grid=24), dict(xcd_remap=2, max_grid=13, lane_order=2),
-           dict(xcd_remap=1, lane_order=1, vectors_per_thread=1)]
+           dict(xcd_remap=1, lane_order=1, vectors_per_thread=1),
+           dict(tile_order=1), dict(tile_order=2), dict(tile_order=2, tile_heads=3, tile_tokens=5, max_grid=11),
+           dict(tile_order=1, xcd_remap=2, lane_order=2, tile_heads=2)]
 
 
 @pytest.mark.parametrize("tuning", TUNINGS, ids=lambda t: ",".join("%s=%s" % kv for kv in t.items()))
@@ -173,7 +175,7 @@ def test_degenerate(emu, shape, mode):
             check_h2s(emu, shape, mode, layout, es)
 
 
-SCALED = [(w[0], w[1], w[2], max(w[3] // 16, w[1]), w[4], w[5], w[6]) for w in workloads.ALL]
+SCALED = [(w[0], w[1], w[2], max(w[3] // 16, w[1]), w[4], w[5], w[6]) for w in workloads.ALL + workloads.EXTRA]
 
 
 @pytest.mark.parametrize("mode", [1, 0], ids=["basp", "ulysses"])
