@@ -433,12 +433,15 @@ def pmc_summary(fetch_dir, write_dir):
         copies = [r for r in rows[marks[1]:] if "copy" in r["Kernel_Name"].lower()]
         if not fused or not copies:
             raise SystemExit("missing fused or copy dispatches for %s" % counter)
-        # the calibration copy is the first copy after the timed region
-        cal = float(copies[0]["Counter_Value"])
+        # the calibration copy: the largest copy after the timed region (small
+        # copies bring results back to the host)
+        cal_row = max(copies, key=lambda r: float(r["Counter_Value"]))
+        cal = float(cal_row["Counter_Value"])
         factor = (CALIB_BYTES / 1024.0) / cal
         kib = statistics.median(float(r["Counter_Value"]) for r in fused)
         out["kernel"] = fused[0]["Kernel_Name"]
-        out[counter] = {"kib_per_launch_raw": kib, "copy_kernel": copies[0]["Kernel_Name"],
+        out[counter] = {"kib_per_launch_raw": kib, "kernel_name": fused[0]["Kernel_Name"],
+                        "copy_kernel": cal_row["Kernel_Name"],
                         "copy_kib_raw": cal, "scale": factor,
                         "bytes_per_launch": kib * factor * 1024.0, "launches": len(fused)}
     out["traffic_bytes_per_launch"] = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]

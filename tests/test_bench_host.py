@@ -35,7 +35,7 @@ def test_pmc_summary_scales_by_the_copy(tmp_path):
     # only launches between the two markers count
     _write_counters(tmp_path / "f", "FETCH_SIZE",
                     [(copy, 5.0), (fused, 3000.0), (spin, 0.0), (fused, 1000.0), (other, 7.0),
-                     (fused, 1002.0), (fused, 998.0), (spin, 0.0), (copy, cal_kib / 2), (copy, 9.0)])
+                     (fused, 1002.0), (fused, 998.0), (spin, 0.0), (copy, 1.5), (copy, cal_kib / 2), (copy, 9.0)])
     _write_counters(tmp_path / "w", "WRITE_SIZE",
                     [(fused, 5.0), (spin, 0.0), (fused, 2000.0), (spin, 0.0), (copy, cal_kib)])
     out = bench.pmc_summary(str(tmp_path / "f"), str(tmp_path / "w"))
