@@ -223,6 +223,11 @@ basp_status basp_seq_to_head_unfused(const basp_plan *plan, const void *q, const
  *   tile_order           1 = token blocks fastest (the head-sharded side's
  *                        order), 2 = head blocks fastest (the sequence-sharded
  *                        side's order)
+ *   stage                1 = rows go straight from load to store registers
+ *                        (built-in), 2 = each tile passes through LDS: loads
+ *                        run along the source's contiguous axis, stores along
+ *                        the destination's (used with 16-byte vectors and
+ *                        tiles of at most 256*vectors_per_thread vectors)
  * basp_plan_set_tuning sets both directions, basp_plan_set_direction_tuning
  * one; basp_plan_get_tuning reads one.  Errors: BASP_ERR_INVALID on a NULL
  * argument, an unknown direction or an out-of-range field;
@@ -243,6 +248,7 @@ typedef struct basp_tuning {
     int32_t lane_order;
     int32_t xcd_remap;
     int32_t tile_order;
+    int32_t stage;
 } basp_tuning;
 basp_status basp_plan_set_tuning(basp_plan *plan, const basp_tuning *tuning);
 basp_status basp_plan_set_direction_tuning(basp_plan *plan, basp_direction dir,

@@ -36,6 +36,7 @@ struct Shape {
     bool heads_first;
     uint32_t grid_cap;
     bool xcd;
+    bool stage;
 };
 
 Shape resolve(const basp_plan &p, const basp_tuning &t, bool s2h)
@@ -51,6 +52,7 @@ Shape resolve(const basp_plan &p, const basp_tuning &t, bool s2h)
     s.heads_first = t.tile_order ? t.tile_order == 2 : !s2h;
     s.grid_cap = t.max_grid ? uint32_t(t.max_grid) : kGridCap;
     s.xcd = t.xcd_remap ? t.xcd_remap == 2 : (s2h || short_rows);
+    s.stage = t.stage == 2;
     return s;
 }
 
@@ -83,7 +85,11 @@ TileShape tile_shape(const basp_plan &p, const Shape &sh, uint32_t Hl, uint32_t 
 {
     const uint64_t rows = std::max<uint64_t>(1, uint64_t(kBlock) * sh.vpt / A);
     uint64_t th = std::min<uint64_t>(sh.tile_heads, Hl);
+    if (sh.stage)   // a staged tile is one pass of the work-group: at most `rows` rows
+        th = std::min<uint64_t>(th, rows);
     uint64_t ts = sh.tile_tokens ? uint64_t(sh.tile_tokens) : std::max<uint64_t>(1, rows / th);
+    if (sh.stage)
+        ts = std::min<uint64_t>(ts, std::max<uint64_t>(1, rows / th));
     ts = std::min<uint64_t>(ts, uint64_t(std::max<int64_t>(p.St, 1)));
     TileShape s;
     s.Ts = uint32_t(ts);
@@ -160,11 +166,19 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
     }
     const int vw = vector_width(p, addrs, 2 * nseg);
     const uint32_t A = uint32_t(p.row_bytes / vw);
-    const Shape sh = resolve(p, p.tuning[s2h ? BASP_SEQ_TO_HEAD : BASP_HEAD_TO_SEQ], s2h);
+    Shape sh = resolve(p, p.tuning[s2h ? BASP_SEQ_TO_HEAD : BASP_HEAD_TO_SEQ], s2h);
+    // LDS staging exists for 16-byte vectors and rows that fit one pass
+    sh.stage = sh.stage && vw == 16 && A <= uint32_t(kBlock * sh.vpt);
     TileDesc &D = L.D;
     D.St = uint32_t(p.St);
     D.row = uint32_t(p.row_bytes);
     D.s_fast = sh.s_fast;
+    // staged loads run along the source's contiguous axis, stores along the
+    // destination's: heads in the sequence-sharded layout and in the
+    // token-major head layout, tokens in the head-major one
+    const bool head_major = p.layout == BASP_LAYOUT_HEAD_MAJOR;
+    D.load_s_fast = s2h ? 0 : head_major;
+    D.store_s_fast = s2h ? head_major : 0;
     D.heads_first = sh.heads_first;
     D.P = make_fastdiv(p.P);
     D.Bl = make_fastdiv(p.Bl);
@@ -195,11 +209,10 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
         sg.head_tok = uint32_t(st.head_tok);
         sg.head_head_lane = ts.Th == 1 ? 0u : uint32_t(st.head_head);
         sg.Hl = Hl;
-        sg.Ts = ts.Ts;
-        sg.Th = ts.Th;
+        sg.Ts = make_fastdiv(ts.Ts);
+        sg.Th = make_fastdiv(ts.Th);
         sg.ntb = make_fastdiv(ts.ntb);
         sg.nhb = make_fastdiv(ts.nhb);
-        sg.fast = make_fastdiv(D.s_fast ? ts.Ts : ts.Th);
         sg.tile_begin = uint32_t(total);
         total += ts.ntiles;
         if (total > kI31Max)
@@ -213,6 +226,7 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
     L.vpt = sh.vpt;
     L.policy = sh.policy;
     L.s2h = s2h;
+    L.staged = sh.stage;
     return BASP_OK;
 }
 

@@ -52,10 +52,9 @@ struct TileSeg {
     uint32_t head_tok;             // byte stride of a token, head-sharded
     uint32_t head_head_lane;       // head stride inside a tile (0 when Th == 1)
     uint32_t Hl;                   // heads per rank
-    uint32_t Ts, Th;               // tile extent in tokens and heads
+    FastDiv Ts, Th;                // tile extent in tokens and heads
     FastDiv ntb;                   // token blocks per member chunk
     FastDiv nhb;                   // head blocks per rank
-    FastDiv fast;                  // extent of the lane-fastest tile axis
     uint32_t tile_begin, tile_end;
 };
 
@@ -65,6 +64,8 @@ struct TileDesc {
     uint32_t St;
     uint32_t row;                  // bytes per (token, head) row
     uint32_t s_fast;               // lanes along tokens (1) or heads (0)
+    uint32_t load_s_fast;          // staged kernel: lane order of the loads
+    uint32_t store_s_fast;         //   and of the stores
     uint32_t heads_first;          // tile order: head block fastest (1) or token block (0)
     uint32_t xcd_span;             // tiles per XCD when remapped, else 0
     FastDiv P, Bl, A;              // group size, sequences per group, vectors per row
@@ -120,9 +121,10 @@ BASP_HD inline TileOrigin tile_origin(const TileDesc &D, uint32_t x)
         g = fastdiv(q4, D.P);
         jh = q4 - g * P;
     }
-    const uint32_t t0 = tb * sg.Ts, hl0 = hb * sg.Th;
-    o.ns = D.St - t0 < sg.Ts ? D.St - t0 : sg.Ts;
-    o.nh = sg.Hl - hl0 < sg.Th ? sg.Hl - hl0 : sg.Th;
+    const uint32_t Ts = sg.Ts.d, Th = sg.Th.d;
+    const uint32_t t0 = tb * Ts, hl0 = hb * Th;
+    o.ns = D.St - t0 < Ts ? D.St - t0 : Ts;
+    o.nh = sg.Hl - hl0 < Th ? sg.Hl - hl0 : Th;
     const uint64_t rs = uint64_t(g) * P + js, rh = uint64_t(g) * P + jh;
     o.seq_off = rs * sg.seq_rank + bl * sg.seq_bl + uint64_t(t0) * sg.seq_tok +
                 (uint64_t(jh) * sg.Hl + hl0) * D.row;
@@ -131,19 +133,32 @@ BASP_HD inline TileOrigin tile_origin(const TileDesc &D, uint32_t x)
     return o;
 }
 
-// Offsets (from the tile base) of the vw-byte vector v of a tile in the
-// sequence-sharded (so) and head-sharded (ho) buffers.  Returns false for a
-// vector outside the tile's present rows.
+// The vw-byte vector v of a tile, with lanes along tokens first (s_fast) or
+// heads first: its byte offsets from the tile base in the sequence-sharded
+// (so) and head-sharded (ho) buffers, and its slot in the tile's
+// [token][head][vector] staging order (st).  Returns false for a vector
+// outside the tile's present rows.
+BASP_HD inline bool tile_vector(const TileDesc &D, const TileSeg &sg, uint32_t ns, uint32_t nh,
+                                uint32_t v, uint32_t vw, bool s_fast, uint32_t &so, uint32_t &ho,
+                                uint32_t &st)
+{
+    const uint32_t A = D.A.d, Ts = sg.Ts.d, Th = sg.Th.d;
+    const uint32_t r = fastdiv(v, D.A), vi = v - r * A;
+    const FastDiv &fast = s_fast ? sg.Ts : sg.Th;
+    const uint32_t slow = fastdiv(r, fast), fst = r - slow * fast.d;
+    const uint32_t sl = s_fast ? fst : slow, hl = s_fast ? slow : fst;
+    so = sl * sg.seq_tok + hl * D.row + vi * vw;
+    ho = sl * sg.head_tok + hl * sg.head_head_lane + vi * vw;
+    st = (sl * Th + hl) * A + vi;
+    return (v < Ts * Th * A) & (sl < ns) & (hl < nh);
+}
+
+// Offsets of vector v in the direct kernel's lane order.
 BASP_HD inline bool lane_offsets(const TileDesc &D, const TileSeg &sg, uint32_t ns, uint32_t nh,
                                  uint32_t v, uint32_t vw, uint32_t &so, uint32_t &ho)
 {
-    const uint32_t nvec = sg.Ts * sg.Th * D.A.d;
-    const uint32_t r = fastdiv(v, D.A), vi = v - r * D.A.d;
-    const uint32_t slow = fastdiv(r, sg.fast), fst = r - slow * sg.fast.d;
-    const uint32_t sl = D.s_fast ? fst : slow, hl = D.s_fast ? slow : fst;
-    so = sl * sg.seq_tok + hl * D.row + vi * vw;
-    ho = sl * sg.head_tok + hl * sg.head_head_lane + vi * vw;
-    return (v < nvec) & (sl < ns) & (hl < nh);
+    uint32_t st;
+    return tile_vector(D, sg, ns, nh, v, vw, D.s_fast, so, ho, st);
 }
 
 struct PermSeg {
@@ -190,6 +205,7 @@ struct TileLaunch {
     TileDesc D;
     int vw, vpt, policy;
     bool s2h;                 // read sequence-sharded, write head-sharded
+    bool staged;              // tiles pass through LDS (one pass per tile)
     uint32_t grid;            // 0: nothing to launch
 };
 

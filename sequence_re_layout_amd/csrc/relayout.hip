@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kBlock) void tile_kernel(const TileDesc D)
         const __amdgpu_buffer_rsrc_t rseq = make_rsrc(sg.seq + o.seq_off, rest(sg.seq_bytes, o.seq_off));
         const __amdgpu_buffer_rsrc_t rhead =
             make_rsrc(sg.head + o.head_off, rest(sg.head_bytes, o.head_off));
-        const uint32_t nvec = sg.Ts * sg.Th * D.A.d;
+        const uint32_t nvec = sg.Ts.d * sg.Th.d * D.A.d;
         for (uint32_t v0 = 0; v0 < nvec; v0 += kBlock * VPT) {
             uint32_t src[VPT], dst[VPT];
 #pragma unroll
@@ -112,6 +112,54 @@ __global__ __launch_bounds__(kBlock) void tile_kernel(const TileDesc D)
             for (int k = 0; k < VPT; ++k)
                 vstore<VW, Policy<POL>::store>(S2H ? rhead : rseq, dst[k], buf[k]);
         }
+    }
+}
+
+// The same re-layout with each tile staged through LDS: the loads run along
+// the source layout's contiguous axis, the stores along the destination's, so
+// both sides of every wave instruction are contiguous.  A tile is one pass of
+// the work-group (the host sizes it to at most kBlock*VPT vectors).
+template <int VPT, int POL, bool S2H>
+__global__ __launch_bounds__(kBlock) void tile_kernel_staged(const TileDesc D)
+{
+    using V = typename Vec<16>::type;
+    __shared__ V stage[kBlock * VPT];
+    for (uint32_t tile = blockIdx.x; tile < D.ntiles; tile += gridDim.x) {
+        const TileOrigin o = tile_origin(D, tile);
+        const TileSeg &sg = D.seg[o.seg];
+        const __amdgpu_buffer_rsrc_t rseq = make_rsrc(sg.seq + o.seq_off, rest(sg.seq_bytes, o.seq_off));
+        const __amdgpu_buffer_rsrc_t rhead =
+            make_rsrc(sg.head + o.head_off, rest(sg.head_bytes, o.head_off));
+        uint32_t off[VPT], slot[VPT];
+        bool ok[VPT];
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            uint32_t so, ho;
+            ok[k] = tile_vector(D, sg, o.ns, o.nh, threadIdx.x + k * kBlock, 16, D.load_s_fast, so,
+                                ho, slot[k]);
+            off[k] = ok[k] ? (S2H ? so : ho) : kOutside;
+        }
+        V buf[VPT];
+#pragma unroll
+        for (int k = 0; k < VPT; ++k)
+            buf[k] = vload<16, Policy<POL>::load>(S2H ? rseq : rhead, off[k]);
+#pragma unroll
+        for (int k = 0; k < VPT; ++k)
+            if (ok[k])
+                stage[slot[k]] = buf[k];
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            uint32_t so, ho;
+            ok[k] = tile_vector(D, sg, o.ns, o.nh, threadIdx.x + k * kBlock, 16, D.store_s_fast, so,
+                                ho, slot[k]);
+            off[k] = ok[k] ? (S2H ? ho : so) : kOutside;
+            buf[k] = stage[ok[k] ? slot[k] : 0];
+        }
+#pragma unroll
+        for (int k = 0; k < VPT; ++k)
+            vstore<16, Policy<POL>::store>(S2H ? rhead : rseq, off[k], buf[k]);
+        __syncthreads();   // the next tile reuses the staging area
     }
 }
 
@@ -172,6 +220,32 @@ TileFn tile_fn_vpt(int vpt, int pol, bool s2h)
     }
 }
 
+template <int VPT, int POL>
+TileFn staged_fn_dir(bool s2h)
+{
+    return s2h ? tile_kernel_staged<VPT, POL, true> : tile_kernel_staged<VPT, POL, false>;
+}
+
+template <int VPT>
+TileFn staged_fn_pol(int pol, bool s2h)
+{
+    switch (pol) {
+    case 1: return staged_fn_dir<VPT, 1>(s2h);
+    case 2: return staged_fn_dir<VPT, 2>(s2h);
+    default: return staged_fn_dir<VPT, 3>(s2h);
+    }
+}
+
+TileFn staged_fn(int vpt, int pol, bool s2h)
+{
+    switch (vpt) {
+    case 1: return staged_fn_pol<1>(pol, s2h);
+    case 2: return staged_fn_pol<2>(pol, s2h);
+    case 8: return staged_fn_pol<8>(pol, s2h);
+    default: return staged_fn_pol<4>(pol, s2h);
+    }
+}
+
 TileFn tile_fn(int vw, int vpt, int pol, bool s2h)
 {
     switch (vw) {
@@ -210,7 +284,7 @@ basp_status launch(const TileLaunch &L, void *stream)
 {
     if (L.grid == 0)
         return BASP_OK;
-    const TileFn fn = tile_fn(L.vw, L.vpt, L.policy, L.s2h);
+    const TileFn fn = L.staged ? staged_fn(L.vpt, L.policy, L.s2h) : tile_fn(L.vw, L.vpt, L.policy, L.s2h);
     return launch_kernel(reinterpret_cast<const void *>(fn), L.grid, L.D, stream, true, true);
 }
 
@@ -240,11 +314,25 @@ basp_status timed_call(F f)
 // ---------------------------------------------------------------- autotune --
 
 // Launch shapes a plan is measured with: tile order x vectors per lane x
-// heads per tile x lane order x XCD order x grid cap, non-temporal loads and
-// stores (the policy every sweep preferred).
+// heads per tile x lane order x XCD order x grid cap, and the LDS-staged
+// kernel over tile order x vectors per lane x heads per tile x XCD order; all
+// with non-temporal loads and stores (the policy every sweep preferred).
 std::vector<basp_tuning> autotune_candidates()
 {
     std::vector<basp_tuning> c;
+    for (int to : {1, 2})
+        for (int vpt : {1, 2, 4})
+            for (int th : {1, 2, 4, 8})
+                for (int xcd : {1, 2}) {
+                    basp_tuning t = {};
+                    t.vectors_per_thread = vpt;
+                    t.tile_heads = th;
+                    t.cache_policy = 3;
+                    t.xcd_remap = xcd;
+                    t.tile_order = to;
+                    t.stage = 2;
+                    c.push_back(t);
+                }
     for (int to : {1, 2})
         for (int vpt : {1, 2, 4})
             for (int th : {1, 2, 4, 8})

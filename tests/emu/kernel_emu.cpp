@@ -10,6 +10,7 @@
 // never has one.
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "launch.hpp"
 #include "plan_internal.hpp"
@@ -30,6 +31,7 @@ void copy(uint64_t dst, uint64_t src, uint32_t vw)
 void run(const TileLaunch &L, uint64_t *bad)
 {
     const TileDesc &D = L.D;
+    std::vector<unsigned char> lds(size_t(kBlock) * L.vpt * 16);
     for (uint32_t block = 0; block < L.grid; ++block) {
         for (uint32_t tile = block; tile < D.ntiles; tile += L.grid) {
             const TileOrigin o = tile_origin(D, tile);
@@ -37,7 +39,35 @@ void run(const TileLaunch &L, uint64_t *bad)
             const uint64_t seq = sg.seq + o.seq_off, head = sg.head + o.head_off;
             const uint64_t nseq = range(rest(sg.seq_bytes, o.seq_off));
             const uint64_t nhead = range(rest(sg.head_bytes, o.head_off));
-            const uint32_t nvec = sg.Ts * sg.Th * D.A.d;
+            const uint64_t src = L.s2h ? seq : head, dst = L.s2h ? head : seq;
+            const uint64_t nsrc = L.s2h ? nseq : nhead, ndst = L.s2h ? nhead : nseq;
+            if (L.staged) {
+                // one pass: every vector of the tile, loads in the load order
+                // into the staging slots, then stores in the store order
+                const uint32_t nv = uint32_t(kBlock) * L.vpt;
+                if (sg.Ts.d * sg.Th.d * D.A.d > nv) {
+                    ++*bad;
+                    continue;
+                }
+                for (int phase = 0; phase < 2; ++phase)
+                    for (uint32_t v = 0; v < nv; ++v) {
+                        uint32_t so, ho, st;
+                        if (!tile_vector(D, sg, o.ns, o.nh, v, L.vw, phase ? D.store_s_fast : D.load_s_fast,
+                                         so, ho, st))
+                            continue;
+                        const uint32_t off = (phase == 0) == L.s2h ? so : ho;
+                        if (!inside(off, L.vw, phase ? ndst : nsrc) || uint64_t(st + 1) * L.vw > lds.size()) {
+                            ++*bad;
+                            continue;
+                        }
+                        if (phase == 0)
+                            std::memcpy(&lds[size_t(st) * L.vw], reinterpret_cast<const void *>(src + off), L.vw);
+                        else
+                            std::memcpy(reinterpret_cast<void *>(dst + off), &lds[size_t(st) * L.vw], L.vw);
+                    }
+                continue;
+            }
+            const uint32_t nvec = sg.Ts.d * sg.Th.d * D.A.d;
             const uint32_t step = kBlock * L.vpt;
             const uint32_t vend = (nvec + step - 1) / step * step;
             for (uint32_t v = 0; v < vend; ++v) {
@@ -83,12 +113,17 @@ void run(const PermLaunch &L, uint64_t *bad)
 
 extern "C" {
 
+// Whether the last emulated tile launch of this process used LDS staging.
+static int g_staged = 0;
+int emu_last_staged(void) { return g_staged; }
+
 int emu_seq_to_head(const basp_plan *p, const void *q, const void *k, const void *v, void *out,
                     uint64_t *bad, int *vw)
 {
     TileLaunch L;
     const int s = prepare_seq_to_head(*p, q, k, v, out, L);
     *vw = L.vw;
+    g_staged = L.staged;
     if (s == BASP_OK)
         run(L, bad);
     return s;
@@ -99,6 +134,7 @@ int emu_head_to_seq(const basp_plan *p, const void *o, void *out, uint64_t *bad,
     TileLaunch L;
     const int s = prepare_head_to_seq(*p, o, out, L);
     *vw = L.vw;
+    g_staged = L.staged;
     if (s == BASP_OK)
         run(L, bad);
     return s;

@@ -165,7 +165,9 @@ TUNINGS = [dict(vectors_per_thread=1), dict(vectors_per_thread=2), dict(vectors_
            dict(vectors_per_thread=8, tile_tokens=5, tile_heads=1, cache_policy=3, max_grid=3),
            dict(lane_order=2, tile_heads=3, tile_tokens=7), dict(xcd_remap=2, max_grid=24),
            dict(xcd_remap=2, max_grid=13, lane_order=2),
-           dict(tile_order=1), dict(tile_order=2, tile_heads=3, tile_tokens=5, max_grid=11)]
+           dict(tile_order=1), dict(tile_order=2, tile_heads=3, tile_tokens=5, max_grid=11),
+           dict(stage=2), dict(stage=2, vectors_per_thread=1, tile_heads=8, cache_policy=2),
+           dict(stage=2, vectors_per_thread=8, tile_tokens=500, tile_order=2, max_grid=5)]
 
 
 @pytest.mark.parametrize("tuning", TUNINGS, ids=lambda t: ",".join("%s=%s" % kv for kv in t.items()))

@@ -35,7 +35,7 @@ def emu(tmp_path_factory):
     lib.basp_plan_create_ex.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32]
     lib.basp_plan_create_ex.restype = vp
     lib.basp_plan_destroy.argtypes = [vp]
-    lib.basp_plan_set_tuning.argtypes = [vp, ctypes.POINTER(ctypes.c_int32 * 8)]
+    lib.basp_plan_set_tuning.argtypes = [vp, ctypes.POINTER(ctypes.c_int32 * 9)]
     lib.basp_plan_set_tuning.restype = i32
     tail = [ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_int)]
     lib.emu_seq_to_head.argtypes = [vp, vp, vp, vp, vp] + tail
@@ -43,6 +43,7 @@ def emu(tmp_path_factory):
     lib.emu_seq_to_head_o.argtypes = [vp, vp, vp] + tail
     lib.emu_head_to_seq_qkv.argtypes = [vp, vp, vp, vp, vp] + tail
     lib.emu_seq_to_head_unfused.argtypes = [vp, vp, vp, vp, vp, vp] + tail
+    lib.emu_last_staged.restype = ctypes.c_int
     return lib
 
 
@@ -57,9 +58,9 @@ class Run:
         self.plan = lib.basp_plan_create_ex(N, B, S, Hq, Hkv, d, dtype, mode, layout)
         assert self.plan, "plan rejected"
         if tuning:
-            t = (ctypes.c_int32 * 8)(*[tuning.get(k, 0) for k in (
+            t = (ctypes.c_int32 * 9)(*[tuning.get(k, 0) for k in (
                 "vectors_per_thread", "tile_tokens", "tile_heads", "cache_policy", "max_grid",
-                "lane_order", "xcd_remap", "tile_order")])
+                "lane_order", "xcd_remap", "tile_order", "stage")])
             assert lib.basp_plan_set_tuning(self.plan, ctypes.byref(t)) == 0
 
     def __call__(self, fn, *arrays):
@@ -144,7 +145,9 @@ TUNINGS = [dict(vectors_per_thread=1), dict(vectors_per_thread=2), dict(vectors_
            dict(xcd_remap=2), dict(xcd_remap=2, max_grid=24), dict(xcd_remap=2, max_grid=13, lane_order=2),
            dict(xcd_remap=1, lane_order=1, vectors_per_thread=1),
            dict(tile_order=1), dict(tile_order=2), dict(tile_order=2, tile_heads=3, tile_tokens=5, max_grid=11),
-           dict(tile_order=1, xcd_remap=2, lane_order=2, tile_heads=2)]
+           dict(tile_order=1, xcd_remap=2, lane_order=2, tile_heads=2),
+           dict(stage=2), dict(stage=2, vectors_per_thread=1, tile_heads=8), dict(stage=2, vectors_per_thread=8, tile_tokens=500),
+           dict(stage=2, tile_order=2, xcd_remap=2, tile_heads=3, max_grid=5)]
 
 
 @pytest.mark.parametrize("tuning", TUNINGS, ids=lambda t: ",".join("%s=%s" % kv for kv in t.items()))
@@ -153,6 +156,18 @@ def test_tunings(emu, tuning):
         for layout in (0, 1):
             check_s2h(emu, shape, mode, layout, 2, tuning)
             check_h2s(emu, shape, mode, layout, 4, tuning)
+
+
+def test_staging_used_where_it_applies(emu):
+    """The staged kernel runs for 16-byte vectors (and is emulated as such);
+    narrower vectors fall back to the direct kernel with the same result."""
+    shape = (8, 2, 8 * 129, 24, 8, 128)
+    check_s2h(emu, shape, 1, 0, 2, dict(stage=2))
+    assert emu.emu_last_staged() == 1
+    check_h2s(emu, shape, 0, 1, 2, dict(stage=2, vectors_per_thread=1))
+    assert emu.emu_last_staged() == 1
+    check_s2h(emu, shape, 1, 0, 2, dict(stage=2), offset=1)
+    assert emu.emu_last_staged() == 0
 
 
 @pytest.mark.parametrize("offset,es,expect_vw", [(0, 2, 16), (1, 2, 2), (2, 2, 4), (4, 2, 8),
