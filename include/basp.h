@@ -223,8 +223,8 @@ basp_status basp_seq_to_head_unfused(const basp_plan *plan, const void *q, const
  *   tile_order           1 = token blocks fastest (the head-sharded side's
  *                        order), 2 = head blocks fastest (the sequence-sharded
  *                        side's order)
- *   stage                1 = rows go straight from load to store registers
- *                        (built-in), 2 = each tile passes through LDS: loads
+ *   stage                1 = rows go straight from load to store registers,
+ *                        2 = each tile passes through LDS: loads
  *                        run along the source's contiguous axis, stores along
  *                        the destination's (used with 16-byte vectors and
  *                        tiles of at most 256*vectors_per_thread vectors)

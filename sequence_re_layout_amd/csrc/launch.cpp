@@ -16,17 +16,17 @@ namespace {
 constexpr uint32_t kGridCap = 1u << 22;  // work-groups per launch at most
 
 // Launch shape of one tile launch: the plan's tuning where set, else the
-// defaults below, chosen on MI355X over every named workload (Llama/Qwen
-// shapes, 128- and 256-byte rows, both modes) as the launch shape whose worst
-// ratio to each workload's best was highest.  Common to all: non-temporal
-// loads and stores.  seq->head walks tiles token block first (the
-// head-sharded destination's order) with 4 heads per tile for 128-byte rows
-// (2 vectors per lane, 8 KiB tiles) and 1 head for longer rows (1 vector per
-// lane); head->seq walks them head block first (the sequence-sharded
-// destination's order) with 4 heads per tile and 4 vectors per lane for
-// 128-byte rows, 8 heads and 2 vectors for longer rows.  Lanes run along
-// heads first, except for head->seq with long rows; each XCD takes one
-// contiguous eighth of the tiles, except for head->seq with long rows.
+// defaults below, chosen on MI355X over every named workload of at least
+// 256 MiB (Llama/Qwen shapes, 128- and 256-byte rows, both modes, rotating
+// buffers) as the launch shape whose worst ratio to each workload's best was
+// highest (0.94 to 0.97).  All use non-temporal loads and stores and two
+// 16-byte vectors per lane.
+//   seq->head, 128-byte rows:  LDS-staged, 4 heads per tile, token blocks
+//                              fastest, XCD-contiguous
+//   seq->head, longer rows:    LDS-staged, 8 heads, head blocks fastest
+//   head->seq, 128-byte rows:  LDS-staged, 8 heads, head blocks fastest
+//   head->seq, longer rows:    direct, 1 head, head blocks fastest, lanes
+//                              along tokens
 // basp_plan_autotune replaces these by measurement.
 struct Shape {
     int vpt, policy;
@@ -42,17 +42,18 @@ struct Shape {
 Shape resolve(const basp_plan &p, const basp_tuning &t, bool s2h)
 {
     const bool short_rows = p.row_bytes <= 128;
+    const bool staged = s2h || short_rows;
     Shape s;
-    s.vpt = t.vectors_per_thread ? t.vectors_per_thread : (s2h ? (short_rows ? 2 : 1) : (short_rows ? 4 : 2));
+    s.vpt = t.vectors_per_thread ? t.vectors_per_thread : 2;
     s.policy = t.cache_policy ? t.cache_policy : 3;
     s.tile_tokens = uint32_t(t.tile_tokens);
-    s.tile_heads = t.tile_heads ? uint32_t(t.tile_heads) : (s2h ? (short_rows ? 4 : 1) : (short_rows ? 4 : 8));
+    s.tile_heads = t.tile_heads ? uint32_t(t.tile_heads) : (s2h && short_rows ? 4 : (staged ? 8 : 1));
     s.heads_given = t.tile_heads != 0;
-    s.s_fast = t.lane_order ? t.lane_order == 1 : (!s2h && !short_rows);
-    s.heads_first = t.tile_order ? t.tile_order == 2 : !s2h;
+    s.s_fast = t.lane_order ? t.lane_order == 1 : !staged;
+    s.heads_first = t.tile_order ? t.tile_order == 2 : !(s2h && short_rows);
     s.grid_cap = t.max_grid ? uint32_t(t.max_grid) : kGridCap;
-    s.xcd = t.xcd_remap ? t.xcd_remap == 2 : (s2h || short_rows);
-    s.stage = t.stage == 2;
+    s.xcd = t.xcd_remap ? t.xcd_remap == 2 : (s2h && short_rows);
+    s.stage = t.stage ? t.stage == 2 : staged;
     return s;
 }
 
