@@ -439,8 +439,9 @@ def pmc_summary(fetch_dir, write_dir):
         if len(marks) < 2:
             raise SystemExit("no timed-region markers for %s" % counter)
         timed = rows[marks[0] + 1:marks[1]]
-        # the fused seq->head kernel: tile_kernel<VW, VPT, POLICY, true>
-        fused = [r for r in timed if "tile_kernel<" in r["Kernel_Name"] and "true>" in r["Kernel_Name"]]
+        # the fused seq->head kernel: tile_kernel<VW, VPT, POLICY, true> or
+        # tile_kernel_staged<VPT, POLICY, true>
+        fused = [r for r in timed if "tile_kernel" in r["Kernel_Name"] and "true>" in r["Kernel_Name"]]
         copies = [r for r in rows[marks[1]:] if "copy" in r["Kernel_Name"].lower()]
         if not fused or not copies:
             raise SystemExit("missing fused or copy dispatches for %s" % counter)

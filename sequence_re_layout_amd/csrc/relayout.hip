@@ -347,6 +347,7 @@ std::vector<basp_tuning> autotune_candidates()
                             t.lane_order = lo;
                             t.xcd_remap = xcd;
                             t.tile_order = to;
+                            t.stage = 1;
                             c.push_back(t);
                         }
     return c;

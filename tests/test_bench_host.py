@@ -25,7 +25,7 @@ def _write_counters(d, counter, rows):
 
 
 def test_pmc_summary_scales_by_the_copy(tmp_path):
-    fused = "void basp::(anonymous namespace)::tile_kernel<16, 1, 3, true>(basp::TileDesc)"
+    fused = "void basp::(anonymous namespace)::tile_kernel_staged<2, 3, true>(basp::TileDesc)"
     other = "void basp::(anonymous namespace)::tile_kernel<16, 2, 3, false>(basp::TileDesc)"
     copy = "__amd_rocclr_copyBuffer"
     cal_kib = bench.CALIB_BYTES / 1024
