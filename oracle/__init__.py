@@ -47,6 +47,8 @@ def _load():
         for fn in (lib.orc_seq_to_head, lib.orc_head_to_seq):
             fn.argtypes = [i32, i32, i64, i64, i64, i64, i64, i64, vp, vp, vp, i32]
             fn.restype = i32
+        lib.orc_source_index.argtypes = [i32, i32, i32, i64, i64, i64, i64, i64, vp, vp, i64]
+        lib.orc_source_index.restype = i32
         lib.orc_max_threads.argtypes = []
         lib.orc_max_threads.restype = i32
         _lib = lib
@@ -104,6 +106,18 @@ def seq_to_head(x, mode, N, B, S, H, d, layout=HEAD_MAJOR, traffic=False, thread
 def head_to_seq(x, mode, N, B, S, H, d, layout=HEAD_MAJOR, traffic=False, threads=None):
     """One tensor, head-sharded -> sequence-sharded (the inverse exchange)."""
     return _run(_load().orc_head_to_seq, x, mode, layout, N, B, S, H, d, traffic, threads)
+
+
+def source_index(direction, dst, mode, N, B, S, H, d, layout=HEAD_MAJOR):
+    """Source element offsets of the destination element offsets ``dst`` of a
+    one-tensor call (direction 0: seq->head, 1: head->seq), one element at a
+    time, for sampled checks at sizes the full loop does not reach."""
+    dst = np.ascontiguousarray(dst, dtype=np.int64)
+    src = np.empty_like(dst)
+    rc = _load().orc_source_index(direction, mode, layout, N, B, S, H, d, _ptr(dst), _ptr(src), dst.size)
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments or an offset")
+    return src
 
 
 def seq_to_head_qkv(q, k, v, mode, N, B, S, Hq, Hkv, d, layout=HEAD_MAJOR, threads=None):

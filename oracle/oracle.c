@@ -216,6 +216,58 @@ int orc_head_to_seq(int mode, int layout, int64_t N, int64_t B, int64_t S, int64
     return 0;
 }
 
+/*
+ * The same two rules, one destination element at a time: for each of the n
+ * destination element offsets dst[i] of a one-tensor call, src[i] receives
+ * the source element offset the element is read from.  For checks of sampled
+ * outputs where the whole loop is too large.  Returns 0, or -1 on invalid
+ * arguments or an offset outside the tensor.
+ */
+int orc_source_index(int direction, int mode, int layout, int64_t N, int64_t B, int64_t S,
+                     int64_t H, int64_t d, const int64_t *dst, int64_t *src, int64_t n)
+{
+    int64_t G, P, Bl;
+    if (check(mode, layout, N, B, S, H, d, 2, &G, &P, &Bl) != 0)
+        return -1;
+    (void)G;
+    const int64_t St = S / P, Hl = H / P, total = B * S * H * d;
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t x = dst[i];
+        if (x < 0 || x >= total)
+            return -1;
+        const int64_t e = x % d;
+        x /= d;
+        if (direction == 0) {
+            /* seq -> head: x enumerates (r, bl, hl, s) or (r, bl, s, hl) */
+            int64_t s, hl;
+            if (layout == ORC_TOKEN_MAJOR) {
+                hl = x % Hl;
+                x /= Hl;
+                s = x % S;
+                x /= S;
+            } else {
+                s = x % S;
+                x /= S;
+                hl = x % Hl;
+                x /= Hl;
+            }
+            const int64_t bl = x % Bl, r = x / Bl;
+            const int64_t g = r / P, j = r % P;
+            src[i] = seq_offset(g * P + s / St, bl, s % St, j * Hl + hl, e, Bl, St, H, d);
+        } else {
+            /* head -> seq: x enumerates (r, bl, t, h) */
+            const int64_t h = x % H;
+            x /= H;
+            const int64_t t = x % St;
+            x /= St;
+            const int64_t bl = x % Bl, r = x / Bl;
+            const int64_t g = r / P, j = r % P;
+            src[i] = head_offset(layout, g * P + h / Hl, bl, h % Hl, j * St + t, e, Bl, Hl, S, d);
+        }
+    }
+    return 0;
+}
+
 /* Number of OpenMP threads a parallel region would get (1 without OpenMP). */
 int orc_max_threads(void)
 {

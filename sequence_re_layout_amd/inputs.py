@@ -33,11 +33,11 @@ def normal_bf16(numel: int, seed: int) -> torch.Tensor:
     return torch.randn(numel, generator=gen, dtype=torch.float32).to(torch.bfloat16)
 
 
-def tags_int32(numel: int, base: int = 0) -> torch.Tensor:
-    """Flat CPU int32 tensor ``base .. base+numel-1``."""
+def tags_int32(numel: int, base: int = 0, device: str = "cpu") -> torch.Tensor:
+    """Flat int32 tensor ``base .. base+numel-1`` (on ``device``)."""
     if base < 0 or base + numel > 2**31:
         raise ValueError("int32 tags must lie in [0, 2^31)")
-    return torch.arange(base, base + numel, dtype=torch.int32)
+    return torch.arange(base, base + numel, dtype=torch.int32, device=device)
 
 
 def all_bf16_patterns() -> torch.Tensor:

@@ -25,6 +25,8 @@ What each check compares with (none re-types the oracle's formulas):
 * ``check_bijection``: every destination is written once from a distinct
   source.
 * ``check_bf16_patterns``: all 65536 bfloat16 bit patterns pass unchanged.
+* ``check_source_index_matches_loop``: the oracle's one-element form (for
+  sampled checks at large sizes) names the element the full loop copies.
 """
 from __future__ import annotations
 
@@ -244,9 +246,24 @@ def check_rejects():
             raise AssertionError("oracle accepted indivisible heads %r" % (args,))
 
 
+def check_source_index_matches_loop(seed=6):
+    """The one-element form names, for every destination, the element the
+    full loop copies there (tags make the source readable from the output)."""
+    rng = np.random.default_rng(seed)
+    for (mode, N, B, S, H, d) in [(BASP, 8, 2, 16, 8, 3), (ULYSSES, 6, 3, 12, 6, 2), (BASP, 4, 8, 4, 2, 5)]:
+        n = B * S * H * d
+        tags = np.arange(n, dtype=np.uint32)
+        dst = rng.integers(0, n, size=500)
+        for layout in (HEAD_MAJOR, TOKEN_MAJOR):
+            for direction, fn in ((0, oracle.seq_to_head), (1, oracle.head_to_seq)):
+                out = fn(tags, mode, N, B, S, H, d, layout)
+                src = oracle.source_index(direction, dst, mode, N, B, S, H, d, layout)
+                assert np.array_equal(out[dst], src.astype(np.uint32)), (mode, layout, direction)
+
+
 ALL_CHECKS = [check_numpy_layouts, check_tagged_brute_force, check_round_trip,
               check_b1_is_ulysses, check_k1_local_transpose, check_traffic,
-              check_bijection, check_bf16_patterns, check_rejects]
+              check_bijection, check_bf16_patterns, check_rejects, check_source_index_matches_loop]
 
 
 def run_all():

@@ -415,3 +415,69 @@ def test_autotune_keeps_results(shape, mode):
     want = oracle.seq_to_head_qkv(bits(q), bits(k), bits(v), mode, N, B, S, Hq, Hkv, d)
     assert np.array_equal(bits(qkv), want)
     assert np.array_equal(bits(o_out), oracle.head_to_seq(bits(o), mode, N, B, S, Hq, d))
+
+
+def _sample(n, rng, extra=()):
+    """Random element offsets of a tensor of n elements plus its first and last
+    elements and given offsets."""
+    pts = list(rng.integers(0, n, size=200000)) + [0, 1, n - 2, n - 1] + [x for x in extra if 0 <= x < n]
+    return np.unique(np.array(pts, dtype=np.int64))
+
+
+@pytest.mark.parametrize("mode,layout", [(1, 0), (0, 0), (1, 1)], ids=["basp", "ulysses", "basp-token-major"])
+def test_beyond_4gib_sampled(mode, layout):
+    """Buffers larger than 2^31 and 2^32 bytes (int32, S = 98304): the fused
+    output is 4.8 GB and Q 3.2 GB, so tile bases need more than 32 bits.
+    Tags name each element's source; sampled outputs, including the elements
+    around the 2 GiB and 4 GiB byte offsets, are checked against the oracle's
+    one-element source index."""
+    needs_gpu()
+    N, B, S, Hq, Hkv, d = 8, 2, 98304, 32, 8, 128
+    print("beyond 4 GiB", mode, layout, flush=True)
+    plan = b.basp_plan_create_ex(N, B, S, Hq, Hkv, d, b.BASP_INT32, mode, layout)
+    i = plan.info
+    nq, nkv = i["q_elems"], i["kv_elems"]
+    assert 4 * i["qkv_elems"] > 2**32 and 4 * nq > 2**31
+    q = inputs.tags_int32(nq, 0, "cuda")
+    k = inputs.tags_int32(nkv, nq, "cuda")
+    v = inputs.tags_int32(nkv, nq + nkv, "cuda")
+    out = torch.empty(i["qkv_elems"], dtype=torch.int32, device="cuda")
+    b.basp_seq_to_head(plan, q, k, v, out)
+    rng = np.random.default_rng(7)
+    edges = [(1 << 29) + x for x in range(-3, 3)] + [(1 << 30) + x for x in range(-3, 3)]
+    for base, n, H in ((0, nq, Hq), (nq, nkv, Hkv), (nq + nkv, nkv, Hkv)):
+        dst = _sample(n, rng, [e - base for e in edges])
+        got = out[torch.from_numpy(dst + base).cuda()].cpu().numpy().astype(np.int64)
+        want = oracle.source_index(0, dst, mode, N, B, S, H, d, layout) + base
+        assert np.array_equal(got, want), "seq->head mismatch in the tensor at %d" % base
+    del q, k, v, out
+    o = inputs.tags_int32(nq, 0, "cuda")
+    back = torch.empty_like(o)
+    b.basp_head_to_seq(plan, o, back)
+    dst = _sample(nq, rng, edges)
+    got = back[torch.from_numpy(dst).cuda()].cpu().numpy().astype(np.int64)
+    assert np.array_equal(got, oracle.source_index(1, dst, mode, N, B, S, Hq, d, layout))
+    del o, back
+    torch.cuda.empty_cache()
+
+
+def test_side_stream():
+    """The library launches on the stream it is given: torch's current stream
+    (a side stream here), or an explicit handle."""
+    needs_gpu()
+    shape = (6, 3, 6 * 37, 12, 6, 40)
+    N, B, S, Hq, Hkv, d = shape
+    plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, 1)
+    q, k, v = (x.cuda() for x in seq_inputs(B, S, Hq, Hkv, d, "bf16"))
+    want = oracle.seq_to_head_qkv(bits(q), bits(k), bits(v), 1, N, B, S, Hq, Hkv, d)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()   # default priority
+    with torch.cuda.stream(side):
+        out = torch.empty(plan.info["qkv_elems"], dtype=torch.bfloat16, device="cuda")
+        b.basp_seq_to_head(plan, q, k, v, out)
+    side.synchronize()
+    assert np.array_equal(bits(out), want)
+    out2 = torch.empty_like(out)
+    b.basp_seq_to_head(plan, q, k, v, out2, stream=side.cuda_stream)
+    side.synchronize()
+    assert np.array_equal(bits(out2), want)

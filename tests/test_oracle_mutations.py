@@ -45,6 +45,10 @@ MUTANTS = [
     ("head_check_dropped", "if (S % *P != 0 || H % *P != 0)", "if (S % *P != 0)", 0),
     ("element_size_ignored", "memcpy((char *)dst + di * es, (const char *)src + si * es, (size_t)es);",
      "memcpy((char *)dst + di * es, (const char *)src + si * es, 2);", 0),
+    ("one_element_token_rule_swapped", "src[i] = seq_offset(g * P + s / St, bl, s % St, j * Hl + hl, e, Bl, St, H, d);",
+     "src[i] = seq_offset(g * P + s % P, bl, s / P, j * Hl + hl, e, Bl, St, H, d);", 0),
+    ("one_element_head_rule_swapped", "src[i] = head_offset(layout, g * P + h / Hl, bl, h % Hl, j * St + t, e, Bl, Hl, S, d);",
+     "src[i] = head_offset(layout, g * P + h % P, bl, h / P, j * St + t, e, Bl, Hl, S, d);", 0),
     ("source_index_off_by_one_channel", "in, seq_offset(src_rank, bl, t, h, e, Bl, St, H, d), es);",
      "in, seq_offset(src_rank, bl, t, h, (e + 1) % d, Bl, St, H, d), es);", 0),
 ]
