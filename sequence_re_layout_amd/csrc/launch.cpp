@@ -57,6 +57,14 @@ Shape resolve(const basp_plan &p, const basp_tuning &t, bool s2h)
     return s;
 }
 
+// LDS staging exists for 16-byte vectors and rows of at most one pass of
+// the work-group; elsewhere the same tile runs through the direct kernel.
+Shape for_vector_width(Shape sh, int vw, uint32_t A)
+{
+    sh.stage = sh.stage && vw == 16 && A <= uint32_t(kBlock * sh.vpt);
+    return sh;
+}
+
 uint64_t addr(const void *p) { return reinterpret_cast<uint64_t>(p); }
 
 // Widest vector (16, 8, 4 or 2 bytes, never below the element size) that
@@ -167,9 +175,8 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
     }
     const int vw = vector_width(p, addrs, 2 * nseg);
     const uint32_t A = uint32_t(p.row_bytes / vw);
-    Shape sh = resolve(p, p.tuning[s2h ? BASP_SEQ_TO_HEAD : BASP_HEAD_TO_SEQ], s2h);
-    // LDS staging exists for 16-byte vectors and rows that fit one pass
-    sh.stage = sh.stage && vw == 16 && A <= uint32_t(kBlock * sh.vpt);
+    const Shape sh =
+        for_vector_width(resolve(p, p.tuning[s2h ? BASP_SEQ_TO_HEAD : BASP_HEAD_TO_SEQ], s2h), vw, A);
     TileDesc &D = L.D;
     D.St = uint32_t(p.St);
     D.row = uint32_t(p.row_bytes);
@@ -313,12 +320,14 @@ basp_status check_launch_limits(const basp_plan &p, const basp_tuning &t, bool s
     if (p.St > int64_t(kI31Max) || p.row_bytes > int64_t(kI31Max) ||
         int64_t(p.Hq) * p.row_bytes > int64_t(kI31Max))
         return BASP_ERR_UNSUPPORTED;
-    const Shape sh = resolve(p, t, s2h);
+    const Shape resolved = resolve(p, t, s2h);
     const uint32_t heads[3] = {uint32_t(p.Hq), uint32_t(p.Hkv), uint32_t(p.Hkv)};
+    // every vector width a launch may pick, with the tile it then uses
     for (int vw = 16; vw >= p.es; vw /= 2) {
         if (p.row_bytes % vw)
             continue;
         const uint32_t A = uint32_t(p.row_bytes / vw);
+        const Shape sh = for_vector_width(resolved, vw, A);
         uint64_t total = 0;
         for (int i = 0; i < 3; ++i) {
             TileShape ts;

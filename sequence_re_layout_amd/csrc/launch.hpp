@@ -19,7 +19,10 @@
 // token block tb fastest, the order of the head-sharded layout, or
 // (g, js, bl, tb, jh, hb), head block hb fastest, the order of the
 // sequence-sharded layout: neighbouring tiles, which run at the same time,
-// then share the DRAM pages of one side.
+// then share the DRAM pages of one side.  Optionally each of the 8 XCDs takes
+// one contiguous eighth of that order (xcd_tile).  The staged variant passes
+// each tile through LDS in one pass: loads in the source's contiguous order,
+// stores in the destination's (tile_vector with an explicit lane order).
 //
 // Perm kernel (unfused baseline).  Writes its destination linearly; row i of
 // the destination has digits (d0..d4), d4 fastest, and is read from source
