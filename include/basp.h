@@ -215,7 +215,10 @@ basp_status basp_seq_to_head_unfused(const basp_plan *plan, const void *q, const
  *   tile_tokens          tokens per work tile (>= 1)
  *   tile_heads           heads per work tile (>= 1, clamped to H/P)
  *   cache_policy         1 = plain loads and stores, 2 = non-temporal stores,
- *                        3 = non-temporal loads and stores (built-in)
+ *                        3 = non-temporal loads and stores, 4 = non-temporal
+ *                        loads, non-temporal device-scope stores (gfx950
+ *                        NT + SC1; built-in), 5 = non-temporal system-scope
+ *                        loads and stores (NT + SC0 + SC1)
  *   max_grid             cap on work-groups per launch (tiles loop beyond it)
  *   lane_order           1 = lanes run along tokens first, 2 = along heads first
  *   xcd_remap            1 = tiles in work-group order, 2 = each of the 8 XCDs
@@ -227,7 +230,10 @@ basp_status basp_seq_to_head_unfused(const basp_plan *plan, const void *q, const
  *                        2 = each tile passes through LDS: loads
  *                        run along the source's contiguous axis, stores along
  *                        the destination's (used with 16-byte vectors and
- *                        tiles of at most 256*vectors_per_thread vectors)
+ *                        tiles of one pass of the work-group)
+ *   block_size           threads per work-group: 64, 128 or 256 (built-in)
+ * vectors_per_thread and block_size apply to 16-byte vectors; rows or
+ * pointers that need narrower vectors run 256 threads with 4 vectors each.
  * basp_plan_set_tuning sets both directions, basp_plan_set_direction_tuning
  * one; basp_plan_get_tuning reads one.  Errors: BASP_ERR_INVALID on a NULL
  * argument, an unknown direction or an out-of-range field;
@@ -249,6 +255,7 @@ typedef struct basp_tuning {
     int32_t xcd_remap;
     int32_t tile_order;
     int32_t stage;
+    int32_t block_size;
 } basp_tuning;
 basp_status basp_plan_set_tuning(basp_plan *plan, const basp_tuning *tuning);
 basp_status basp_plan_set_direction_tuning(basp_plan *plan, basp_direction dir,

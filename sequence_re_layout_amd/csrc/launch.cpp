@@ -19,17 +19,18 @@ constexpr uint32_t kGridCap = 1u << 22;  // work-groups per launch at most
 // defaults below, chosen on MI355X over every named workload of at least
 // 256 MiB (Llama/Qwen shapes, 128- and 256-byte rows, both modes, rotating
 // buffers) as the launch shape whose worst ratio to each workload's best was
-// highest (0.94 to 0.97).  All use non-temporal loads and stores and two
-// 16-byte vectors per lane.
-//   seq->head, 128-byte rows:  LDS-staged, 4 heads per tile, token blocks
-//                              fastest, XCD-contiguous
-//   seq->head, longer rows:    LDS-staged, 8 heads, head blocks fastest
-//   head->seq, 128-byte rows:  LDS-staged, 8 heads, head blocks fastest
-//   head->seq, longer rows:    direct, 1 head, head blocks fastest, lanes
-//                              along tokens
+// highest (0.94 to 0.98).  All are direct (no LDS staging), with 256 threads
+// per work-group, non-temporal loads and non-temporal device-scope stores.
+//   seq->head: token blocks fastest, XCD-contiguous, lanes along heads;
+//              4 heads per tile and 2 vectors per lane for 128-byte rows,
+//              1 head and 1 vector for longer rows
+//   head->seq: head blocks fastest, work-group order, 8 heads per tile,
+//              2 vectors per lane; lanes along heads for 128-byte rows,
+//              along tokens for longer rows
 // basp_plan_autotune replaces these by measurement.
 struct Shape {
     int vpt, policy;
+    int block;                          // threads per work-group
     uint32_t tile_tokens, tile_heads;   // tile_tokens 0: derived
     bool heads_given;                   // tile_heads set by the tuning
     bool s_fast;
@@ -42,26 +43,32 @@ struct Shape {
 Shape resolve(const basp_plan &p, const basp_tuning &t, bool s2h)
 {
     const bool short_rows = p.row_bytes <= 128;
-    const bool staged = s2h || short_rows;
     Shape s;
-    s.vpt = t.vectors_per_thread ? t.vectors_per_thread : 2;
-    s.policy = t.cache_policy ? t.cache_policy : 3;
+    s.vpt = t.vectors_per_thread ? t.vectors_per_thread : (s2h && !short_rows ? 1 : 2);
+    s.policy = t.cache_policy ? t.cache_policy : 4;
+    s.block = t.block_size ? t.block_size : kBlock;
     s.tile_tokens = uint32_t(t.tile_tokens);
-    s.tile_heads = t.tile_heads ? uint32_t(t.tile_heads) : (s2h && short_rows ? 4 : (staged ? 8 : 1));
+    s.tile_heads = t.tile_heads ? uint32_t(t.tile_heads) : (s2h ? (short_rows ? 4 : 1) : 8);
     s.heads_given = t.tile_heads != 0;
-    s.s_fast = t.lane_order ? t.lane_order == 1 : !staged;
-    s.heads_first = t.tile_order ? t.tile_order == 2 : !(s2h && short_rows);
+    s.s_fast = t.lane_order ? t.lane_order == 1 : (!s2h && !short_rows);
+    s.heads_first = t.tile_order ? t.tile_order == 2 : !s2h;
     s.grid_cap = t.max_grid ? uint32_t(t.max_grid) : kGridCap;
-    s.xcd = t.xcd_remap ? t.xcd_remap == 2 : (s2h && short_rows);
-    s.stage = t.stage ? t.stage == 2 : staged;
+    s.xcd = t.xcd_remap ? t.xcd_remap == 2 : s2h;
+    s.stage = t.stage == 2;
     return s;
 }
 
-// LDS staging exists for 16-byte vectors and rows of at most one pass of
-// the work-group; elsewhere the same tile runs through the direct kernel.
+// The launch shape a vector width runs with.  The tuned work-group size and
+// vectors per lane, and LDS staging (for rows of at most one pass of the
+// work-group), exist for 16-byte vectors; narrower vectors run the direct
+// kernel with 256 threads and 4 vectors per lane.
 Shape for_vector_width(Shape sh, int vw, uint32_t A)
 {
-    sh.stage = sh.stage && vw == 16 && A <= uint32_t(kBlock * sh.vpt);
+    if (vw != 16) {
+        sh.block = kBlock;
+        sh.vpt = 4;
+    }
+    sh.stage = sh.stage && vw == 16 && A <= uint32_t(sh.block * sh.vpt);
     return sh;
 }
 
@@ -88,11 +95,11 @@ struct TileShape {
     uint64_t ntiles;
 };
 
-// Tile of one tensor with Hl heads per rank and A vectors per row: about
-// kBlock*vpt vectors unless the tile extent is given.
+// Tile of one tensor with Hl heads per rank and A vectors per row: about one
+// pass of the work-group (block * vpt vectors) unless the tile extent is given.
 TileShape tile_shape(const basp_plan &p, const Shape &sh, uint32_t Hl, uint32_t A)
 {
-    const uint64_t rows = std::max<uint64_t>(1, uint64_t(kBlock) * sh.vpt / A);
+    const uint64_t rows = std::max<uint64_t>(1, uint64_t(sh.block) * sh.vpt / A);
     uint64_t th = std::min<uint64_t>(sh.tile_heads, Hl);
     if (sh.stage)   // a staged tile is one pass of the work-group: at most `rows` rows
         th = std::min<uint64_t>(th, rows);
@@ -232,6 +239,7 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
     L.grid = uint32_t(std::min<uint64_t>(total, sh.grid_cap));
     L.vw = vw;
     L.vpt = sh.vpt;
+    L.block = sh.block;
     L.policy = sh.policy;
     L.s2h = s2h;
     L.staged = sh.stage;

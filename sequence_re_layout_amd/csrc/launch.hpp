@@ -37,7 +37,7 @@ struct basp_plan;
 
 namespace basp {
 
-constexpr int kBlock = 256;               // threads per work-group (4 waves)
+constexpr int kBlock = 256;               // threads per work-group unless tuned (4 waves)
 constexpr uint64_t kI31Max = 0x7fffffffull;
 // Buffer descriptors span at most kI31Max bytes and every real offset is
 // below that, so a lane given kOutside touches nothing: its load returns zero
@@ -207,6 +207,7 @@ BASP_HD inline uint32_t perm_source(const PermDesc &D, const PermSeg &sg, uint32
 struct TileLaunch {
     TileDesc D;
     int vw, vpt, policy;
+    int block;                // threads per work-group: 64, 128 or 256
     bool s2h;                 // read sequence-sharded, write head-sharded
     bool staged;              // tiles pass through LDS (one pass per tile)
     uint32_t grid;            // 0: nothing to launch

@@ -38,13 +38,16 @@ template <> struct Vec<8> { typedef u32x2 type; };
 template <> struct Vec<4> { typedef uint32_t type; };
 template <> struct Vec<2> { typedef uint16_t type; };
 
-// Cache-policy bits of gfx940-family memory instructions: bit 1 is NT
-// (non-temporal: the line is not expected to be reused).
-constexpr int kNT = 2;
+// Cache-policy bits of gfx940-family memory instructions: SC0 (bit 0) and
+// SC1 (bit 4) give the coherence scope, NT (bit 1) marks a line that is not
+// expected to be reused.
+constexpr int kSC0 = 1, kNT = 2, kSC1 = 16;
 template <int POL> struct Policy;
 template <> struct Policy<1> { static constexpr int load = 0, store = 0; };
 template <> struct Policy<2> { static constexpr int load = 0, store = kNT; };
 template <> struct Policy<3> { static constexpr int load = kNT, store = kNT; };
+template <> struct Policy<4> { static constexpr int load = kNT, store = kNT | kSC1; };
+template <> struct Policy<5> { static constexpr int load = kNT | kSC0 | kSC1, store = kNT | kSC0 | kSC1; };
 
 // Bytes of a buffer of `bytes` bytes from offset `off` on (0 past the end).
 __device__ inline uint64_t rest(uint64_t bytes, uint64_t off) { return off < bytes ? bytes - off : 0; }
@@ -84,8 +87,8 @@ __device__ inline void vstore(__amdgpu_buffer_rsrc_t r, uint32_t off, typename V
 
 // Fused re-layout of up to three tensors: S2H reads the sequence-sharded
 // side and writes the head-sharded side, !S2H the reverse.
-template <int VW, int VPT, int POL, bool S2H>
-__global__ __launch_bounds__(kBlock) void tile_kernel(const TileDesc D)
+template <int BS, int VW, int VPT, int POL, bool S2H>
+__global__ __launch_bounds__(BS) void tile_kernel(const TileDesc D)
 {
     using V = typename Vec<VW>::type;
     for (uint32_t tile = blockIdx.x; tile < D.ntiles; tile += gridDim.x) {
@@ -95,12 +98,12 @@ __global__ __launch_bounds__(kBlock) void tile_kernel(const TileDesc D)
         const __amdgpu_buffer_rsrc_t rhead =
             make_rsrc(sg.head + o.head_off, rest(sg.head_bytes, o.head_off));
         const uint32_t nvec = sg.Ts.d * sg.Th.d * D.A.d;
-        for (uint32_t v0 = 0; v0 < nvec; v0 += kBlock * VPT) {
+        for (uint32_t v0 = 0; v0 < nvec; v0 += BS * VPT) {
             uint32_t src[VPT], dst[VPT];
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 uint32_t so, ho;
-                const bool ok = lane_offsets(D, sg, o.ns, o.nh, v0 + threadIdx.x + k * kBlock, VW, so, ho);
+                const bool ok = lane_offsets(D, sg, o.ns, o.nh, v0 + threadIdx.x + k * BS, VW, so, ho);
                 src[k] = ok ? (S2H ? so : ho) : kOutside;
                 dst[k] = ok ? (S2H ? ho : so) : kOutside;
             }
@@ -119,11 +122,11 @@ __global__ __launch_bounds__(kBlock) void tile_kernel(const TileDesc D)
 // the source layout's contiguous axis, the stores along the destination's, so
 // both sides of every wave instruction are contiguous.  A tile is one pass of
 // the work-group (the host sizes it to at most kBlock*VPT vectors).
-template <int VPT, int POL, bool S2H>
-__global__ __launch_bounds__(kBlock) void tile_kernel_staged(const TileDesc D)
+template <int BS, int VPT, int POL, bool S2H>
+__global__ __launch_bounds__(BS) void tile_kernel_staged(const TileDesc D)
 {
     using V = typename Vec<16>::type;
-    __shared__ V stage[kBlock * VPT];
+    __shared__ V stage[BS * VPT];
     for (uint32_t tile = blockIdx.x; tile < D.ntiles; tile += gridDim.x) {
         const TileOrigin o = tile_origin(D, tile);
         const TileSeg &sg = D.seg[o.seg];
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(kBlock) void tile_kernel_staged(const TileDesc D)
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             uint32_t so, ho;
-            ok[k] = tile_vector(D, sg, o.ns, o.nh, threadIdx.x + k * kBlock, 16, D.load_s_fast, so,
+            ok[k] = tile_vector(D, sg, o.ns, o.nh, threadIdx.x + k * BS, 16, D.load_s_fast, so,
                                 ho, slot[k]);
             off[k] = ok[k] ? (S2H ? so : ho) : kOutside;
         }
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(kBlock) void tile_kernel_staged(const TileDesc D)
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             uint32_t so, ho;
-            ok[k] = tile_vector(D, sg, o.ns, o.nh, threadIdx.x + k * kBlock, 16, D.store_s_fast, so,
+            ok[k] = tile_vector(D, sg, o.ns, o.nh, threadIdx.x + k * BS, 16, D.store_s_fast, so,
                                 ho, slot[k]);
             off[k] = ok[k] ? (S2H ? ho : so) : kOutside;
             buf[k] = stage[ok[k] ? slot[k] : 0];
@@ -193,66 +196,69 @@ __global__ __launch_bounds__(kBlock) void perm_kernel(const PermDesc D)
 
 typedef void (*TileFn)(const TileDesc);
 
-template <int VW, int VPT, int POL>
-TileFn tile_fn_dir(bool s2h)
+// Kernel instances: 16-byte vectors with every work-group size, vectors per
+// lane, cache policy and direction, direct or staged; narrower vectors direct
+// with 256 threads and 4 vectors per lane.
+template <int BS, int VW, int VPT, int POL>
+TileFn direct_fn(bool s2h)
 {
-    return s2h ? tile_kernel<VW, VPT, POL, true> : tile_kernel<VW, VPT, POL, false>;
+    return s2h ? tile_kernel<BS, VW, VPT, POL, true> : tile_kernel<BS, VW, VPT, POL, false>;
 }
 
-template <int VW, int VPT>
-TileFn tile_fn_pol(int pol, bool s2h)
+template <int BS, int VPT, int POL>
+TileFn staged_fn(bool s2h)
+{
+    return s2h ? tile_kernel_staged<BS, VPT, POL, true> : tile_kernel_staged<BS, VPT, POL, false>;
+}
+
+template <int BS, int VW, int VPT>
+TileFn by_policy(int pol, bool s2h, bool staged)
 {
     switch (pol) {
-    case 1: return tile_fn_dir<VW, VPT, 1>(s2h);
-    case 3: return tile_fn_dir<VW, VPT, 3>(s2h);
-    default: return tile_fn_dir<VW, VPT, 2>(s2h);
+    case 1: return staged ? staged_fn<BS, VPT, 1>(s2h) : direct_fn<BS, VW, VPT, 1>(s2h);
+    case 2: return staged ? staged_fn<BS, VPT, 2>(s2h) : direct_fn<BS, VW, VPT, 2>(s2h);
+    case 4: return staged ? staged_fn<BS, VPT, 4>(s2h) : direct_fn<BS, VW, VPT, 4>(s2h);
+    case 5: return staged ? staged_fn<BS, VPT, 5>(s2h) : direct_fn<BS, VW, VPT, 5>(s2h);
+    default: return staged ? staged_fn<BS, VPT, 3>(s2h) : direct_fn<BS, VW, VPT, 3>(s2h);
+    }
+}
+
+template <int BS>
+TileFn by_vpt(int vpt, int pol, bool s2h, bool staged)
+{
+    switch (vpt) {
+    case 1: return by_policy<BS, 16, 1>(pol, s2h, staged);
+    case 2: return by_policy<BS, 16, 2>(pol, s2h, staged);
+    case 8: return by_policy<BS, 16, 8>(pol, s2h, staged);
+    default: return by_policy<BS, 16, 4>(pol, s2h, staged);
     }
 }
 
 template <int VW>
-TileFn tile_fn_vpt(int vpt, int pol, bool s2h)
-{
-    switch (vpt) {
-    case 1: return tile_fn_pol<VW, 1>(pol, s2h);
-    case 2: return tile_fn_pol<VW, 2>(pol, s2h);
-    case 8: return tile_fn_pol<VW, 8>(pol, s2h);
-    default: return tile_fn_pol<VW, 4>(pol, s2h);
-    }
-}
-
-template <int VPT, int POL>
-TileFn staged_fn_dir(bool s2h)
-{
-    return s2h ? tile_kernel_staged<VPT, POL, true> : tile_kernel_staged<VPT, POL, false>;
-}
-
-template <int VPT>
-TileFn staged_fn_pol(int pol, bool s2h)
+TileFn narrow_fn(int pol, bool s2h)
 {
     switch (pol) {
-    case 1: return staged_fn_dir<VPT, 1>(s2h);
-    case 2: return staged_fn_dir<VPT, 2>(s2h);
-    default: return staged_fn_dir<VPT, 3>(s2h);
+    case 1: return direct_fn<kBlock, VW, 4, 1>(s2h);
+    case 2: return direct_fn<kBlock, VW, 4, 2>(s2h);
+    case 4: return direct_fn<kBlock, VW, 4, 4>(s2h);
+    case 5: return direct_fn<kBlock, VW, 4, 5>(s2h);
+    default: return direct_fn<kBlock, VW, 4, 3>(s2h);
     }
 }
 
-TileFn staged_fn(int vpt, int pol, bool s2h)
+TileFn tile_fn(const TileLaunch &L)
 {
-    switch (vpt) {
-    case 1: return staged_fn_pol<1>(pol, s2h);
-    case 2: return staged_fn_pol<2>(pol, s2h);
-    case 8: return staged_fn_pol<8>(pol, s2h);
-    default: return staged_fn_pol<4>(pol, s2h);
+    if (L.vw == 16) {
+        switch (L.block) {
+        case 64: return by_vpt<64>(L.vpt, L.policy, L.s2h, L.staged);
+        case 128: return by_vpt<128>(L.vpt, L.policy, L.s2h, L.staged);
+        default: return by_vpt<256>(L.vpt, L.policy, L.s2h, L.staged);
+        }
     }
-}
-
-TileFn tile_fn(int vw, int vpt, int pol, bool s2h)
-{
-    switch (vw) {
-    case 16: return tile_fn_vpt<16>(vpt, pol, s2h);
-    case 8: return tile_fn_vpt<8>(vpt, pol, s2h);
-    case 4: return tile_fn_vpt<4>(vpt, pol, s2h);
-    default: return tile_fn_vpt<2>(vpt, pol, s2h);
+    switch (L.vw) {
+    case 8: return narrow_fn<8>(L.policy, L.s2h);
+    case 4: return narrow_fn<4>(L.policy, L.s2h);
+    default: return narrow_fn<2>(L.policy, L.s2h);
     }
 }
 
@@ -266,17 +272,17 @@ thread_local Timing t_timing;
 // code in the process may have left set).  first/last: this launch opens or
 // closes the current entry-point call, for the timing events.
 template <typename Desc>
-basp_status launch_kernel(const void *fn, uint32_t grid, const Desc &D, void *stream, bool first,
-                          bool last)
+basp_status launch_kernel(const void *fn, uint32_t grid, int block, const Desc &D, void *stream,
+                          bool first, bool last)
 {
     void *args[] = {const_cast<Desc *>(&D)};
     const hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (t_timing.start || t_timing.stop)
-        e = hipExtLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, st,
+        e = hipExtLaunchKernel(fn, dim3(grid), dim3(block), args, 0, st,
                                first ? t_timing.start : nullptr, last ? t_timing.stop : nullptr, 0);
     else
-        e = hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, st);
+        e = hipLaunchKernel(fn, dim3(grid), dim3(block), args, 0, st);
     return e == hipSuccess ? BASP_OK : BASP_ERR_HIP;
 }
 
@@ -284,8 +290,8 @@ basp_status launch(const TileLaunch &L, void *stream)
 {
     if (L.grid == 0)
         return BASP_OK;
-    const TileFn fn = L.staged ? staged_fn(L.vpt, L.policy, L.s2h) : tile_fn(L.vw, L.vpt, L.policy, L.s2h);
-    return launch_kernel(reinterpret_cast<const void *>(fn), L.grid, L.D, stream, true, true);
+    return launch_kernel(reinterpret_cast<const void *>(tile_fn(L)), L.grid, L.block, L.D, stream,
+                         true, true);
 }
 
 basp_status launch(const PermLaunch &L, void *stream, bool first, bool last)
@@ -299,7 +305,7 @@ basp_status launch(const PermLaunch &L, void *stream, bool first, bool last)
     case 4: fn = reinterpret_cast<const void *>(perm_kernel<4>); break;
     default: fn = reinterpret_cast<const void *>(perm_kernel<2>); break;
     }
-    return launch_kernel(fn, L.grid, L.D, stream, first, last);
+    return launch_kernel(fn, L.grid, kBlock, L.D, stream, first, last);
 }
 
 // Runs f, the body of an entry point, and clears the timing request after it.
@@ -313,43 +319,34 @@ basp_status timed_call(F f)
 
 // ---------------------------------------------------------------- autotune --
 
-// Launch shapes a plan is measured with: tile order x vectors per lane x
-// heads per tile x lane order x XCD order x grid cap, and the LDS-staged
-// kernel over tile order x vectors per lane x heads per tile x XCD order; all
-// with non-temporal loads and stores (the policy every sweep preferred).
+// Launch shapes a plan is measured with, all with non-temporal loads and
+// non-temporal device-scope stores (the policy the sweeps preferred) and 64
+// or 256 threads per work-group: direct over tile order x vectors per lane x
+// heads per tile x lane order x XCD order, and LDS-staged over tile order x
+// vectors per lane x heads per tile x XCD order.
 std::vector<basp_tuning> autotune_candidates()
 {
     std::vector<basp_tuning> c;
-    for (int to : {1, 2})
-        for (int vpt : {1, 2, 4})
-            for (int th : {1, 2, 4, 8})
-                for (int xcd : {1, 2}) {
-                    basp_tuning t = {};
-                    t.vectors_per_thread = vpt;
-                    t.tile_heads = th;
-                    t.cache_policy = 3;
-                    t.xcd_remap = xcd;
-                    t.tile_order = to;
-                    t.stage = 2;
-                    c.push_back(t);
-                }
-    for (int to : {1, 2})
-        for (int vpt : {1, 2, 4})
-            for (int th : {1, 2, 4, 8})
-                for (int lo : {1, 2})
-                    for (int xcd : {1, 2})
-                        for (int grid : {0, 8192}) {
-                            basp_tuning t = {};
-                            t.vectors_per_thread = vpt;
-                            t.tile_heads = th;
-                            t.cache_policy = 3;
-                            t.max_grid = grid;
+    for (int block : {64, 256})
+        for (int to : {1, 2})
+            for (int vpt : {1, 2, 4})
+                for (int th : {1, 2, 4, 8})
+                    for (int xcd : {1, 2}) {
+                        basp_tuning t = {};
+                        t.block_size = block;
+                        t.tile_order = to;
+                        t.vectors_per_thread = vpt;
+                        t.tile_heads = th;
+                        t.xcd_remap = xcd;
+                        t.cache_policy = 4;
+                        t.stage = 2;
+                        c.push_back(t);
+                        t.stage = 1;
+                        for (int lo : {1, 2}) {
                             t.lane_order = lo;
-                            t.xcd_remap = xcd;
-                            t.tile_order = to;
-                            t.stage = 1;
                             c.push_back(t);
                         }
+                    }
     return c;
 }
 

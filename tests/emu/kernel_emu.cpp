@@ -31,7 +31,7 @@ void copy(uint64_t dst, uint64_t src, uint32_t vw)
 void run(const TileLaunch &L, uint64_t *bad)
 {
     const TileDesc &D = L.D;
-    std::vector<unsigned char> lds(size_t(kBlock) * L.vpt * 16);
+    std::vector<unsigned char> lds(size_t(L.block) * L.vpt * 16);
     for (uint32_t block = 0; block < L.grid; ++block) {
         for (uint32_t tile = block; tile < D.ntiles; tile += L.grid) {
             const TileOrigin o = tile_origin(D, tile);
@@ -44,7 +44,7 @@ void run(const TileLaunch &L, uint64_t *bad)
             if (L.staged) {
                 // one pass: every vector of the tile, loads in the load order
                 // into the staging slots, then stores in the store order
-                const uint32_t nv = uint32_t(kBlock) * L.vpt;
+                const uint32_t nv = uint32_t(L.block) * L.vpt;
                 if (sg.Ts.d * sg.Th.d * D.A.d > nv) {
                     ++*bad;
                     continue;
@@ -68,7 +68,7 @@ void run(const TileLaunch &L, uint64_t *bad)
                 continue;
             }
             const uint32_t nvec = sg.Ts.d * sg.Th.d * D.A.d;
-            const uint32_t step = kBlock * L.vpt;
+            const uint32_t step = L.block * L.vpt;
             const uint32_t vend = (nvec + step - 1) / step * step;
             for (uint32_t v = 0; v < vend; ++v) {
                 uint32_t so, ho;

@@ -167,7 +167,9 @@ TUNINGS = [dict(vectors_per_thread=1), dict(vectors_per_thread=2), dict(vectors_
            dict(xcd_remap=2, max_grid=13, lane_order=2),
            dict(tile_order=1), dict(tile_order=2, tile_heads=3, tile_tokens=5, max_grid=11),
            dict(stage=2), dict(stage=2, vectors_per_thread=1, tile_heads=8, cache_policy=2),
-           dict(stage=2, vectors_per_thread=8, tile_tokens=500, tile_order=2, max_grid=5)]
+           dict(stage=2, vectors_per_thread=8, tile_tokens=500, tile_order=2, max_grid=5),
+           dict(block_size=64, cache_policy=4), dict(block_size=128, stage=2, vectors_per_thread=8, cache_policy=5),
+           dict(block_size=64, stage=1, tile_tokens=9, max_grid=7)]
 
 
 @pytest.mark.parametrize("tuning", TUNINGS, ids=lambda t: ",".join("%s=%s" % kv for kv in t.items()))
@@ -405,7 +407,7 @@ def test_autotune_keeps_results(shape, mode):
     b.basp_plan_autotune(plan, q, k, v, qkv, o, o_out)
     for direction in (b.BASP_SEQ_TO_HEAD, b.BASP_HEAD_TO_SEQ):
         t = b.basp_plan_get_tuning(plan, direction)
-        assert t["vectors_per_thread"] in (1, 2, 4) and t["cache_policy"] == 3
+        assert t["vectors_per_thread"] in (1, 2, 4) and t["cache_policy"] == 4
         assert t["stage"] in (1, 2) and t["tile_order"] in (1, 2)   # explicit, not "built-in"
     qkv.fill_(0)
     o_out.fill_(0)

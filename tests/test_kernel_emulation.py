@@ -35,7 +35,7 @@ def emu(tmp_path_factory):
     lib.basp_plan_create_ex.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32]
     lib.basp_plan_create_ex.restype = vp
     lib.basp_plan_destroy.argtypes = [vp]
-    lib.basp_plan_set_tuning.argtypes = [vp, ctypes.POINTER(ctypes.c_int32 * 9)]
+    lib.basp_plan_set_tuning.argtypes = [vp, ctypes.POINTER(ctypes.c_int32 * 10)]
     lib.basp_plan_set_tuning.restype = i32
     tail = [ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_int)]
     lib.emu_seq_to_head.argtypes = [vp, vp, vp, vp, vp] + tail
@@ -58,9 +58,9 @@ class Run:
         self.plan = lib.basp_plan_create_ex(N, B, S, Hq, Hkv, d, dtype, mode, layout)
         assert self.plan, "plan rejected"
         if tuning:
-            t = (ctypes.c_int32 * 9)(*[tuning.get(k, 0) for k in (
+            t = (ctypes.c_int32 * 10)(*[tuning.get(k, 0) for k in (
                 "vectors_per_thread", "tile_tokens", "tile_heads", "cache_policy", "max_grid",
-                "lane_order", "xcd_remap", "tile_order", "stage")])
+                "lane_order", "xcd_remap", "tile_order", "stage", "block_size")])
             assert lib.basp_plan_set_tuning(self.plan, ctypes.byref(t)) == 0
 
     def __call__(self, fn, *arrays):
@@ -147,7 +147,10 @@ TUNINGS = [dict(vectors_per_thread=1), dict(vectors_per_thread=2), dict(vectors_
            dict(tile_order=1), dict(tile_order=2), dict(tile_order=2, tile_heads=3, tile_tokens=5, max_grid=11),
            dict(tile_order=1, xcd_remap=2, lane_order=2, tile_heads=2),
            dict(stage=2), dict(stage=2, vectors_per_thread=1, tile_heads=8), dict(stage=2, vectors_per_thread=8, tile_tokens=500),
-           dict(stage=2, tile_order=2, xcd_remap=2, tile_heads=3, max_grid=5)]
+           dict(stage=2, tile_order=2, xcd_remap=2, tile_heads=3, max_grid=5),
+           dict(block_size=64), dict(block_size=128, vectors_per_thread=1, stage=1),
+           dict(block_size=64, stage=2, vectors_per_thread=8, tile_heads=8), dict(block_size=64, stage=1, tile_tokens=9),
+           dict(cache_policy=4), dict(cache_policy=5, block_size=128, stage=2)]
 
 
 @pytest.mark.parametrize("tuning", TUNINGS, ids=lambda t: ",".join("%s=%s" % kv for kv in t.items()))
