@@ -350,28 +350,83 @@ std::vector<basp_tuning> autotune_candidates()
     return c;
 }
 
-// Median kernel time (ms) of `reps` launches of one tile launch, each timed
-// from its own dispatch timestamps; after one untimed launch.  -1 on error.
-float time_tile_launch(const TileLaunch &L, void *stream, hipEvent_t *ev, int reps)
+// One timed launch of the autotuner: a direction and a candidate shape.
+struct Job {
+    int dir, cand;
+    float ms;
+};
+
+// Launch every job once, each timed from its own dispatch timestamps, in
+// batches of kPool launches that share a pool of events.  False on a HIP
+// error; a job whose shape the plan rejects gets a time < 0.
+constexpr int kPool = 64;
+
+bool run_jobs(basp_plan &p, const std::vector<basp_tuning> &cands, std::vector<Job> &jobs,
+              const void *q, const void *k, const void *v, void *qkv, const void *o, void *o_out,
+              void *stream, hipEvent_t *ev)
 {
-    if (launch(L, stream) != BASP_OK)
-        return -1.f;
-    std::vector<float> ms(reps);
-    for (int r = 0; r < reps; ++r) {
-        t_timing.start = ev[2 * r];
-        t_timing.stop = ev[2 * r + 1];
-        const basp_status s = launch(L, stream);
-        t_timing = Timing();
-        if (s != BASP_OK)
-            return -1.f;
+    for (size_t first = 0; first < jobs.size(); first += kPool) {
+        const size_t last = std::min(jobs.size(), first + kPool);
+        for (size_t j = first; j < last; ++j) {
+            Job &job = jobs[j];
+            p.tuning[job.dir] = cands[job.cand];
+            TileLaunch L;
+            const int st = job.dir == BASP_SEQ_TO_HEAD ? prepare_seq_to_head(p, q, k, v, qkv, L)
+                                                       : prepare_head_to_seq(p, o, o_out, L);
+            job.ms = -1.f;
+            if (st != BASP_OK)
+                continue;
+            t_timing.start = ev[2 * (j - first)];
+            t_timing.stop = ev[2 * (j - first) + 1];
+            const basp_status ls = launch(L, stream);
+            t_timing = Timing();
+            if (ls != BASP_OK)
+                return false;
+            job.ms = 0.f;
+        }
+        if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+            return false;
+        for (size_t j = first; j < last; ++j)
+            if (jobs[j].ms == 0.f &&
+                hipEventElapsedTime(&jobs[j].ms, ev[2 * (j - first)], ev[2 * (j - first) + 1]) != hipSuccess)
+                return false;
     }
-    if (hipEventSynchronize(ev[2 * reps - 1]) != hipSuccess)
-        return -1.f;
-    for (int r = 0; r < reps; ++r)
-        if (hipEventElapsedTime(&ms[r], ev[2 * r], ev[2 * r + 1]) != hipSuccess)
-            return -1.f;
-    std::nth_element(ms.begin(), ms.begin() + reps / 2, ms.end());
-    return ms[reps / 2];
+    return true;
+}
+
+// Median time of each (direction, candidate) over `rounds` rounds in which
+// every pair is launched once, seq->head and head->seq alternating, so that
+// each launch follows one that streamed other buffers and slow drifts of the
+// device affect all candidates alike.
+bool measure_rounds(basp_plan &p, const std::vector<basp_tuning> &cands,
+                    const std::vector<int> (&pick)[2], int rounds, std::vector<float> (&med)[2],
+                    const void *q, const void *k, const void *v, void *qkv, const void *o,
+                    void *o_out, void *stream, hipEvent_t *ev)
+{
+    const size_t n = std::max(pick[0].size(), pick[1].size());
+    std::vector<std::vector<float>> times[2];
+    times[0].assign(pick[0].size(), {});
+    times[1].assign(pick[1].size(), {});
+    for (int r = 0; r < rounds; ++r) {
+        std::vector<Job> jobs;
+        for (size_t i = 0; i < n; ++i)
+            for (int dir = 0; dir < 2; ++dir)
+                if (i < pick[dir].size())
+                    jobs.push_back({dir, pick[dir][i], 0.f});
+        if (!run_jobs(p, cands, jobs, q, k, v, qkv, o, o_out, stream, ev))
+            return false;
+        size_t idx[2] = {0, 0};
+        for (const Job &job : jobs)
+            times[job.dir][idx[job.dir]++].push_back(job.ms);
+    }
+    for (int dir = 0; dir < 2; ++dir) {
+        med[dir].clear();
+        for (std::vector<float> &t : times[dir]) {
+            std::nth_element(t.begin(), t.begin() + t.size() / 2, t.end());
+            med[dir].push_back(t[t.size() / 2]);
+        }
+    }
+    return true;
 }
 
 }  // namespace
@@ -393,56 +448,54 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
     if (s != BASP_OK || p->S == 0)
         return record(basp_status(s));
 
-    constexpr int kCoarse = 3, kFine = 9, kKeep = 4;
-    hipEvent_t ev[2 * kFine];
+    constexpr int kCoarse = 3, kFine = 7, kKeep = 6;
+    hipEvent_t ev[2 * basp::kPool];
     int made = 0;
-    for (; made < 2 * kFine; ++made)
+    for (; made < 2 * basp::kPool; ++made)
         if (hipEventCreate(&ev[made]) != hipSuccess)
             break;
     const basp_tuning saved[2] = {p->tuning[0], p->tuning[1]};
-    basp_status status = made == 2 * kFine ? BASP_OK : BASP_ERR_HIP;
+    bool ok = made == 2 * basp::kPool;
     const std::vector<basp_tuning> cands = basp::autotune_candidates();
-    for (int dir = 0; dir < 2 && status == BASP_OK; ++dir) {
-        const bool s2h = dir == BASP_SEQ_TO_HEAD;
-        auto measure = [&](const basp_tuning &t, int reps) -> float {
-            p->tuning[dir] = t;
-            const int st = s2h ? basp::prepare_seq_to_head(*p, q, k, v, qkv, L)
-                               : basp::prepare_head_to_seq(*p, o, o_out, L);
-            return st == BASP_OK ? basp::time_tile_launch(L, stream, ev, reps) : -2.f;
-        };
-        std::vector<std::pair<float, int>> coarse;
-        for (int i = 0; i < int(cands.size()) && status == BASP_OK; ++i) {
-            if (basp::check_launch_limits(*p, cands[i], s2h) != BASP_OK)
-                continue;
-            const float ms = measure(cands[i], kCoarse);
-            if (ms == -1.f)
-                status = BASP_ERR_HIP;
-            else if (ms >= 0.f)
-                coarse.push_back({ms, i});
-        }
-        if (status != BASP_OK || coarse.empty())
-            break;
-        std::sort(coarse.begin(), coarse.end());
-        float best = -1.f;
-        basp_tuning pick = cands[coarse[0].second];
-        for (int j = 0; j < int(coarse.size()) && j < kKeep && status == BASP_OK; ++j) {
-            const float ms = measure(cands[coarse[j].second], kFine);
-            if (ms == -1.f)
-                status = BASP_ERR_HIP;
-            else if (ms >= 0.f && (best < 0.f || ms < best)) {
-                best = ms;
-                pick = cands[coarse[j].second];
-            }
-        }
-        p->tuning[dir] = pick;
+    std::vector<int> pick[2];
+    for (int dir = 0; dir < 2; ++dir)
+        for (int i = 0; i < int(cands.size()); ++i)
+            if (basp::check_launch_limits(*p, cands[i], dir == BASP_SEQ_TO_HEAD) == BASP_OK)
+                pick[dir].push_back(i);
+    std::vector<float> med[2];
+    // coarse pass over every candidate, then a longer one over the best few;
+    // a direction without any measured candidate keeps its tuning
+    ok = ok && basp::measure_rounds(*p, cands, pick, kCoarse, med, q, k, v, qkv, o, o_out, stream, ev);
+    for (int dir = 0; dir < 2 && ok; ++dir) {
+        std::vector<std::pair<float, int>> order;
+        for (size_t i = 0; i < pick[dir].size(); ++i)
+            if (med[dir][i] > 0.f)
+                order.push_back({med[dir][i], pick[dir][i]});
+        std::sort(order.begin(), order.end());
+        pick[dir].clear();
+        for (size_t i = 0; i < order.size() && int(i) < kKeep; ++i)
+            pick[dir].push_back(order[i].second);
     }
+    ok = ok && basp::measure_rounds(*p, cands, pick, kFine, med, q, k, v, qkv, o, o_out, stream, ev);
+    basp_tuning chosen[2] = {saved[0], saved[1]};
+    for (int dir = 0; dir < 2 && ok; ++dir) {
+        int best = -1;
+        for (size_t i = 0; i < pick[dir].size(); ++i)
+            if (med[dir][i] > 0.f && (best < 0 || med[dir][i] < med[dir][best]))
+                best = int(i);
+        if (best >= 0)
+            chosen[dir] = cands[pick[dir][best]];
+    }
+    p->tuning[0] = chosen[0];
+    p->tuning[1] = chosen[1];
     for (int i = 0; i < made; ++i)
         (void)hipEventDestroy(ev[i]);
-    if (status != BASP_OK) {
+    if (!ok) {
         p->tuning[0] = saved[0];
         p->tuning[1] = saved[1];
+        return record(BASP_ERR_HIP);
     }
-    return record(status);
+    return record(BASP_OK);
 }
 
 extern "C" basp_status basp_time_next_call(void *start_event, void *stop_event)
