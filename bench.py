@@ -21,9 +21,11 @@ the 8 TB/s HBM peak, its duration taken from HIP events that its own launch
 records (hipExtLaunchKernel start/stop timestamps, via basp_time_next_call)
 on the stream it runs on, on every --sample-every'th step of the timed
 region.  ``detail`` holds per-kernel rates of both modes, the unfused
-three-pass baseline, the backward entry points, the token-major layout and a
-plain device copy; ``workloads`` the fused seq->head and head->seq rates of
-every named workload in both modes.  ``cpu_baseline`` is the CPU oracle
+three-pass baseline, the backward entry points, the token-major layout and
+torch's device copy; ``workloads`` the fused seq->head and head->seq rates of
+every named workload in both modes.  ``copy_ceiling`` is basp_stream_copy,
+a plain copy with the kernels' access rules, at the same byte counts: the
+rate a read-once, write-once kernel reaches on this part.  ``cpu_baseline`` is the CPU oracle
 doing the same step on the host, repeated for about --cpu-seconds.
 
     python bench.py --pmc-summary FETCH_DIR WRITE_DIR
@@ -232,6 +234,11 @@ def run_gpu(args):
         "h2s_gbs": rate(w.h2s_bytes, statistics.mean(h2s_t)),
     }
 
+    # the ceiling: basp_stream_copy (a plain read-once/write-once copy with
+    # the same access rules) at the byte counts of the two kernels, timed the
+    # same way on rotating buffers
+    res["copy_ceiling"] = copy_ceiling(b, (w.s2h_bytes, w.h2s_bytes), 100)
+
     # device round trip of the timed buffers: head->seq of the Q part of the
     # fused output must give Q back bit for bit
     s = sets[0]
@@ -257,6 +264,27 @@ def run_gpu(args):
                      "autotuned": not args.no_autotune}
     res["w"] = w
     return res
+
+
+def copy_ceiling(b, moved, n):
+    """Average duration and rate of basp_stream_copy moving each byte count
+    in `moved` (read + write: a copy of moved/2 bytes), n timed launches each
+    on buffer sets more than 1 GiB apart."""
+    import torch
+    out = {}
+    for m in moved:
+        nb = m // 2
+        R = max(2, -(-(3 << 30) // m))
+        src = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(R)]
+        dst = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(R)]
+        for i in range(R):
+            b.basp_stream_copy(dst[i], src[i])
+        t = time_launches(b, lambda i: b.basp_stream_copy(dst[i], src[i]), n, R)
+        out[str(m)] = {"bytes_moved": m, "avg_us": statistics.mean(t) * 1e6,
+                       "median_us": statistics.median(t) * 1e6, "gbs": rate(m, statistics.mean(t))}
+        del src, dst
+        torch.cuda.empty_cache()
+    return out
 
 
 def detail(args, b, w):
@@ -344,7 +372,7 @@ def workload_table(b, iters, autotune):
             sets = []
             for _ in range(R):
                 x = torch.empty(2 * i["q_elems"] + 2 * i["kv_elems"], dtype=torch.bfloat16, device="cuda").normal_()
-                sets.append({"q": x[:i["q_elems"]], "k": x[i["q_elems"]:i["q_elems"] + i["kv_elems"]],
+                sets.append({"x": x, "q": x[:i["q_elems"]], "k": x[i["q_elems"]:i["q_elems"] + i["kv_elems"]],
                              "v": x[i["q_elems"] + i["kv_elems"]:i["q_elems"] + 2 * i["kv_elems"]],
                              "o": x[i["q_elems"] + 2 * i["kv_elems"]:],
                              "out": torch.empty(i["qkv_elems"], dtype=torch.bfloat16, device="cuda"),
@@ -362,6 +390,13 @@ def workload_table(b, iters, autotune):
                 "s2h_gbs": rate(i["qkv_bytes_moved"], t), "s2h_frac": rate(i["qkv_bytes_moved"], t) / HBM_PEAK_GBS,
                 "h2s_bytes": i["o_bytes_moved"], "h2s_us": u * 1e6,
                 "h2s_gbs": rate(i["o_bytes_moved"], u), "h2s_frac": rate(i["o_bytes_moved"], u) / HBM_PEAK_GBS}
+            if mode == "basp":   # both modes move the same bytes: one copy per workload
+                qkv_b, o_b = i["qkv_bytes_moved"] // 2, i["o_bytes_moved"] // 2
+                tc = statistics.median(time_launches(b, lambda j: b.basp_stream_copy(
+                    sets[j]["out"], sets[j]["x"], qkv_b), iters, R))
+                uc = statistics.median(time_launches(b, lambda j: b.basp_stream_copy(
+                    sets[j]["o_out"], sets[j]["x"], o_b), iters, R))
+                out[name]["copy"] = {"s2h_bytes_gbs": rate(2 * qkv_b, tc), "h2s_bytes_gbs": rate(2 * o_b, uc)}
             del sets
             torch.cuda.empty_cache()
     return out
@@ -442,7 +477,8 @@ def pmc_summary(fetch_dir, write_dir):
         # the fused seq->head kernel: tile_kernel<VW, VPT, POLICY, true> or
         # tile_kernel_staged<VPT, POLICY, true>
         fused = [r for r in timed if "tile_kernel" in r["Kernel_Name"] and "true>" in r["Kernel_Name"]]
-        copies = [r for r in rows[marks[1]:] if "copy" in r["Kernel_Name"].lower()]
+        copies = [r for r in rows[marks[1]:] if "copy" in r["Kernel_Name"].lower()
+                  and "stream_copy_kernel" not in r["Kernel_Name"]]
         if not fused or not copies:
             raise SystemExit("missing fused or copy dispatches for %s" % counter)
         # the calibration copy: the largest copy after the timed region (small
@@ -503,6 +539,12 @@ def main(argv=None):
                      "frac": r["s2h_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": r["s2h_bytes"], "avg_launch_us": r["s2h_avg_us"],
                      "timed_launches": r["timed_launches_per_kernel"]},
+        "copy_ceiling": {
+            "kernel": "basp_stream_copy (16-byte loads/stores, same cache policy, read once, written once)",
+            "s2h_bytes_gbs": r["copy_ceiling"][str(r["s2h_bytes"])]["gbs"],
+            "h2s_bytes_gbs": r["copy_ceiling"][str(r["h2s_bytes"])]["gbs"],
+            "s2h_frac_of_copy": r["s2h_gbs"] / r["copy_ceiling"][str(r["s2h_bytes"])]["gbs"],
+            "h2s_frac_of_copy": r["h2s_gbs"] / r["copy_ceiling"][str(r["h2s_bytes"])]["gbs"]},
         "head_to_seq": {"achieved": r["h2s_gbs"], "frac": r["h2s_gbs"] / HBM_PEAK_GBS,
                         "avg_launch_us": r["h2s_avg_us"], "bytes_per_launch": r["h2s_bytes"]},
         "round_trip_bit_exact": r["round_trip_bit_exact"],

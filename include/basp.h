@@ -136,8 +136,9 @@ typedef struct basp_plan_info {
  *   BASP_ERR_INDIVISIBLE  BASP with B <= N and N % B != 0 [review, Summary];
  *                         BASP with B > N and B % N != 0; S % P, Hq % P or
  *                         Hkv % P != 0 [review, Frequently asked questions]
- *   BASP_ERR_UNSUPPORTED  a buffer of more than 2^62 bytes, or more than
- *                         2^31 - 1 work tiles in one launch
+ *   BASP_ERR_UNSUPPORTED  a buffer of more than 2^62 bytes, a tensor of
+ *                         2^32 or more (token, head) rows (B*S*max(Hq, Hkv)),
+ *                         or more than 2^31 - 1 work tiles in one launch
  * basp_plan_create uses BASP_LAYOUT_HEAD_MAJOR.
  */
 basp_plan *basp_plan_create(int N, int B, int64_t S, int Hq, int Hkv, int d,
@@ -288,6 +289,23 @@ basp_status basp_plan_autotune(basp_plan *plan, const void *q, const void *k, co
  * or launches nothing) and is then cleared.  Returns BASP_OK.
  */
 basp_status basp_time_next_call(void *start_event, void *stop_event);
+
+/*
+ * Plain device copy of bytes bytes from src to dst, with the access rules of
+ * the re-layout kernels: 16-byte buffer loads and stores, non-temporal loads
+ * and non-temporal device-scope stores, one wave of 64 lanes per work-group.
+ * It is not part of the method.  It is the simplest kernel that reads every
+ * byte once and writes every byte once, so its rate at the same byte count
+ * is the ceiling a re-layout call is measured against.
+ *   src, dst  device pointers, 16-byte aligned, owned by the caller; they
+ *             may be NULL when bytes is 0
+ *   bytes     a multiple of 16, at most 2^56
+ * Asynchronous on stream, no allocation; basp_time_next_call applies to it.
+ * Errors: BASP_ERR_INVALID (NULL pointer with bytes > 0), BASP_ERR_ALIGN
+ * (pointer or size not a multiple of 16), BASP_ERR_ALIAS (the two ranges
+ * overlap), BASP_ERR_UNSUPPORTED (bytes above 2^56), BASP_ERR_HIP.
+ */
+basp_status basp_stream_copy(void *dst, const void *src, uint64_t bytes, void *stream);
 
 /* Status of the last call made by this thread, and a static description. */
 basp_status basp_last_error(void);

@@ -110,6 +110,8 @@ _lib.basp_plan_autotune.argtypes = [_plan_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.basp_plan_autotune.restype = _i32
 _lib.basp_time_next_call.argtypes = [_vp, _vp]
 _lib.basp_time_next_call.restype = _i32
+_lib.basp_stream_copy.argtypes = [_vp, _vp, ctypes.c_uint64, _vp]
+_lib.basp_stream_copy.restype = _i32
 _lib.basp_last_error.argtypes = []
 _lib.basp_last_error.restype = _i32
 _lib.basp_status_str.argtypes = [_i32]
@@ -310,3 +312,23 @@ def basp_seq_to_head_unfused(plan: Plan, q, k, v, out, ws, stream=None) -> None:
         plan.handle, _ptr(q, plan, i["q_elems"], "q"), _ptr(k, plan, i["kv_elems"], "k"),
         _ptr(v, plan, i["kv_elems"], "v"), _ptr(out, plan, i["qkv_elems"], "out"), ws,
         _stream(stream)), "basp_seq_to_head_unfused")
+
+
+def basp_stream_copy(dst, src, nbytes=None, stream=None) -> None:
+    """Plain device copy of nbytes bytes (default: all of src) with the
+    re-layout kernels' access rules; dst and src are device tensors or raw
+    addresses."""
+    def addr(x, name):
+        if isinstance(x, int) or x is None:
+            return x
+        if not x.is_cuda or not x.is_contiguous():
+            raise ValueError("%s must be a contiguous device tensor" % name)
+        return x.data_ptr()
+
+    if nbytes is None:
+        nbytes = src.numel() * src.element_size()
+    for x, name in ((dst, "dst"), (src, "src")):
+        if not isinstance(x, int) and x is not None and x.numel() * x.element_size() < nbytes:
+            raise ValueError("%s holds fewer than %d bytes" % (name, nbytes))
+    _check(_lib.basp_stream_copy(addr(dst, "dst"), addr(src, "src"), nbytes, _stream(stream)),
+           "basp_stream_copy")

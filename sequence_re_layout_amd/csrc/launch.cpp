@@ -92,7 +92,7 @@ int vector_width(const basp_plan &p, const uint64_t *addrs, int n)
 
 struct TileShape {
     uint32_t Ts, Th, ntb, nhb;
-    uint64_t ntiles;
+    uint64_t ntiles;   // tiles of one (member, batch index) plane
 };
 
 // Tile of one tensor with Hl heads per rank and A vectors per row: about one
@@ -112,34 +112,41 @@ TileShape tile_shape(const basp_plan &p, const Shape &sh, uint32_t Hl, uint32_t 
     s.Th = uint32_t(th);
     s.ntb = uint32_t((uint64_t(p.St) + ts - 1) / ts);
     s.nhb = uint32_t((Hl + th - 1) / th);
-    s.ntiles = uint64_t(p.G) * p.P * p.Bl * s.nhb * p.P * s.ntb;
+    s.ntiles = uint64_t(s.nhb) * p.P * s.ntb;
     return s;
 }
 
 struct Strides {
-    uint64_t seq_rank, seq_bl, seq_tok;
-    uint64_t head_rank, head_bl, head_tok, head_head;
+    uint64_t seq_tok, head_tok, head_head;
 };
 
-// Byte strides of both layouts for a tensor of H heads (basp.h, "Memory layouts").
+// Byte strides inside a tile, for a tensor of H heads (basp.h, "Memory layouts").
 Strides strides(const basp_plan &p, uint32_t H)
 {
-    const uint64_t row = p.row_bytes, Hl = H / p.P, S = p.S, St = p.St, Bl = p.Bl;
+    const uint64_t row = p.row_bytes, Hl = H / p.P, S = p.S;
     Strides s;
     s.seq_tok = H * row;
-    s.seq_bl = St * s.seq_tok;
-    s.seq_rank = Bl * s.seq_bl;
     if (p.layout == BASP_LAYOUT_HEAD_MAJOR) {
         s.head_tok = row;
         s.head_head = S * row;
-        s.head_bl = Hl * S * row;
     } else {
         s.head_head = row;
         s.head_tok = Hl * row;
-        s.head_bl = S * Hl * row;
     }
-    s.head_rank = Bl * s.head_bl;
     return s;
+}
+
+constexpr uint32_t kGridYZ = 65535;   // work-groups along y and along z at most
+
+// What the tile launch grid and tile_origin assume of a plan: every tensor
+// holds fewer than 2^32 rows (tile bases are 32-bit row indices, and S fits
+// 32 bits), P and B fit the grid's y and z extents, and one of G, Bl, P is 1
+// (true of Ulysses, BASP and the data-parallel fallback).
+bool grid_fits(const basp_plan &p)
+{
+    const uint64_t H = uint64_t(std::max(p.Hq, p.Hkv));
+    return uint64_t(p.S) <= 0xffffffffull / (uint64_t(p.B) * H) && uint32_t(p.P) <= kGridYZ &&
+           uint32_t(p.B) <= kGridYZ && (p.G == 1 || p.Bl == 1 || p.P == 1);
 }
 
 // Every offset a lane computes inside a tile stays below kI31Max.
@@ -175,6 +182,8 @@ struct SegSpec {
 int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, TileLaunch &L)
 {
     std::memset(&L, 0, sizeof(L));
+    if (!grid_fits(p))
+        return BASP_ERR_UNSUPPORTED;
     uint64_t addrs[6];
     for (int i = 0; i < nseg; ++i) {
         addrs[2 * i] = segs[i].seq;
@@ -186,6 +195,8 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
         for_vector_width(resolve(p, p.tuning[s2h ? BASP_SEQ_TO_HEAD : BASP_HEAD_TO_SEQ], s2h), vw, A);
     TileDesc &D = L.D;
     D.St = uint32_t(p.St);
+    D.S = uint32_t(p.S);
+    D.token_major = p.layout == BASP_LAYOUT_TOKEN_MAJOR;
     D.row = uint32_t(p.row_bytes);
     D.s_fast = sh.s_fast;
     // staged loads run along the source's contiguous axis, stores along the
@@ -196,7 +207,8 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
     D.store_s_fast = s2h ? head_major : 0;
     D.heads_first = sh.heads_first;
     D.P = make_fastdiv(p.P);
-    D.Bl = make_fastdiv(p.Bl);
+    D.Bl = uint32_t(p.Bl);
+    D.bmul = p.Bl == 1 ? uint32_t(p.P) : 1u;
     D.A = make_fastdiv(A);
     uint64_t total = 0;
     for (int i = 0; i < 3; ++i) {
@@ -215,28 +227,24 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
         sg.head = segs[i].head;
         sg.seq_bytes = uint64_t(p.B) * p.S * H * p.row_bytes;
         sg.head_bytes = sg.seq_bytes;
-        sg.seq_rank = st.seq_rank;
-        sg.seq_bl = st.seq_bl;
-        sg.head_rank = st.head_rank;
-        sg.head_bl = st.head_bl;
-        sg.head_head = st.head_head;
         sg.seq_tok = uint32_t(st.seq_tok);
         sg.head_tok = uint32_t(st.head_tok);
         sg.head_head_lane = ts.Th == 1 ? 0u : uint32_t(st.head_head);
         sg.Hl = Hl;
         sg.Ts = make_fastdiv(ts.Ts);
         sg.Th = make_fastdiv(ts.Th);
-        sg.ntb = make_fastdiv(ts.ntb);
-        sg.nhb = make_fastdiv(ts.nhb);
+        sg.fast = make_fastdiv(sh.heads_first ? ts.nhb : ts.ntb);
         sg.tile_begin = uint32_t(total);
         total += ts.ntiles;
         if (total > kI31Max)
             return BASP_ERR_UNSUPPORTED;
         sg.tile_end = uint32_t(total);
     }
-    D.ntiles = uint32_t(total);
+    D.plane = uint32_t(total);
     D.xcd_span = sh.xcd ? uint32_t(total / kXcds) : 0;
     L.grid = uint32_t(std::min<uint64_t>(total, sh.grid_cap));
+    L.grid_y = uint32_t(p.P);
+    L.grid_z = uint32_t(p.B);
     L.vw = vw;
     L.vpt = sh.vpt;
     L.block = sh.block;
@@ -326,7 +334,7 @@ int build_perm(const basp_plan &p, const PermSpec *ps, int n, int vw, PermLaunch
 basp_status check_launch_limits(const basp_plan &p, const basp_tuning &t, bool s2h)
 {
     if (p.St > int64_t(kI31Max) || p.row_bytes > int64_t(kI31Max) ||
-        int64_t(p.Hq) * p.row_bytes > int64_t(kI31Max))
+        int64_t(p.Hq) * p.row_bytes > int64_t(kI31Max) || !grid_fits(p))
         return BASP_ERR_UNSUPPORTED;
     const Shape resolved = resolve(p, t, s2h);
     const uint32_t heads[3] = {uint32_t(p.Hq), uint32_t(p.Hkv), uint32_t(p.Hkv)};

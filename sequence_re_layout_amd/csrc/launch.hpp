@@ -15,14 +15,22 @@
 //     head-major        h*S*row + t*row
 //     token-major       t*Hl*row + h*row
 // so a work-group computes the tile's two base addresses once and each lane
-// only adds 32-bit offsets.  Tiles are numbered either (g, jh, bl, hb, js, tb),
-// token block tb fastest, the order of the head-sharded layout, or
-// (g, js, bl, tb, jh, hb), head block hb fastest, the order of the
-// sequence-sharded layout: neighbouring tiles, which run at the same time,
-// then share the DRAM pages of one side.  Optionally each of the 8 XCDs takes
-// one contiguous eighth of that order (xcd_tile).  The staged variant passes
-// each tile through LDS in one pass: loads in the source's contiguous order,
-// stores in the destination's (tile_vector with an explicit lane order).
+// only adds 32-bit offsets.
+//
+// Launch grid.  blockIdx.z is the batch index b, blockIdx.y one group member
+// and blockIdx.x a tile of the (y, z) plane, Q, K and V planes one after the
+// other.  Two tile orders:
+//   token blocks fastest (the head-sharded layout's order): y = jh and x runs
+//     over (hb, js, tb), so neighbouring tiles continue one destination head
+//     across source members;
+//   head blocks fastest (the sequence-sharded layout's order): y = js and x
+//     runs over (tb, jh, hb), so neighbouring tiles continue one source token
+//     across destination members.
+// Neighbouring tiles run at the same time and share the DRAM pages of one
+// side.  Optionally each XCD takes one contiguous eighth of a plane
+// (xcd_tile).  The staged variant passes each tile through LDS in one pass:
+// loads in the source's contiguous order, stores in the destination's
+// (tile_vector with an explicit lane order).
 //
 // Perm kernel (unfused baseline).  Writes its destination linearly; row i of
 // the destination has digits (d0..d4), d4 fastest, and is read from source
@@ -48,35 +56,36 @@ constexpr uint32_t kOutside = 0x80000000u;
 struct TileSeg {
     uint64_t seq, head;            // buffer addresses
     uint64_t seq_bytes, head_bytes;
-    uint64_t seq_rank, seq_bl;     // byte strides of a rank and a local sequence
-    uint64_t head_rank, head_bl;
-    uint64_t head_head;            // byte stride of a head, head-sharded
     uint32_t seq_tok;              // byte stride of a token, sequence-sharded
     uint32_t head_tok;             // byte stride of a token, head-sharded
     uint32_t head_head_lane;       // head stride inside a tile (0 when Th == 1)
     uint32_t Hl;                   // heads per rank
     FastDiv Ts, Th;                // tile extent in tokens and heads
-    FastDiv ntb;                   // token blocks per member chunk
-    FastDiv nhb;                   // head blocks per rank
-    uint32_t tile_begin, tile_end;
+    FastDiv fast;                  // blocks along the fast axis: token blocks per
+                                   // member chunk, or head blocks per rank
+    uint32_t tile_begin, tile_end; // this tensor's tiles in the plane
 };
 
 struct TileDesc {
     TileSeg seg[3];
-    uint32_t ntiles;
+    uint32_t plane;                // tiles per (y, z) plane
     uint32_t St;
+    uint32_t S;
+    uint32_t token_major;          // head-sharded side is [Bl][S][Hl][d] (else [Bl][Hl][S][d])
     uint32_t row;                  // bytes per (token, head) row
     uint32_t s_fast;               // lanes along tokens (1) or heads (0)
     uint32_t load_s_fast;          // staged kernel: lane order of the loads
     uint32_t store_s_fast;         //   and of the stores
     uint32_t heads_first;          // tile order: head block fastest (1) or token block (0)
     uint32_t xcd_span;             // tiles per XCD when remapped, else 0
-    FastDiv P, Bl, A;              // group size, sequences per group, vectors per row
+    uint32_t Bl;                   // sequences per group
+    uint32_t bmul;                 // P when Bl == 1, else 1 (see tile_origin)
+    FastDiv P, A;                  // group size, vectors per row
 };
 
-// Work-groups are dispatched round-robin over the 8 XCDs (work-group i runs
-// on XCD i % 8).  With xcd_span = n/8 > 0 the i-th tile in launch order is
-// renumbered so that each XCD walks one contiguous eighth of the first
+// Work-groups are dispatched round-robin over the 8 XCDs.  With
+// xcd_span = plane/8 > 0 the i-th tile of a plane is renumbered so that
+// consecutive work-groups of one XCD walk one contiguous eighth of the first
 // 8*xcd_span tiles; the remaining tiles keep their number.  A bijection.
 constexpr uint32_t kXcds = 8;
 
@@ -92,47 +101,46 @@ struct TileOrigin {
     uint32_t ns, nh;               // tokens and heads present (ragged tail)
 };
 
-BASP_HD inline TileOrigin tile_origin(const TileDesc &D, uint32_t x)
+// Tile x of the plane of group member y and batch index b.
+BASP_HD inline TileOrigin tile_origin(const TileDesc &D, uint32_t x, uint32_t y, uint32_t b)
 {
     const uint32_t tile = xcd_tile(x, D.xcd_span);
     TileOrigin o;
-    o.seg = (tile >= D.seg[0].tile_end) + (tile >= D.seg[1].tile_end);
+    o.seg = tile < D.seg[0].tile_end ? 0u : (tile < D.seg[1].tile_end ? 1u : 2u);
     const TileSeg &sg = D.seg[o.seg];
     const uint32_t P = D.P.d;
     const uint32_t local = tile - sg.tile_begin;
-    uint32_t tb, js, hb, bl, g, jh;
-    if (D.heads_first) {   // (g, js, bl, tb, jh, hb)
-        const uint32_t q1 = fastdiv(local, sg.nhb);
-        hb = local - q1 * sg.nhb.d;
-        const uint32_t q2 = fastdiv(q1, D.P);
-        jh = q1 - q2 * P;
-        const uint32_t q3 = fastdiv(q2, sg.ntb);
-        tb = q2 - q3 * sg.ntb.d;
-        const uint32_t q4 = fastdiv(q3, D.Bl);
-        bl = q3 - q4 * D.Bl.d;
-        g = fastdiv(q4, D.P);
-        js = q4 - g * P;
-    } else {               // (g, jh, bl, hb, js, tb)
-        const uint32_t q1 = fastdiv(local, sg.ntb);
-        tb = local - q1 * sg.ntb.d;
-        const uint32_t q2 = fastdiv(q1, D.P);
-        js = q1 - q2 * P;
-        const uint32_t q3 = fastdiv(q2, sg.nhb);
-        hb = q2 - q3 * sg.nhb.d;
-        const uint32_t q4 = fastdiv(q3, D.Bl);
-        bl = q3 - q4 * D.Bl.d;
-        g = fastdiv(q4, D.P);
-        jh = q4 - g * P;
+    const uint32_t q = fastdiv(local, sg.fast), f = local - q * sg.fast.d;
+    const uint32_t slow = fastdiv(q, D.P), m = q - slow * P;
+    uint32_t tb, hb, js, jh;
+    if (D.heads_first) {   // x = (tb, jh, hb), y = js
+        hb = f;
+        jh = m;
+        tb = slow;
+        js = y;
+    } else {               // x = (hb, js, tb), y = jh
+        tb = f;
+        js = m;
+        hb = slow;
+        jh = y;
     }
-    const uint32_t Ts = sg.Ts.d, Th = sg.Th.d;
+    const uint32_t Ts = sg.Ts.d, Th = sg.Th.d, Hl = sg.Hl;
     const uint32_t t0 = tb * Ts, hl0 = hb * Th;
     o.ns = D.St - t0 < Ts ? D.St - t0 : Ts;
-    o.nh = sg.Hl - hl0 < Th ? sg.Hl - hl0 : Th;
-    const uint64_t rs = uint64_t(g) * P + js, rh = uint64_t(g) * P + jh;
-    o.seq_off = rs * sg.seq_rank + bl * sg.seq_bl + uint64_t(t0) * sg.seq_tok +
-                (uint64_t(jh) * sg.Hl + hl0) * D.row;
-    o.head_off = rh * sg.head_rank + bl * sg.head_bl + (uint64_t(js) * D.St + t0) * sg.head_tok +
-                 uint64_t(hl0) * sg.head_head;
+    o.nh = Hl - hl0 < Th ? Hl - hl0 : Th;
+    // Row indices of the tile base in 32 bits (a tensor holds fewer than 2^32
+    // rows; the host checks), then one widening multiply by the row size.
+    // Rank r = g*P + j holds local sequence bl of batch index b = g*Bl + bl.
+    // In every plan G, Bl or P is 1, so r*Bl + bl = b*bmul + j*Bl.
+    // Sequence-sharded: ((r*Bl + bl)*St + t)*H + h with j = js and
+    // h = jh*Hl + hl; head-sharded: ((r*Bl + bl)*Hl + hl)*S + s, or
+    // ((r*Bl + bl)*S + s)*Hl + hl, with j = jh and s = js*St + t.
+    const uint32_t pre_s = b * D.bmul + js * D.Bl, pre_h = b * D.bmul + jh * D.Bl;
+    const uint32_t seq_row = (pre_s * D.St + t0) * (P * Hl) + jh * Hl + hl0;
+    const uint32_t s0 = js * D.St + t0;
+    const uint32_t head_row = D.token_major ? (pre_h * D.S + s0) * Hl + hl0 : (pre_h * Hl + hl0) * D.S + s0;
+    o.seq_off = uint64_t(seq_row) * D.row;
+    o.head_off = uint64_t(head_row) * D.row;
     return o;
 }
 
@@ -210,7 +218,8 @@ struct TileLaunch {
     int block;                // threads per work-group: 64, 128 or 256
     bool s2h;                 // read sequence-sharded, write head-sharded
     bool staged;              // tiles pass through LDS (one pass per tile)
-    uint32_t grid;            // 0: nothing to launch
+    uint32_t grid;            // work-groups along x (tiles loop beyond it); 0: nothing to launch
+    uint32_t grid_y, grid_z;  // P group members, B batch indices
 };
 
 struct PermLaunch {

@@ -91,8 +91,8 @@ template <int BS, int VW, int VPT, int POL, bool S2H>
 __global__ __launch_bounds__(BS) void tile_kernel(const TileDesc D)
 {
     using V = typename Vec<VW>::type;
-    for (uint32_t tile = blockIdx.x; tile < D.ntiles; tile += gridDim.x) {
-        const TileOrigin o = tile_origin(D, tile);
+    for (uint32_t tile = blockIdx.x; tile < D.plane; tile += gridDim.x) {
+        const TileOrigin o = tile_origin(D, tile, blockIdx.y, blockIdx.z);
         const TileSeg &sg = D.seg[o.seg];
         const __amdgpu_buffer_rsrc_t rseq = make_rsrc(sg.seq + o.seq_off, rest(sg.seq_bytes, o.seq_off));
         const __amdgpu_buffer_rsrc_t rhead =
@@ -127,8 +127,8 @@ __global__ __launch_bounds__(BS) void tile_kernel_staged(const TileDesc D)
 {
     using V = typename Vec<16>::type;
     __shared__ V stage[BS * VPT];
-    for (uint32_t tile = blockIdx.x; tile < D.ntiles; tile += gridDim.x) {
-        const TileOrigin o = tile_origin(D, tile);
+    for (uint32_t tile = blockIdx.x; tile < D.plane; tile += gridDim.x) {
+        const TileOrigin o = tile_origin(D, tile, blockIdx.y, blockIdx.z);
         const TileSeg &sg = D.seg[o.seg];
         const __amdgpu_buffer_rsrc_t rseq = make_rsrc(sg.seq + o.seq_off, rest(sg.seq_bytes, o.seq_off));
         const __amdgpu_buffer_rsrc_t rhead =
@@ -191,6 +191,31 @@ __global__ __launch_bounds__(kBlock) void perm_kernel(const PermDesc D)
 #pragma unroll
         for (int k = 0; k < kPermVpt; ++k)
             vstore<VW, kNT>(rd, dst[k], buf[k]);
+    }
+}
+
+// Plain copy with the same access rules, the ceiling the re-layout kernels
+// are measured against: chunk c is bytes [c*kCopyWg, (c+1)*kCopyWg), one
+// 16-byte vector per lane, read and written through descriptors that cover
+// only the rest of each buffer, so lanes past the end read zeros and drop
+// the store.  Work-groups loop over chunks beyond the grid cap.
+constexpr int kCopyBlock = 64;
+constexpr uint32_t kCopyWg = kCopyBlock * 16;
+constexpr uint32_t kCopyGridCap = 1u << 22;
+
+struct CopyDesc {
+    uint64_t src, dst, bytes, chunks;
+};
+
+__global__ __launch_bounds__(kCopyBlock) void stream_copy_kernel(const CopyDesc D)
+{
+    for (uint64_t c = blockIdx.x; c < D.chunks; c += gridDim.x) {
+        const uint64_t base = c * kCopyWg;   // < D.bytes
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(D.src + base, D.bytes - base);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(D.dst + base, D.bytes - base);
+        const uint32_t off = threadIdx.x * 16;
+        const u32x4 x = vload<16, Policy<4>::load>(rs, off);
+        vstore<16, Policy<4>::store>(rd, off, x);
     }
 }
 
@@ -272,17 +297,17 @@ thread_local Timing t_timing;
 // code in the process may have left set).  first/last: this launch opens or
 // closes the current entry-point call, for the timing events.
 template <typename Desc>
-basp_status launch_kernel(const void *fn, uint32_t grid, int block, const Desc &D, void *stream,
+basp_status launch_kernel(const void *fn, dim3 grid, int block, const Desc &D, void *stream,
                           bool first, bool last)
 {
     void *args[] = {const_cast<Desc *>(&D)};
     const hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (t_timing.start || t_timing.stop)
-        e = hipExtLaunchKernel(fn, dim3(grid), dim3(block), args, 0, st,
+        e = hipExtLaunchKernel(fn, grid, dim3(block), args, 0, st,
                                first ? t_timing.start : nullptr, last ? t_timing.stop : nullptr, 0);
     else
-        e = hipLaunchKernel(fn, dim3(grid), dim3(block), args, 0, st);
+        e = hipLaunchKernel(fn, grid, dim3(block), args, 0, st);
     return e == hipSuccess ? BASP_OK : BASP_ERR_HIP;
 }
 
@@ -290,7 +315,8 @@ basp_status launch(const TileLaunch &L, void *stream)
 {
     if (L.grid == 0)
         return BASP_OK;
-    return launch_kernel(reinterpret_cast<const void *>(tile_fn(L)), L.grid, L.block, L.D, stream,
+    return launch_kernel(reinterpret_cast<const void *>(tile_fn(L)), dim3(L.grid, L.grid_y, L.grid_z),
+                         L.block, L.D, stream,
                          true, true);
 }
 
@@ -305,7 +331,7 @@ basp_status launch(const PermLaunch &L, void *stream, bool first, bool last)
     case 4: fn = reinterpret_cast<const void *>(perm_kernel<4>); break;
     default: fn = reinterpret_cast<const void *>(perm_kernel<2>); break;
     }
-    return launch_kernel(fn, L.grid, kBlock, L.D, stream, first, last);
+    return launch_kernel(fn, dim3(L.grid), kBlock, L.D, stream, first, last);
 }
 
 // Runs f, the body of an entry point, and clears the timing request after it.
@@ -549,6 +575,28 @@ extern "C" basp_status basp_head_to_seq_qkv(const basp_plan *p, const void *in, 
         basp::TileLaunch L;
         const int s = basp::prepare_head_to_seq_qkv(*p, in, dq, dk, dv, L);
         return s != BASP_OK ? basp_status(s) : basp::launch(L, stream);
+    });
+}
+
+extern "C" basp_status basp_stream_copy(void *dst, const void *src, uint64_t bytes, void *stream)
+{
+    return basp::timed_call([&]() -> basp_status {
+        if (bytes == 0)
+            return BASP_OK;
+        if (!dst || !src)
+            return BASP_ERR_INVALID;
+        const uint64_t d = reinterpret_cast<uint64_t>(dst), s = reinterpret_cast<uint64_t>(src);
+        if ((d | s | bytes) % 16 != 0)
+            return BASP_ERR_ALIGN;
+        if (bytes > (uint64_t(1) << 56))
+            return BASP_ERR_UNSUPPORTED;
+        if (d < s + bytes && s < d + bytes)
+            return BASP_ERR_ALIAS;
+        const uint64_t chunks = (bytes + basp::kCopyWg - 1) / basp::kCopyWg;
+        const basp::CopyDesc D = {s, d, bytes, chunks};
+        const uint32_t grid = static_cast<uint32_t>(std::min<uint64_t>(chunks, basp::kCopyGridCap));
+        return basp::launch_kernel(reinterpret_cast<const void *>(basp::stream_copy_kernel), dim3(grid),
+                                   basp::kCopyBlock, D, stream, true, true);
     });
 }
 

@@ -32,9 +32,14 @@ void run(const TileLaunch &L, uint64_t *bad)
 {
     const TileDesc &D = L.D;
     std::vector<unsigned char> lds(size_t(L.block) * L.vpt * 16);
-    for (uint32_t block = 0; block < L.grid; ++block) {
-        for (uint32_t tile = block; tile < D.ntiles; tile += L.grid) {
-            const TileOrigin o = tile_origin(D, tile);
+    // the launch grid: x work-groups looping over a plane's tiles, y group
+    // members, z batch indices
+    const uint64_t groups = uint64_t(L.grid) * L.grid_y * L.grid_z;
+    for (uint64_t w = 0; w < groups; ++w) {
+        const uint32_t block = uint32_t(w % L.grid), by = uint32_t(w / L.grid % L.grid_y);
+        const uint32_t bz = uint32_t(w / L.grid / L.grid_y);
+        for (uint32_t tile = block; tile < D.plane; tile += L.grid) {
+            const TileOrigin o = tile_origin(D, tile, by, bz);
             const TileSeg &sg = D.seg[o.seg];
             const uint64_t seq = sg.seq + o.seq_off, head = sg.head + o.head_off;
             const uint64_t nseq = range(rest(sg.seq_bytes, o.seq_off));

@@ -144,7 +144,7 @@ def test_tuning_validation():
             b.basp_plan_set_tuning(p, **bad)
         assert e.value.status == b.BASP_ERR_INVALID
     # a 1-token x 1-head tile over a huge sequence exceeds the tile index range
-    big = b.basp_plan_create(1, 1, 1 << 30, 8, 8, 8, b.BASP_BF16, b.BASP_MODE_ULYSSES)
+    big = b.basp_plan_create(1, 1, 1 << 28, 8, 8, 8, b.BASP_BF16, b.BASP_MODE_ULYSSES)
     with pytest.raises(b.BaspError) as e:
         b.basp_plan_set_tuning(big, tile_tokens=1, tile_heads=1)
     assert e.value.status == b.BASP_ERR_UNSUPPORTED
@@ -175,3 +175,38 @@ def test_pointer_checks_before_launch():
     e = b.basp_plan_create(4, 2, 0, 8, 8, 64)
     assert lib.basp_seq_to_head(e.handle, None, None, None, None, None) == b.BASP_OK
     assert lib.basp_head_to_seq(e.handle, None, None, None) == b.BASP_OK
+
+
+def test_stream_copy_checks_before_launch():
+    """The copy rejects NULL, misaligned, overlapping and oversized arguments
+    before any device call; zero bytes is a no-op."""
+    lib = b.library()
+    base = 1 << 40  # fake addresses: never dereferenced
+    n = 1 << 20
+    assert lib.basp_stream_copy(None, None, 0, None) == b.BASP_OK
+    assert lib.basp_stream_copy(None, base, n, None) == b.BASP_ERR_INVALID
+    assert lib.basp_stream_copy(base + n, None, n, None) == b.BASP_ERR_INVALID
+    assert lib.basp_stream_copy(base + n, base + 8, n, None) == b.BASP_ERR_ALIGN
+    assert lib.basp_stream_copy(base + n + 4, base, n, None) == b.BASP_ERR_ALIGN
+    assert lib.basp_stream_copy(base + n, base, n + 2, None) == b.BASP_ERR_ALIGN
+    assert lib.basp_stream_copy(base + n - 16, base, n, None) == b.BASP_ERR_ALIAS
+    assert lib.basp_stream_copy(base, base + n - 16, n, None) == b.BASP_ERR_ALIAS
+    assert lib.basp_stream_copy(base, base, n, None) == b.BASP_ERR_ALIAS
+    assert lib.basp_stream_copy(base, base + (1 << 58), (1 << 56) + 16, None) == b.BASP_ERR_UNSUPPORTED
+    assert b.basp_last_error() == b.BASP_ERR_UNSUPPORTED
+
+
+def test_row_count_limit():
+    """Tile bases are 32-bit row indices: a tensor of 2^32 or more rows
+    (B*S*max(Hq, Hkv)) is rejected at plan creation, 2^32 - 8 is not."""
+    ok = b.basp_plan_create(1, 1, (1 << 29) - 1, 8, 8, 8, b.BASP_BF16, b.BASP_MODE_ULYSSES)
+    assert ok.info["q_elems"] == ((1 << 32) - 8) * 8
+    with pytest.raises(b.BaspError) as e:
+        b.basp_plan_create(1, 1, 1 << 29, 8, 8, 8, b.BASP_BF16, b.BASP_MODE_ULYSSES)
+    assert e.value.status == b.BASP_ERR_UNSUPPORTED
+    with pytest.raises(b.BaspError) as e:
+        b.basp_plan_create(4, 1, 1 << 30, 4, 4, 8, b.BASP_BF16, b.BASP_MODE_ULYSSES)   # 2^32 rows
+    assert e.value.status == b.BASP_ERR_UNSUPPORTED
+    with pytest.raises(b.BaspError) as e:
+        b.basp_plan_create(2, 2, 1 << 29, 4, 8, 8, b.BASP_BF16, b.BASP_MODE_BASP)   # Hkv > Hq
+    assert e.value.status == b.BASP_ERR_UNSUPPORTED

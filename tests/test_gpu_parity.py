@@ -483,3 +483,94 @@ def test_side_stream():
     b.basp_seq_to_head(plan, q, k, v, out2, stream=side.cuda_stream)
     side.synchronize()
     assert np.array_equal(bits(out2), want)
+
+
+@pytest.mark.parametrize("shape", [workloads.LLAMA_1B[1:], (6, 3, 6 * 37, 12, 6, 40)],
+                         ids=["llama1b", "ragged"])
+def test_graph_capture_replays(shape):
+    """Every entry point launches only kernels on its stream (no allocation,
+    no memset, no synchronisation), so a whole step captures into a HIP
+    graph.  Each replay runs on fresh inputs copied into the captured
+    buffers, with eager work and synchronisation between replays, and is
+    checked against the oracle."""
+    needs_gpu()
+    N, B, S, Hq, Hkv, d = shape
+    plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, 1)
+    i = plan.info
+    nq, nkv, nqkv = i["q_elems"], i["kv_elems"], i["qkv_elems"]
+    dev = lambda n: torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    q, k, v, o, do, g = dev(nq), dev(nkv), dev(nkv), dev(nq), dev(nq), dev(nqkv)
+    qkv, qkv_u, o_seq, do_head = dev(nqkv), dev(nqkv), dev(nq), dev(nq)
+    dq, dk, dv = dev(nq), dev(nkv), dev(nkv)
+    ws = torch.empty(b.basp_unfused_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        b.basp_seq_to_head(plan, q, k, v, qkv)
+        b.basp_head_to_seq(plan, o, o_seq)
+        b.basp_seq_to_head_o(plan, do, do_head)
+        b.basp_head_to_seq_qkv(plan, g, dq, dk, dv)
+        b.basp_seq_to_head_unfused(plan, q, k, v, qkv_u, ws)
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        seeds = [100 + 10 * rep + j for j in range(6)]
+        host = [inputs.normal_bf16(n, s) for n, s in zip((nq, nkv, nkv, nq, nq, nqkv), seeds)]
+        for dst, src in zip((q, k, v, o, do, g), host):
+            dst.copy_(src)
+        for t in (qkv, qkv_u, o_seq, do_head, dq, dk, dv):
+            t.fill_(float("nan"))
+        scratch = dev(nq)
+        b.basp_head_to_seq(plan, o, scratch)          # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        hq, hk, hv, ho, hdo, hg = (inputs.raw_bits(x) for x in host)
+        want = oracle.seq_to_head_qkv(hq, hk, hv, 1, N, B, S, Hq, Hkv, d)
+        assert np.array_equal(bits(qkv), want), "replay %d: fused seq->head" % rep
+        assert np.array_equal(bits(qkv_u), want), "replay %d: unfused seq->head" % rep
+        want_o = oracle.head_to_seq(ho, 1, N, B, S, Hq, d)
+        assert np.array_equal(bits(o_seq), want_o), "replay %d: head->seq" % rep
+        assert np.array_equal(bits(scratch), want_o), "replay %d: eager head->seq" % rep
+        assert np.array_equal(bits(do_head), oracle.seq_to_head(hdo, 1, N, B, S, Hq, d)), \
+            "replay %d: dO seq->head" % rep
+        wq, wk, wv = oracle.head_to_seq_qkv(hg, 1, N, B, S, Hq, Hkv, d)
+        assert np.array_equal(bits(dq), wq) and np.array_equal(bits(dk), wk) and \
+            np.array_equal(bits(dv), wv), "replay %d: fused dQ/dK/dV head->seq" % rep
+    del graph
+
+
+@pytest.mark.parametrize("nbytes", [16, 1008, 1024, 1040, (3 << 20) + 112, (4 << 30) + 1040],
+                         ids=["16B", "1008B", "1KiB", "1040B", "3MiB+112", "4GiB+1040"])
+def test_stream_copy(nbytes):
+    """The copy the re-layout is measured against: every byte copied, nothing
+    outside the destination written.  4 GiB + 1040 bytes takes offsets past
+    32 bits and more chunks than the grid, so work-groups loop."""
+    needs_gpu()
+    gen = torch.Generator(device="cuda").manual_seed(nbytes % 1000003)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=gen)
+    whole = torch.full((nbytes + 2 * GUARD,), 0x5A, dtype=torch.uint8, device="cuda")
+    dst = whole[GUARD:GUARD + nbytes]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()   # torch creates an event's handle when it is first recorded
+    stop.record()
+    torch.cuda.synchronize()
+    b.basp_time_next_call(start, stop)
+    b.basp_stream_copy(dst, src)
+    torch.cuda.synchronize()
+    assert start.elapsed_time(stop) > 0
+    assert torch.equal(dst, src)
+    assert bool((whole[:GUARD] == 0x5A).all()) and bool((whole[GUARD + nbytes:] == 0x5A).all())
+    del src, whole, dst
+    torch.cuda.empty_cache()
+
+
+def test_stream_copy_errors_on_device():
+    needs_gpu()
+    x = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    with pytest.raises(b.BaspError):
+        b.basp_stream_copy(x[16:], x, 1024)           # overlapping ranges
+    with pytest.raises(b.BaspError):
+        b.basp_stream_copy(x[2048:], x[1:], 1024)     # misaligned source
+    b.basp_stream_copy(x[2048:], x, 0)                # zero bytes: nothing to do
