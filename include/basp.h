@@ -209,25 +209,31 @@ basp_status basp_seq_to_head_unfused(const basp_plan *plan, const void *q, const
  * basp_seq_to_head and basp_seq_to_head_o, BASP_HEAD_TO_SEQ to
  * basp_head_to_seq and basp_head_to_seq_qkv (the unfused baseline has a
  * fixed shape).  Zero fields keep the built-in choice, which depends on the
- * direction and on the row size d*elem_size (measured on MI355X over the
- * Llama/Qwen attention shapes).  Results never depend on these values, only
- * the speed does.
- *   vectors_per_thread   1, 2, 4 or 8 (16-byte vectors held in flight per lane)
- *   tile_tokens          tokens per work tile (>= 1)
- *   tile_heads           heads per work tile (>= 1, clamped to H/P)
+ * row size d*elem_size (measured on MI355X over the Llama/Qwen attention
+ * shapes).  Results never depend on these values, only the speed does.
+ *   vectors_per_thread   1, 2, 4 or 8 (16-byte vectors held in flight per
+ *                        lane; built-in 1)
+ *   tile_tokens          tokens per work tile (>= 1; built-in: one pass of
+ *                        the work-group)
+ *   tile_heads           heads per work tile (>= 1, clamped to H/P; built-in
+ *                        8 for rows of at most 128 bytes, else 1)
  *   cache_policy         1 = plain loads and stores, 2 = non-temporal stores,
  *                        3 = non-temporal loads and stores, 4 = non-temporal
  *                        loads, non-temporal device-scope stores (gfx950
  *                        NT + SC1; built-in), 5 = non-temporal system-scope
  *                        loads and stores (NT + SC0 + SC1)
- *   max_grid             cap on work-groups per launch (tiles loop beyond it)
- *   lane_order           1 = lanes run along tokens first, 2 = along heads first
- *   xcd_remap            1 = tiles in work-group order, 2 = each of the 8 XCDs
- *                        takes one contiguous eighth of the tiles
+ *   max_grid             cap on work-groups along x, the tiles of one
+ *                        (group member, batch index) pair (tiles loop beyond it)
+ *   lane_order           1 = lanes run along tokens first, 2 = along heads
+ *                        first (built-in)
+ *   xcd_remap            1 = tiles in work-group order (built-in), 2 = each of
+ *                        the 8 XCDs takes one contiguous eighth of the tiles
+ *                        of a (group member, batch index) pair
  *   tile_order           1 = token blocks fastest (the head-sharded side's
  *                        order), 2 = head blocks fastest (the sequence-sharded
- *                        side's order)
- *   stage                1 = rows go straight from load to store registers,
+ *                        side's order; built-in)
+ *   stage                1 = rows go straight from load to store registers
+ *                        (built-in),
  *                        2 = each tile passes through LDS: loads
  *                        run along the source's contiguous axis, stores along
  *                        the destination's (used with 16-byte vectors and

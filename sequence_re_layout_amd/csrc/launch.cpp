@@ -17,17 +17,13 @@ constexpr uint32_t kGridCap = 1u << 22;  // work-groups per launch at most
 
 // Launch shape of one tile launch: the plan's tuning where set, else the
 // defaults below, chosen on MI355X over every named workload of at least
-// 256 MiB (Llama/Qwen shapes, 128- and 256-byte rows, both modes, rotating
-// buffers) as the launch shape whose worst ratio to each workload's best was
-// highest (0.94 to 0.98).  All are direct (no LDS staging), with 256 threads
-// per work-group, non-temporal loads and non-temporal device-scope stores.
-//   seq->head: token blocks fastest, XCD-contiguous, lanes along heads;
-//              4 heads per tile and 2 vectors per lane for 128-byte rows,
-//              1 head and 1 vector for longer rows
-//   head->seq: head blocks fastest, work-group order, 8 heads per tile,
-//              2 vectors per lane; lanes along heads for 128-byte rows,
-//              along tokens for longer rows
-// basp_plan_autotune replaces these by measurement.
+// 256 MiB (Llama/Qwen shapes, 128- and 256-byte rows, both modes, both
+// directions, rotating buffers) as the launch shape whose worst ratio to
+// each workload's best was highest (0.95; 0.98 on average): direct (no LDS
+// staging), 256 threads per work-group, one vector per lane, head blocks
+// fastest in work-group order, lanes along heads, non-temporal loads and
+// non-temporal device-scope stores; 8 heads per tile for 128-byte rows, one
+// head for longer rows.  basp_plan_autotune replaces these by measurement.
 struct Shape {
     int vpt, policy;
     int block;                          // threads per work-group
@@ -40,20 +36,20 @@ struct Shape {
     bool stage;
 };
 
-Shape resolve(const basp_plan &p, const basp_tuning &t, bool s2h)
+Shape resolve(const basp_plan &p, const basp_tuning &t)
 {
     const bool short_rows = p.row_bytes <= 128;
     Shape s;
-    s.vpt = t.vectors_per_thread ? t.vectors_per_thread : (s2h && !short_rows ? 1 : 2);
+    s.vpt = t.vectors_per_thread ? t.vectors_per_thread : 1;
     s.policy = t.cache_policy ? t.cache_policy : 4;
     s.block = t.block_size ? t.block_size : kBlock;
     s.tile_tokens = uint32_t(t.tile_tokens);
-    s.tile_heads = t.tile_heads ? uint32_t(t.tile_heads) : (s2h ? (short_rows ? 4 : 1) : 8);
+    s.tile_heads = t.tile_heads ? uint32_t(t.tile_heads) : (short_rows ? 8 : 1);
     s.heads_given = t.tile_heads != 0;
-    s.s_fast = t.lane_order ? t.lane_order == 1 : (!s2h && !short_rows);
-    s.heads_first = t.tile_order ? t.tile_order == 2 : !s2h;
+    s.s_fast = t.lane_order == 1;
+    s.heads_first = t.tile_order != 1;
     s.grid_cap = t.max_grid ? uint32_t(t.max_grid) : kGridCap;
-    s.xcd = t.xcd_remap ? t.xcd_remap == 2 : s2h;
+    s.xcd = t.xcd_remap == 2;
     s.stage = t.stage == 2;
     return s;
 }
@@ -192,7 +188,7 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
     const int vw = vector_width(p, addrs, 2 * nseg);
     const uint32_t A = uint32_t(p.row_bytes / vw);
     const Shape sh =
-        for_vector_width(resolve(p, p.tuning[s2h ? BASP_SEQ_TO_HEAD : BASP_HEAD_TO_SEQ], s2h), vw, A);
+        for_vector_width(resolve(p, p.tuning[s2h ? BASP_SEQ_TO_HEAD : BASP_HEAD_TO_SEQ]), vw, A);
     TileDesc &D = L.D;
     D.St = uint32_t(p.St);
     D.S = uint32_t(p.S);
@@ -331,12 +327,12 @@ int build_perm(const basp_plan &p, const PermSpec *ps, int n, int vw, PermLaunch
 
 }  // namespace
 
-basp_status check_launch_limits(const basp_plan &p, const basp_tuning &t, bool s2h)
+basp_status check_launch_limits(const basp_plan &p, const basp_tuning &t)
 {
     if (p.St > int64_t(kI31Max) || p.row_bytes > int64_t(kI31Max) ||
         int64_t(p.Hq) * p.row_bytes > int64_t(kI31Max) || !grid_fits(p))
         return BASP_ERR_UNSUPPORTED;
-    const Shape resolved = resolve(p, t, s2h);
+    const Shape resolved = resolve(p, t);
     const uint32_t heads[3] = {uint32_t(p.Hq), uint32_t(p.Hkv), uint32_t(p.Hkv)};
     // every vector width a launch may pick, with the tile it then uses
     for (int vw = 16; vw >= p.es; vw /= 2) {

@@ -130,9 +130,7 @@ extern "C" basp_plan *basp_plan_create_ex(int N, int B, int64_t S, int Hq, int H
     p->kv_elems = kv_elems;
     std::memset(p->tuning, 0, sizeof(p->tuning));
 
-    basp_status lim = basp::check_launch_limits(*p, p->tuning[0], true);
-    if (lim == BASP_OK)
-        lim = basp::check_launch_limits(*p, p->tuning[1], false);
+    const basp_status lim = basp::check_launch_limits(*p, p->tuning[0]);
     if (lim != BASP_OK) {
         delete p;
         record(lim);
@@ -217,7 +215,7 @@ extern "C" basp_status basp_plan_set_direction_tuning(basp_plan *p, basp_directi
 {
     if (!p || !t || (dir != BASP_SEQ_TO_HEAD && dir != BASP_HEAD_TO_SEQ) || !basp::tuning_in_range(*t))
         return record(BASP_ERR_INVALID);
-    const basp_status lim = basp::check_launch_limits(*p, *t, dir == BASP_SEQ_TO_HEAD);
+    const basp_status lim = basp::check_launch_limits(*p, *t);
     if (lim != BASP_OK)
         return record(lim);
     p->tuning[dir] = *t;
@@ -228,9 +226,7 @@ extern "C" basp_status basp_plan_set_tuning(basp_plan *p, const basp_tuning *t)
 {
     if (!p || !t || !basp::tuning_in_range(*t))
         return record(BASP_ERR_INVALID);
-    basp_status lim = basp::check_launch_limits(*p, *t, true);
-    if (lim == BASP_OK)
-        lim = basp::check_launch_limits(*p, *t, false);
+    const basp_status lim = basp::check_launch_limits(*p, *t);
     if (lim != BASP_OK)
         return record(lim);
     p->tuning[0] = p->tuning[1] = *t;

@@ -32,8 +32,8 @@ basp_status record(basp_status s);
 // Fields of a tuning within their documented ranges.
 bool tuning_in_range(const basp_tuning &t);
 
-// Check that every launch of this plan in one direction fits the kernels'
-// 31-bit index arithmetic with the given tuning.
-basp_status check_launch_limits(const basp_plan &p, const basp_tuning &t, bool s2h);
+// Check that every launch of this plan fits the kernels' index arithmetic
+// with the given tuning (the limits are the same in both directions).
+basp_status check_launch_limits(const basp_plan &p, const basp_tuning &t);
 
 }  // namespace basp

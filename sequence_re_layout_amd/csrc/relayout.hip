@@ -346,16 +346,16 @@ basp_status timed_call(F f)
 // ---------------------------------------------------------------- autotune --
 
 // Launch shapes a plan is measured with, all with non-temporal loads and
-// non-temporal device-scope stores (the policy the sweeps preferred) and 64
-// or 256 threads per work-group: direct over tile order x vectors per lane x
-// heads per tile x lane order x XCD order, and LDS-staged over tile order x
-// vectors per lane x heads per tile x XCD order.
+// non-temporal device-scope stores (the policy the sweeps preferred) and 64,
+// 128 or 256 threads per work-group: direct over tile order x vectors per
+// lane x heads per tile x lane order x XCD order, and LDS-staged over tile
+// order x vectors per lane x heads per tile x XCD order.
 std::vector<basp_tuning> autotune_candidates()
 {
     std::vector<basp_tuning> c;
-    for (int block : {64, 256})
+    for (int block : {64, 128, 256})
         for (int to : {1, 2})
-            for (int vpt : {1, 2, 4})
+            for (int vpt : {1, 2})
                 for (int th : {1, 2, 4, 8})
                     for (int xcd : {1, 2}) {
                         basp_tuning t = {};
@@ -486,7 +486,7 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
     std::vector<int> pick[2];
     for (int dir = 0; dir < 2; ++dir)
         for (int i = 0; i < int(cands.size()); ++i)
-            if (basp::check_launch_limits(*p, cands[i], dir == BASP_SEQ_TO_HEAD) == BASP_OK)
+            if (basp::check_launch_limits(*p, cands[i]) == BASP_OK)
                 pick[dir].push_back(i);
     std::vector<float> med[2];
     // coarse pass over every candidate, then a longer one over the best few;

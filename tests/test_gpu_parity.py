@@ -407,7 +407,8 @@ def test_autotune_keeps_results(shape, mode):
     b.basp_plan_autotune(plan, q, k, v, qkv, o, o_out)
     for direction in (b.BASP_SEQ_TO_HEAD, b.BASP_HEAD_TO_SEQ):
         t = b.basp_plan_get_tuning(plan, direction)
-        assert t["vectors_per_thread"] in (1, 2, 4) and t["cache_policy"] == 4
+        assert t["vectors_per_thread"] in (1, 2) and t["cache_policy"] == 4
+        assert t["block_size"] in (64, 128, 256) and t["xcd_remap"] in (1, 2)
         assert t["stage"] in (1, 2) and t["tile_order"] in (1, 2)   # explicit, not "built-in"
     qkv.fill_(0)
     o_out.fill_(0)
