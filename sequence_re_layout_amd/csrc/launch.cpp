@@ -237,6 +237,8 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
         sg.tile_end = uint32_t(total);
     }
     D.plane = uint32_t(total);
+    D.seg_end0 = D.seg[0].tile_end;
+    D.seg_end1 = D.seg[1].tile_end;
     D.xcd_span = sh.xcd ? uint32_t(total / kXcds) : 0;
     L.grid = uint32_t(std::min<uint64_t>(total, sh.grid_cap));
     L.grid_y = uint32_t(p.P);

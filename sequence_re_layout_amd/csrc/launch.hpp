@@ -66,9 +66,11 @@ struct TileSeg {
     uint32_t tile_begin, tile_end; // this tensor's tiles in the plane
 };
 
+// Launch-wide fields first: a kernel reads them in one batch of scalar
+// loads, then the one TileSeg its tile belongs to in a second batch.
 struct TileDesc {
-    TileSeg seg[3];
     uint32_t plane;                // tiles per (y, z) plane
+    uint32_t seg_end0, seg_end1;   // ends of the first and second tensor's tiles
     uint32_t St;
     uint32_t S;
     uint32_t token_major;          // head-sharded side is [Bl][S][Hl][d] (else [Bl][Hl][S][d])
@@ -81,6 +83,7 @@ struct TileDesc {
     uint32_t Bl;                   // sequences per group
     uint32_t bmul;                 // P when Bl == 1, else 1 (see tile_origin)
     FastDiv P, A;                  // group size, vectors per row
+    TileSeg seg[3];
 };
 
 // Work-groups are dispatched round-robin over the 8 XCDs.  With
@@ -96,18 +99,22 @@ BASP_HD inline uint32_t xcd_tile(uint32_t x, uint32_t span)
 
 // Where a tile starts and how much of it is real.
 struct TileOrigin {
-    uint32_t seg;
     uint64_t seq_off, head_off;    // byte offsets of the tile base
     uint32_t ns, nh;               // tokens and heads present (ragged tail)
 };
 
-// Tile x of the plane of group member y and batch index b.
-BASP_HD inline TileOrigin tile_origin(const TileDesc &D, uint32_t x, uint32_t y, uint32_t b)
+// The tensor a (remapped) tile of the plane belongs to.
+BASP_HD inline uint32_t tile_segment(const TileDesc &D, uint32_t tile)
 {
-    const uint32_t tile = xcd_tile(x, D.xcd_span);
+    return tile < D.seg_end0 ? 0u : (tile < D.seg_end1 ? 1u : 2u);
+}
+
+// Tile `tile` (after xcd_tile) of tensor sg, in the plane of group member y
+// and batch index b.
+BASP_HD inline TileOrigin tile_origin(const TileDesc &D, const TileSeg &sg, uint32_t tile, uint32_t y,
+                                      uint32_t b)
+{
     TileOrigin o;
-    o.seg = tile < D.seg[0].tile_end ? 0u : (tile < D.seg[1].tile_end ? 1u : 2u);
-    const TileSeg &sg = D.seg[o.seg];
     const uint32_t P = D.P.d;
     const uint32_t local = tile - sg.tile_begin;
     const uint32_t q = fastdiv(local, sg.fast), f = local - q * sg.fast.d;
@@ -155,7 +162,7 @@ BASP_HD inline bool tile_vector(const TileDesc &D, const TileSeg &sg, uint32_t n
 {
     const uint32_t A = D.A.d, Ts = sg.Ts.d, Th = sg.Th.d;
     const uint32_t r = fastdiv(v, D.A), vi = v - r * A;
-    const FastDiv &fast = s_fast ? sg.Ts : sg.Th;
+    const FastDiv fast = s_fast ? sg.Ts : sg.Th;
     const uint32_t slow = fastdiv(r, fast), fst = r - slow * fast.d;
     const uint32_t sl = s_fast ? fst : slow, hl = s_fast ? slow : fst;
     so = sl * sg.seq_tok + hl * D.row + vi * vw;

@@ -91,9 +91,14 @@ template <int BS, int VW, int VPT, int POL, bool S2H>
 __global__ __launch_bounds__(BS) void tile_kernel(const TileDesc D)
 {
     using V = typename Vec<VW>::type;
-    for (uint32_t tile = blockIdx.x; tile < D.plane; tile += gridDim.x) {
-        const TileOrigin o = tile_origin(D, tile, blockIdx.y, blockIdx.z);
-        const TileSeg &sg = D.seg[o.seg];
+    // a launch has at most D.plane work-groups along x, so each has a tile;
+    // testing only after the first lets the first tile's scalar loads go
+    // out in one batch
+    uint32_t tile = blockIdx.x;
+    do {
+        const uint32_t t = xcd_tile(tile, D.xcd_span);
+        const TileSeg sg = D.seg[tile_segment(D, t)];   // one batch of scalar loads
+        const TileOrigin o = tile_origin(D, sg, t, blockIdx.y, blockIdx.z);
         const __amdgpu_buffer_rsrc_t rseq = make_rsrc(sg.seq + o.seq_off, rest(sg.seq_bytes, o.seq_off));
         const __amdgpu_buffer_rsrc_t rhead =
             make_rsrc(sg.head + o.head_off, rest(sg.head_bytes, o.head_off));
@@ -115,7 +120,7 @@ __global__ __launch_bounds__(BS) void tile_kernel(const TileDesc D)
             for (int k = 0; k < VPT; ++k)
                 vstore<VW, Policy<POL>::store>(S2H ? rhead : rseq, dst[k], buf[k]);
         }
-    }
+    } while ((tile += gridDim.x) < D.plane);
 }
 
 // The same re-layout with each tile staged through LDS: the loads run along
@@ -127,9 +132,14 @@ __global__ __launch_bounds__(BS) void tile_kernel_staged(const TileDesc D)
 {
     using V = typename Vec<16>::type;
     __shared__ V stage[BS * VPT];
-    for (uint32_t tile = blockIdx.x; tile < D.plane; tile += gridDim.x) {
-        const TileOrigin o = tile_origin(D, tile, blockIdx.y, blockIdx.z);
-        const TileSeg &sg = D.seg[o.seg];
+    // a launch has at most D.plane work-groups along x, so each has a tile;
+    // testing only after the first lets the first tile's scalar loads go
+    // out in one batch
+    uint32_t tile = blockIdx.x;
+    do {
+        const uint32_t t = xcd_tile(tile, D.xcd_span);
+        const TileSeg sg = D.seg[tile_segment(D, t)];   // one batch of scalar loads
+        const TileOrigin o = tile_origin(D, sg, t, blockIdx.y, blockIdx.z);
         const __amdgpu_buffer_rsrc_t rseq = make_rsrc(sg.seq + o.seq_off, rest(sg.seq_bytes, o.seq_off));
         const __amdgpu_buffer_rsrc_t rhead =
             make_rsrc(sg.head + o.head_off, rest(sg.head_bytes, o.head_off));
@@ -163,7 +173,7 @@ __global__ __launch_bounds__(BS) void tile_kernel_staged(const TileDesc D)
         for (int k = 0; k < VPT; ++k)
             vstore<16, Policy<POL>::store>(S2H ? rhead : rseq, off[k], buf[k]);
         __syncthreads();   // the next tile reuses the staging area
-    }
+    } while ((tile += gridDim.x) < D.plane);
 }
 
 // One pass of the unfused baseline: linear destination, permuted source.

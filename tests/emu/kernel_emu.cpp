@@ -39,8 +39,9 @@ void run(const TileLaunch &L, uint64_t *bad)
         const uint32_t block = uint32_t(w % L.grid), by = uint32_t(w / L.grid % L.grid_y);
         const uint32_t bz = uint32_t(w / L.grid / L.grid_y);
         for (uint32_t tile = block; tile < D.plane; tile += L.grid) {
-            const TileOrigin o = tile_origin(D, tile, by, bz);
-            const TileSeg &sg = D.seg[o.seg];
+            const uint32_t t = xcd_tile(tile, D.xcd_span);
+            const TileSeg &sg = D.seg[tile_segment(D, t)];
+            const TileOrigin o = tile_origin(D, sg, t, by, bz);
             const uint64_t seq = sg.seq + o.seq_off, head = sg.head + o.head_off;
             const uint64_t nseq = range(rest(sg.seq_bytes, o.seq_off));
             const uint64_t nhead = range(rest(sg.head_bytes, o.head_off));
