@@ -138,7 +138,9 @@ typedef struct basp_plan_info {
  *                         Hkv % P != 0 [review, Frequently asked questions]
  *   BASP_ERR_UNSUPPORTED  a buffer of more than 2^62 bytes, a tensor of
  *                         2^32 or more (token, head) rows (B*S*max(Hq, Hkv)),
- *                         or more than 2^31 - 1 work tiles in one launch
+ *                         B above 65535 (the launch grid's z extent), or more
+ *                         than 2^31 - 1 work tiles per (group member, batch
+ *                         index) in one launch
  * basp_plan_create uses BASP_LAYOUT_HEAD_MAJOR.
  */
 basp_plan *basp_plan_create(int N, int B, int64_t S, int Hq, int Hkv, int d,

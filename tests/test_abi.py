@@ -210,3 +210,15 @@ def test_row_count_limit():
     with pytest.raises(b.BaspError) as e:
         b.basp_plan_create(2, 2, 1 << 29, 4, 8, 8, b.BASP_BF16, b.BASP_MODE_BASP)   # Hkv > Hq
     assert e.value.status == b.BASP_ERR_UNSUPPORTED
+
+
+def test_batch_fits_the_launch_grid():
+    """The batch index is the launch grid's z coordinate: B above 65535 is
+    rejected (here in the data-parallel fallback, N = 1), 65535 is not.  The
+    group size, the y coordinate, is bounded by the row limit (H >= P and
+    S >= P give P*P rows at least)."""
+    ok = b.basp_plan_create(1, 65535, 1, 1, 1, 8, b.BASP_BF16, b.BASP_MODE_BASP)
+    assert (ok.info["G"], ok.info["P"], ok.info["Bl"]) == (1, 1, 65535)
+    with pytest.raises(b.BaspError) as e:
+        b.basp_plan_create(1, 65536, 1, 1, 1, 8, b.BASP_BF16, b.BASP_MODE_BASP)
+    assert e.value.status == b.BASP_ERR_UNSUPPORTED
