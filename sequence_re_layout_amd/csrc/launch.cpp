@@ -19,11 +19,12 @@ constexpr uint32_t kGridCap = 1u << 22;  // work-groups per launch at most
 // defaults below, chosen on MI355X over every named workload of at least
 // 256 MiB (Llama/Qwen shapes, 128- and 256-byte rows, both modes, both
 // directions, rotating buffers) as the launch shape whose worst ratio to
-// each workload's best was highest (0.95; 0.98 on average): direct (no LDS
-// staging), 256 threads per work-group, one vector per lane, head blocks
-// fastest in work-group order, lanes along heads, non-temporal loads and
-// non-temporal device-scope stores; 8 heads per tile for 128-byte rows, one
-// head for longer rows.  basp_plan_autotune replaces these by measurement.
+// each workload's best was highest (0.94-0.95 in sweeps of two builds, 0.98
+// on average): direct (no LDS staging), 256 threads per work-group, one
+// vector per lane, head blocks fastest in work-group order, lanes along
+// heads, non-temporal loads and non-temporal device-scope stores; 8 heads
+// per tile for 128-byte rows, one head for longer rows.
+// basp_plan_autotune replaces these by measurement.
 struct Shape {
     int vpt, policy;
     int block;                          // threads per work-group

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(BS) void tile_kernel(const TileDesc D)
 // The same re-layout with each tile staged through LDS: the loads run along
 // the source layout's contiguous axis, the stores along the destination's, so
 // both sides of every wave instruction are contiguous.  A tile is one pass of
-// the work-group (the host sizes it to at most kBlock*VPT vectors).
+// the work-group (the host sizes it to at most BS*VPT vectors).
 template <int BS, int VPT, int POL, bool S2H>
 __global__ __launch_bounds__(BS) void tile_kernel_staged(const TileDesc D)
 {
