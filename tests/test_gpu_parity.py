@@ -343,6 +343,15 @@ def test_device_error_paths():
     # q, k and v may share one buffer
     b.basp_seq_to_head(plan, q, q, q, out)
     torch.cuda.synchronize()
+    # the NULL stream (0) is a valid stream
+    N, B, S, Hq, Hkv, d = 4, 2, 64, 8, 8, 64
+    qt, kt, vt = (x.cuda() for x in seq_inputs(B, S, Hq, Hkv, d, "int32"))
+    plan32 = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_INT32, b.BASP_MODE_BASP)
+    out32 = torch.empty(plan32.info["qkv_elems"], dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    b.basp_seq_to_head(plan32, qt, kt, vt, out32, stream=0)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out32), oracle.seq_to_head_qkv(bits(qt), bits(kt), bits(vt), 1, N, B, S, Hq, Hkv, d))
 
 
 def test_single_hip_runtime_and_native_library():
