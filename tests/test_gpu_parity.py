@@ -11,7 +11,10 @@ Coverage:
   (B > N), N = 1, unaligned (2-byte) views, all bf16 bit patterns;
 * guard bands around the output and a sentinel fill (each destination written
   exactly once, nothing outside written);
-* the backward entry points, the token-major layout and the unfused baseline.
+* the backward entry points, the token-major layout and the unfused baseline;
+* outputs beyond 4 GiB on sampled destinations, side streams and the NULL
+  stream, a whole step captured in a HIP graph and replayed, autotuning;
+* the plain copy the kernels are measured against (basp_stream_copy).
 """
 import numpy as np
 import pytest
