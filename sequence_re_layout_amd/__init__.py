@@ -9,10 +9,15 @@ before the library is built.  Using a binding name without a built
 """
 
 
+_SUBMODULES = ("binding", "build", "inputs", "workloads")
+
+
 def __getattr__(name):
     import importlib
     if name.startswith("__"):
         raise AttributeError(name)
+    if name in _SUBMODULES:   # `from sequence_re_layout_amd import build` before a build
+        return importlib.import_module(__name__ + "." + name)
     binding = importlib.import_module(__name__ + ".binding")
     try:
         return getattr(binding, name)
