@@ -241,6 +241,9 @@ basp_status basp_seq_to_head_unfused(const basp_plan *plan, const void *q, const
  *                        the destination's (used with 16-byte vectors and
  *                        tiles of one pass of the work-group)
  *   block_size           threads per work-group: 64, 128 or 256 (built-in)
+ *   batch_order          1 = the batch indices one after another (built-in),
+ *                        2 = batch indices interleaved with the tiles, so
+ *                        that neighbouring work-groups alternate sequences
  * vectors_per_thread and block_size apply to 16-byte vectors; rows or
  * pointers that need narrower vectors run 256 threads with 4 vectors each.
  * basp_plan_set_tuning sets both directions, basp_plan_set_direction_tuning
@@ -265,6 +268,7 @@ typedef struct basp_tuning {
     int32_t tile_order;
     int32_t stage;
     int32_t block_size;
+    int32_t batch_order;
 } basp_tuning;
 basp_status basp_plan_set_tuning(basp_plan *plan, const basp_tuning *tuning);
 basp_status basp_plan_set_direction_tuning(basp_plan *plan, basp_direction dir,

@@ -57,7 +57,7 @@ class basp_plan_info(ctypes.Structure):
 class basp_tuning(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "vectors_per_thread", "tile_tokens", "tile_heads", "cache_policy", "max_grid",
-        "lane_order", "xcd_remap", "tile_order", "stage", "block_size")]
+        "lane_order", "xcd_remap", "tile_order", "stage", "block_size", "batch_order")]
 
 
 class BaspError(RuntimeError):
@@ -181,7 +181,7 @@ def basp_plan_query(plan: Plan) -> dict:
 
 
 _TUNING_FIELDS = ("vectors_per_thread", "tile_tokens", "tile_heads", "cache_policy", "max_grid",
-                  "lane_order", "xcd_remap", "tile_order", "stage", "block_size")
+                  "lane_order", "xcd_remap", "tile_order", "stage", "block_size", "batch_order")
 
 
 def _tuning(fields) -> basp_tuning:

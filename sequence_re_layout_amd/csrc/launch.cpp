@@ -35,6 +35,7 @@ struct Shape {
     uint32_t grid_cap;
     bool xcd;
     bool stage;
+    bool batch_x;
 };
 
 Shape resolve(const basp_plan &p, const basp_tuning &t)
@@ -52,6 +53,7 @@ Shape resolve(const basp_plan &p, const basp_tuning &t)
     s.grid_cap = t.max_grid ? uint32_t(t.max_grid) : kGridCap;
     s.xcd = t.xcd_remap == 2;
     s.stage = t.stage == 2;
+    s.batch_x = t.batch_order == 2;
     return s;
 }
 
@@ -238,12 +240,17 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
         sg.tile_end = uint32_t(total);
     }
     D.plane = uint32_t(total);
+    D.batch_x = sh.batch_x && p.B > 1;
+    D.nb = make_fastdiv(uint32_t(p.B));
+    if (D.batch_x && total * uint64_t(p.B) > kI31Max)
+        return BASP_ERR_UNSUPPORTED;
+    D.xbound = D.batch_x ? uint32_t(total * uint64_t(p.B)) : uint32_t(total);
     D.seg_end0 = D.seg[0].tile_end;
     D.seg_end1 = D.seg[1].tile_end;
     D.xcd_span = sh.xcd ? uint32_t(total / kXcds) : 0;
-    L.grid = uint32_t(std::min<uint64_t>(total, sh.grid_cap));
+    L.grid = uint32_t(std::min<uint64_t>(D.xbound, sh.grid_cap));
     L.grid_y = uint32_t(p.P);
-    L.grid_z = uint32_t(p.B);
+    L.grid_z = D.batch_x ? 1u : uint32_t(p.B);
     L.vw = vw;
     L.vpt = sh.vpt;
     L.block = sh.block;
@@ -350,7 +357,7 @@ basp_status check_launch_limits(const basp_plan &p, const basp_tuning &t)
                 return BASP_ERR_UNSUPPORTED;
             total += ts.ntiles;
         }
-        if (total > kI31Max)
+        if (total * (sh.batch_x ? uint64_t(p.B) : 1u) > kI31Max)
             return BASP_ERR_UNSUPPORTED;
     }
     return BASP_OK;

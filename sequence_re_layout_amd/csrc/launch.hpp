@@ -19,7 +19,8 @@
 //
 // Launch grid.  blockIdx.z is the batch index b, blockIdx.y one group member
 // and blockIdx.x a tile of the (y, z) plane, Q, K and V planes one after the
-// other.  Two tile orders:
+// other; optionally the batch index is folded into x instead (tile_and_batch).
+// Two tile orders:
 //   token blocks fastest (the head-sharded layout's order): y = jh and x runs
 //     over (hb, js, tb), so neighbouring tiles continue one destination head
 //     across source members;
@@ -83,8 +84,26 @@ struct TileDesc {
     uint32_t Bl;                   // sequences per group
     uint32_t bmul;                 // P when Bl == 1, else 1 (see tile_origin)
     FastDiv P, A;                  // group size, vectors per row
+    uint32_t batch_x;              // batch index folded into x (else blockIdx.z)
+    uint32_t xbound;               // tiles along x: plane, or plane * B with batch_x
+    FastDiv nb;                    // B
     TileSeg seg[3];
 };
+
+// A work-group's tile of the plane and its batch index.  Either the grid's z
+// coordinate is the batch index, or (batch_x) x runs over (tile, batch
+// index) with the batch index fastest, so neighbouring work-groups take the
+// same tile of consecutive sequences.
+BASP_HD inline void tile_and_batch(const TileDesc &D, uint32_t x, uint32_t z, uint32_t &tile, uint32_t &b)
+{
+    if (D.batch_x) {
+        tile = fastdiv(x, D.nb);
+        b = x - tile * D.nb.d;
+    } else {
+        tile = x;
+        b = z;
+    }
+}
 
 // Work-groups are dispatched round-robin over the 8 XCDs.  With
 // xcd_span = plane/8 > 0 the i-th tile of a plane is renumbered so that

@@ -91,14 +91,16 @@ template <int BS, int VW, int VPT, int POL, bool S2H>
 __global__ __launch_bounds__(BS) void tile_kernel(const TileDesc D)
 {
     using V = typename Vec<VW>::type;
-    // a launch has at most D.plane work-groups along x, so each has a tile;
+    // a launch has at most D.xbound work-groups along x, so each has a tile;
     // testing only after the first lets the first tile's scalar loads go
     // out in one batch
-    uint32_t tile = blockIdx.x;
+    uint32_t x = blockIdx.x;
     do {
+        uint32_t tile, bz;
+        tile_and_batch(D, x, blockIdx.z, tile, bz);
         const uint32_t t = xcd_tile(tile, D.xcd_span);
         const TileSeg sg = D.seg[tile_segment(D, t)];   // one batch of scalar loads
-        const TileOrigin o = tile_origin(D, sg, t, blockIdx.y, blockIdx.z);
+        const TileOrigin o = tile_origin(D, sg, t, blockIdx.y, bz);
         const __amdgpu_buffer_rsrc_t rseq = make_rsrc(sg.seq + o.seq_off, rest(sg.seq_bytes, o.seq_off));
         const __amdgpu_buffer_rsrc_t rhead =
             make_rsrc(sg.head + o.head_off, rest(sg.head_bytes, o.head_off));
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(BS) void tile_kernel(const TileDesc D)
             for (int k = 0; k < VPT; ++k)
                 vstore<VW, Policy<POL>::store>(S2H ? rhead : rseq, dst[k], buf[k]);
         }
-    } while ((tile += gridDim.x) < D.plane);
+    } while ((x += gridDim.x) < D.xbound);
 }
 
 // The same re-layout with each tile staged through LDS: the loads run along
@@ -132,14 +134,16 @@ __global__ __launch_bounds__(BS) void tile_kernel_staged(const TileDesc D)
 {
     using V = typename Vec<16>::type;
     __shared__ V stage[BS * VPT];
-    // a launch has at most D.plane work-groups along x, so each has a tile;
+    // a launch has at most D.xbound work-groups along x, so each has a tile;
     // testing only after the first lets the first tile's scalar loads go
     // out in one batch
-    uint32_t tile = blockIdx.x;
+    uint32_t x = blockIdx.x;
     do {
+        uint32_t tile, bz;
+        tile_and_batch(D, x, blockIdx.z, tile, bz);
         const uint32_t t = xcd_tile(tile, D.xcd_span);
         const TileSeg sg = D.seg[tile_segment(D, t)];   // one batch of scalar loads
-        const TileOrigin o = tile_origin(D, sg, t, blockIdx.y, blockIdx.z);
+        const TileOrigin o = tile_origin(D, sg, t, blockIdx.y, bz);
         const __amdgpu_buffer_rsrc_t rseq = make_rsrc(sg.seq + o.seq_off, rest(sg.seq_bytes, o.seq_off));
         const __amdgpu_buffer_rsrc_t rhead =
             make_rsrc(sg.head + o.head_off, rest(sg.head_bytes, o.head_off));
@@ -173,7 +177,7 @@ __global__ __launch_bounds__(BS) void tile_kernel_staged(const TileDesc D)
         for (int k = 0; k < VPT; ++k)
             vstore<16, Policy<POL>::store>(S2H ? rhead : rseq, off[k], buf[k]);
         __syncthreads();   // the next tile reuses the staging area
-    } while ((tile += gridDim.x) < D.plane);
+    } while ((x += gridDim.x) < D.xbound);
 }
 
 // One pass of the unfused baseline: linear destination, permuted source.
@@ -356,33 +360,36 @@ basp_status timed_call(F f)
 // ---------------------------------------------------------------- autotune --
 
 // Launch shapes a plan is measured with, all with non-temporal loads and
-// non-temporal device-scope stores (the policy the sweeps preferred) and 64,
-// 128 or 256 threads per work-group: direct over tile order x vectors per
-// lane x heads per tile x lane order x XCD order, and LDS-staged over tile
-// order x vectors per lane x heads per tile x XCD order.
+// non-temporal device-scope stores (the policy the sweeps preferred), over
+// batch order x work-group size (64, 128, 256) x tile order x vectors per
+// lane x heads per tile x XCD order, each direct with both lane orders and
+// LDS-staged.
 std::vector<basp_tuning> autotune_candidates()
 {
     std::vector<basp_tuning> c;
-    for (int block : {64, 128, 256})
-        for (int to : {1, 2})
-            for (int vpt : {1, 2})
-                for (int th : {1, 2, 4, 8})
-                    for (int xcd : {1, 2}) {
-                        basp_tuning t = {};
-                        t.block_size = block;
-                        t.tile_order = to;
-                        t.vectors_per_thread = vpt;
-                        t.tile_heads = th;
-                        t.xcd_remap = xcd;
-                        t.cache_policy = 4;
-                        t.stage = 2;
-                        c.push_back(t);
-                        t.stage = 1;
-                        for (int lo : {1, 2}) {
-                            t.lane_order = lo;
+    const int blocks[] = {64, 128, 256}, heads[] = {1, 2, 4, 8};
+    for (int bo = 1; bo <= 2; ++bo)
+        for (int block : blocks)
+            for (int to = 1; to <= 2; ++to)
+                for (int vpt = 1; vpt <= 2; ++vpt)
+                    for (int th : heads)
+                        for (int xcd = 1; xcd <= 2; ++xcd) {
+                            basp_tuning t = {};
+                            t.batch_order = bo;
+                            t.block_size = block;
+                            t.tile_order = to;
+                            t.vectors_per_thread = vpt;
+                            t.tile_heads = th;
+                            t.xcd_remap = xcd;
+                            t.cache_policy = 4;
+                            t.stage = 2;
                             c.push_back(t);
+                            t.stage = 1;
+                            for (int lo = 1; lo <= 2; ++lo) {
+                                t.lane_order = lo;
+                                c.push_back(t);
+                            }
                         }
-                    }
     return c;
 }
 

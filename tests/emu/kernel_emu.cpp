@@ -38,10 +38,12 @@ void run(const TileLaunch &L, uint64_t *bad)
     for (uint64_t w = 0; w < groups; ++w) {
         const uint32_t block = uint32_t(w % L.grid), by = uint32_t(w / L.grid % L.grid_y);
         const uint32_t bz = uint32_t(w / L.grid / L.grid_y);
-        for (uint32_t tile = block; tile < D.plane; tile += L.grid) {
+        for (uint32_t x = block; x < D.xbound; x += L.grid) {
+            uint32_t tile, b;
+            tile_and_batch(D, x, bz, tile, b);
             const uint32_t t = xcd_tile(tile, D.xcd_span);
             const TileSeg &sg = D.seg[tile_segment(D, t)];
-            const TileOrigin o = tile_origin(D, sg, t, by, bz);
+            const TileOrigin o = tile_origin(D, sg, t, by, b);
             const uint64_t seq = sg.seq + o.seq_off, head = sg.head + o.head_off;
             const uint64_t nseq = range(rest(sg.seq_bytes, o.seq_off));
             const uint64_t nhead = range(rest(sg.head_bytes, o.head_off));

@@ -112,6 +112,7 @@ int main()
     small.lane_order = 1;
     small.tile_order = 1;
     small.xcd_remap = 2;
+    small.batch_order = 2;
     for (const Shape &s : shapes) {
         run_case(s, nullptr);
         run_case(s, &staged);

@@ -139,7 +139,8 @@ def test_tuning_validation():
     assert e.value.status == b.BASP_ERR_INVALID
     with pytest.raises(TypeError):
         b.basp_plan_set_tuning(p, tile_size=3)
-    for bad in (dict(vectors_per_thread=3), dict(cache_policy=6), dict(tile_tokens=-1), dict(block_size=96)):
+    for bad in (dict(vectors_per_thread=3), dict(cache_policy=6), dict(tile_tokens=-1), dict(block_size=96),
+                dict(batch_order=3)):
         with pytest.raises(b.BaspError) as e:
             b.basp_plan_set_tuning(p, **bad)
         assert e.value.status == b.BASP_ERR_INVALID

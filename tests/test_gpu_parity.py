@@ -172,7 +172,8 @@ TUNINGS = [dict(vectors_per_thread=1), dict(vectors_per_thread=2), dict(vectors_
            dict(stage=2), dict(stage=2, vectors_per_thread=1, tile_heads=8, cache_policy=2),
            dict(stage=2, vectors_per_thread=8, tile_tokens=500, tile_order=2, max_grid=5),
            dict(block_size=64, cache_policy=4), dict(block_size=128, stage=2, vectors_per_thread=8, cache_policy=5),
-           dict(block_size=64, stage=1, tile_tokens=9, max_grid=7)]
+           dict(block_size=64, stage=1, tile_tokens=9, max_grid=7),
+           dict(batch_order=2), dict(batch_order=2, stage=2, tile_order=1, xcd_remap=2, max_grid=9)]
 
 
 @pytest.mark.parametrize("tuning", TUNINGS, ids=lambda t: ",".join("%s=%s" % kv for kv in t.items()))

@@ -35,7 +35,7 @@ def emu(tmp_path_factory):
     lib.basp_plan_create_ex.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32]
     lib.basp_plan_create_ex.restype = vp
     lib.basp_plan_destroy.argtypes = [vp]
-    lib.basp_plan_set_tuning.argtypes = [vp, ctypes.POINTER(ctypes.c_int32 * 10)]
+    lib.basp_plan_set_tuning.argtypes = [vp, ctypes.POINTER(ctypes.c_int32 * 11)]
     lib.basp_plan_set_tuning.restype = i32
     tail = [ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_int)]
     lib.emu_seq_to_head.argtypes = [vp, vp, vp, vp, vp] + tail
@@ -58,9 +58,9 @@ class Run:
         self.plan = lib.basp_plan_create_ex(N, B, S, Hq, Hkv, d, dtype, mode, layout)
         assert self.plan, "plan rejected"
         if tuning:
-            t = (ctypes.c_int32 * 10)(*[tuning.get(k, 0) for k in (
+            t = (ctypes.c_int32 * 11)(*[tuning.get(k, 0) for k in (
                 "vectors_per_thread", "tile_tokens", "tile_heads", "cache_policy", "max_grid",
-                "lane_order", "xcd_remap", "tile_order", "stage", "block_size")])
+                "lane_order", "xcd_remap", "tile_order", "stage", "block_size", "batch_order")])
             assert lib.basp_plan_set_tuning(self.plan, ctypes.byref(t)) == 0
 
     def __call__(self, fn, *arrays):
@@ -150,7 +150,10 @@ TUNINGS = [dict(vectors_per_thread=1), dict(vectors_per_thread=2), dict(vectors_
            dict(stage=2, tile_order=2, xcd_remap=2, tile_heads=3, max_grid=5),
            dict(block_size=64), dict(block_size=128, vectors_per_thread=1, stage=1),
            dict(block_size=64, stage=2, vectors_per_thread=8, tile_heads=8), dict(block_size=64, stage=1, tile_tokens=9),
-           dict(cache_policy=4), dict(cache_policy=5, block_size=128, stage=2)]
+           dict(cache_policy=4), dict(cache_policy=5, block_size=128, stage=2),
+           dict(batch_order=2), dict(batch_order=2, tile_order=1, max_grid=5),
+           dict(batch_order=2, stage=2, xcd_remap=2, block_size=64, tile_heads=2),
+           dict(batch_order=1, tile_order=1, xcd_remap=2)]
 
 
 @pytest.mark.parametrize("tuning", TUNINGS, ids=lambda t: ",".join("%s=%s" % kv for kv in t.items()))
@@ -191,6 +194,9 @@ def test_degenerate(emu, shape, mode):
         for es in (2, 4):
             check_s2h(emu, shape, mode, layout, es)
             check_h2s(emu, shape, mode, layout, es)
+    # batch indices interleaved with the tiles
+    check_s2h(emu, shape, mode, 0, 2, dict(batch_order=2))
+    check_h2s(emu, shape, mode, 1, 4, dict(batch_order=2, tile_order=1))
 
 
 SCALED = [(w[0], w[1], w[2], max(w[3] // 16, w[1]), w[4], w[5], w[6]) for w in workloads.ALL + workloads.EXTRA]
@@ -206,7 +212,7 @@ def test_workloads_scaled(emu, w, mode):
 @pytest.mark.parametrize("mode", [1, 0], ids=["basp", "ulysses"])
 def test_llama1b_full_size(emu, mode):
     check_s2h(emu, workloads.LLAMA_1B[1:], mode, 0, 2)
-    check_h2s(emu, workloads.LLAMA_1B[1:], mode, 0, 2)
+    check_h2s(emu, workloads.LLAMA_1B[1:], mode, 0, 2, dict(batch_order=2))
 
 
 @pytest.mark.parametrize("mode", [1, 0], ids=["basp", "ulysses"])
