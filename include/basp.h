@@ -279,9 +279,11 @@ basp_status basp_plan_get_tuning(const basp_plan *plan, basp_direction dir, basp
  * Choose the launch shape of both directions by measurement on the caller's
  * buffers (as a planner that times candidates): a fixed set of launch shapes
  * is timed for seq->head on (q, k, v -> qkv) and for head->seq on
- * (o -> o_out), in rounds that alternate the two directions, and the shape
- * with the lowest median time in each direction is stored in the plan,
- * replacing its tuning.  The buffers are those of basp_seq_to_head and
+ * (o -> o_out), in rounds that alternate the two directions, each timed
+ * launch right after an untimed launch of the other direction with the
+ * plan's shape on entry (as the two run back to back in a step), and the
+ * shape with the lowest median time in each direction is stored in the
+ * plan, replacing its tuning.  The buffers are those of basp_seq_to_head and
  * basp_head_to_seq, with the same checks; qkv and o_out are overwritten.
  * Runs on stream and waits for it; creates and destroys HIP events but
  * allocates no device memory.  A pending basp_time_next_call request is

@@ -400,13 +400,17 @@ struct Job {
 };
 
 // Launch every job once, each timed from its own dispatch timestamps, in
-// batches of kPool launches that share a pool of events.  False on a HIP
-// error; a job whose shape the plan rejects gets a time < 0.
+// batches of kPool launches that share a pool of events.  Each timed launch
+// comes right after an untimed launch of the other direction (partner), as
+// in a step that runs the two back to back: a launch timed alone starts on a
+// drained memory system, and launch shapes ranked that way did not keep
+// their order back to back.  False on a HIP error; a job whose shape the
+// plan rejects gets a time < 0.
 constexpr int kPool = 64;
 
 bool run_jobs(basp_plan &p, const std::vector<basp_tuning> &cands, std::vector<Job> &jobs,
-              const void *q, const void *k, const void *v, void *qkv, const void *o, void *o_out,
-              void *stream, hipEvent_t *ev)
+              const TileLaunch (&partner)[2], const void *q, const void *k, const void *v,
+              void *qkv, const void *o, void *o_out, void *stream, hipEvent_t *ev)
 {
     for (size_t first = 0; first < jobs.size(); first += kPool) {
         const size_t last = std::min(jobs.size(), first + kPool);
@@ -419,6 +423,8 @@ bool run_jobs(basp_plan &p, const std::vector<basp_tuning> &cands, std::vector<J
             job.ms = -1.f;
             if (st != BASP_OK)
                 continue;
+            if (launch(partner[1 - job.dir], stream) != BASP_OK)
+                return false;
             t_timing.start = ev[2 * (j - first)];
             t_timing.stop = ev[2 * (j - first) + 1];
             const basp_status ls = launch(L, stream);
@@ -439,12 +445,11 @@ bool run_jobs(basp_plan &p, const std::vector<basp_tuning> &cands, std::vector<J
 
 // Median time of each (direction, candidate) over `rounds` rounds in which
 // every pair is launched once, seq->head and head->seq alternating, so that
-// each launch follows one that streamed other buffers and slow drifts of the
-// device affect all candidates alike.
+// slow drifts of the device affect all candidates alike.
 bool measure_rounds(basp_plan &p, const std::vector<basp_tuning> &cands,
                     const std::vector<int> (&pick)[2], int rounds, std::vector<float> (&med)[2],
-                    const void *q, const void *k, const void *v, void *qkv, const void *o,
-                    void *o_out, void *stream, hipEvent_t *ev)
+                    const TileLaunch (&partner)[2], const void *q, const void *k, const void *v,
+                    void *qkv, const void *o, void *o_out, void *stream, hipEvent_t *ev)
 {
     const size_t n = std::max(pick[0].size(), pick[1].size());
     std::vector<std::vector<float>> times[2];
@@ -456,7 +461,7 @@ bool measure_rounds(basp_plan &p, const std::vector<basp_tuning> &cands,
             for (int dir = 0; dir < 2; ++dir)
                 if (i < pick[dir].size())
                     jobs.push_back({dir, pick[dir][i], 0.f});
-        if (!run_jobs(p, cands, jobs, q, k, v, qkv, o, o_out, stream, ev))
+        if (!run_jobs(p, cands, jobs, partner, q, k, v, qkv, o, o_out, stream, ev))
             return false;
         size_t idx[2] = {0, 0};
         for (const Job &job : jobs)
@@ -484,10 +489,11 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
     basp::t_timing = basp::Timing();
     if (!p)
         return record(BASP_ERR_INVALID);
-    basp::TileLaunch L;
-    int s = basp::prepare_seq_to_head(*p, q, k, v, qkv, L);
+    // the partner launches: each direction with the plan's shape on entry
+    basp::TileLaunch partner[2];
+    int s = basp::prepare_seq_to_head(*p, q, k, v, qkv, partner[BASP_SEQ_TO_HEAD]);
     if (s == BASP_OK)
-        s = basp::prepare_head_to_seq(*p, o, o_out, L);
+        s = basp::prepare_head_to_seq(*p, o, o_out, partner[BASP_HEAD_TO_SEQ]);
     if (s != BASP_OK || p->S == 0)
         return record(basp_status(s));
 
@@ -508,7 +514,7 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
     std::vector<float> med[2];
     // coarse pass over every candidate, then a longer one over the best few;
     // a direction without any measured candidate keeps its tuning
-    ok = ok && basp::measure_rounds(*p, cands, pick, kCoarse, med, q, k, v, qkv, o, o_out, stream, ev);
+    ok = ok && basp::measure_rounds(*p, cands, pick, kCoarse, med, partner, q, k, v, qkv, o, o_out, stream, ev);
     for (int dir = 0; dir < 2 && ok; ++dir) {
         std::vector<std::pair<float, int>> order;
         for (size_t i = 0; i < pick[dir].size(); ++i)
@@ -519,7 +525,7 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
         for (size_t i = 0; i < order.size() && int(i) < kKeep; ++i)
             pick[dir].push_back(order[i].second);
     }
-    ok = ok && basp::measure_rounds(*p, cands, pick, kFine, med, q, k, v, qkv, o, o_out, stream, ev);
+    ok = ok && basp::measure_rounds(*p, cands, pick, kFine, med, partner, q, k, v, qkv, o, o_out, stream, ev);
     basp_tuning chosen[2] = {saved[0], saved[1]};
     for (int dir = 0; dir < 2 && ok; ++dir) {
         int best = -1;
