@@ -134,6 +134,18 @@ def test_workload_full_size(w, mode):
 
 
 @pytest.mark.parametrize("mode", ["basp", "ulysses"])
+@pytest.mark.parametrize("w", [workloads.LLAMA_1B, workloads.LONG_CONTEXT[-1]],
+                         ids=[workloads.LLAMA_1B[0], workloads.LONG_CONTEXT[-1][0]])
+def test_workload_full_size_token_major(w, mode):
+    """The token-major head layout ([Bl][S][Hl][d]) at full size."""
+    needs_gpu()
+    print("workload token-major", w, mode, flush=True)
+    run_s2h(w[1:], mode, layout=1)
+    run_h2s(w[1:], mode, layout=1)
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode", ["basp", "ulysses"])
 def test_tiny_int32_tagged(mode):
     needs_gpu()
     shape = workloads.TINY[1:]
