@@ -547,7 +547,17 @@ def pmc_summary(fetch_dir, write_dir):
                         "copy_kernel": cal_row["Kernel_Name"],
                         "copy_kib_raw": cal, "scale": factor,
                         "bytes_per_launch": kib * factor * 1024.0, "launches": len(fused)}
+        # the head->seq kernel of the same steps, for reference
+        back = [r for r in timed if "tile_kernel" in r["Kernel_Name"] and "false>" in r["Kernel_Name"]]
+        if back:
+            kb = statistics.median(float(r["Counter_Value"]) for r in back)
+            out.setdefault("head_to_seq", {})[counter] = {
+                "kib_per_launch_raw": kb, "kernel_name": back[0]["Kernel_Name"],
+                "bytes_per_launch": kb * factor * 1024.0, "launches": len(back)}
     out["traffic_bytes_per_launch"] = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
+    if len(out.get("head_to_seq", {})) == 2:
+        h = out["head_to_seq"]
+        h["traffic_bytes_per_launch"] = h["FETCH_SIZE"]["bytes_per_launch"] + h["WRITE_SIZE"]["bytes_per_launch"]
     return out
 
 
