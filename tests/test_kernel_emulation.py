@@ -182,6 +182,10 @@ def test_vector_width_follows_alignment(emu, offset, es, expect_vw):
     shape = (4, 2, 4 * 21, 8, 4, 64)
     assert check_s2h(emu, shape, 1, 0, es, offset=offset) == expect_vw
     assert check_h2s(emu, shape, 0, 1, es, offset=offset) == expect_vw
+    # the same vector width with batch indices interleaved and a capped grid
+    tuning = dict(batch_order=2, max_grid=5, tile_order=1)
+    assert check_s2h(emu, shape, 0, 1, es, tuning, offset=offset) == expect_vw
+    assert check_h2s(emu, shape, 1, 0, es, tuning, offset=offset) == expect_vw
 
 
 @pytest.mark.parametrize("shape,mode", [
