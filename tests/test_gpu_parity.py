@@ -251,11 +251,15 @@ def test_unaligned_views():
         return buf[1:]
     out_buf = torch.empty(plan.info["qkv_elems"] + 1, dtype=torch.bfloat16, device="cuda")
     out = out_buf[1:]
-    b.basp_seq_to_head(plan, shifted(q), shifted(k), shifted(v), out)
-    torch.cuda.synchronize()
     want = oracle.seq_to_head_qkv(inputs.raw_bits(q), inputs.raw_bits(k), inputs.raw_bits(v),
                                   1, N, B, S, Hq, Hkv, d)
-    assert np.array_equal(bits(out), want)
+    for tuning in ({}, dict(batch_order=2, max_grid=5, tile_order=1)):
+        if tuning:
+            b.basp_plan_set_tuning(plan, **tuning)
+        out.fill_(0)
+        b.basp_seq_to_head(plan, shifted(q), shifted(k), shifted(v), out)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), want), tuning
 
 
 def test_all_bf16_patterns_round_trip():
