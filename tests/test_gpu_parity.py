@@ -604,3 +604,45 @@ def test_stream_copy_errors_on_device():
     with pytest.raises(b.BaspError):
         b.basp_stream_copy(x[2048:], x[1:], 1024)     # misaligned source
     b.basp_stream_copy(x[2048:], x, 0)                # zero bytes: nothing to do
+
+
+def test_plan_shared_by_threads_and_streams():
+    """One plan used at the same time by four host threads, each launching
+    both directions on its own stream (default priority) on its own buffers;
+    every result matches the oracle."""
+    needs_gpu()
+    import threading
+    N, B, S, Hq, Hkv, d = 6, 3, 6 * 37, 12, 6, 40
+    plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_INT32, 0)
+    i = plan.info
+    q, k, v = seq_inputs(B, S, Hq, Hkv, d, "int32")
+    o = inputs.tags_int32(i["q_elems"], 7)
+    want_s = oracle.seq_to_head_qkv(bits(q), bits(k), bits(v), 0, N, B, S, Hq, Hkv, d)
+    want_h = oracle.head_to_seq(bits(o), 0, N, B, S, Hq, d)
+    results, errors = {}, []
+    torch.cuda.synchronize()
+
+    def worker(t):
+        try:
+            torch.cuda.set_device(0)
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                qd, kd, vd, od = (x.cuda() for x in (q, k, v, o))
+                out = torch.empty(i["qkv_elems"], dtype=torch.int32, device="cuda")
+                back = torch.empty(i["q_elems"], dtype=torch.int32, device="cuda")
+                for _ in range(20):
+                    b.basp_seq_to_head(plan, qd, kd, vd, out)
+                    b.basp_head_to_seq(plan, od, back)
+            stream.synchronize()
+            results[t] = (bits(out), bits(back))
+        except Exception as e:   # reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    for t in range(4):
+        assert np.array_equal(results[t][0], want_s) and np.array_equal(results[t][1], want_h), t
