@@ -21,6 +21,7 @@ import pytest
 import torch
 
 import oracle
+from tests import random_cases
 from sequence_re_layout_amd import inputs, workloads
 
 pytestmark = pytest.mark.gpu
@@ -646,3 +647,15 @@ def test_plan_shared_by_threads_and_streams():
     assert not errors, errors
     for t in range(4):
         assert np.array_equal(results[t][0], want_s) and np.array_equal(results[t][1], want_h), t
+
+
+@pytest.mark.parametrize("seed", range(random_cases.COUNT))
+def test_random_shapes_and_tunings(seed):
+    """Seeded random plans and launch shapes (odd row sizes, every tuning
+    field), both directions, int32 tags and bf16, inside guard bands."""
+    needs_gpu()
+    shape, mode, layout, tuning = random_cases.case(seed)
+    dtype = "int32" if seed % 2 else "bf16"
+    print("random case", seed, shape, mode, layout, tuning, flush=True)
+    run_s2h(shape, mode, dtype, layout, tuning)
+    run_h2s(shape, mode, dtype, layout, tuning)

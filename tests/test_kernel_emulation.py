@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 
 import oracle
+from tests import random_cases
 from sequence_re_layout_amd import workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -242,3 +243,14 @@ def test_backward_and_unfused(emu, shape, layout, mode):
     ws = _empty(2 * (nq + 2 * nkv), 2)
     run("emu_seq_to_head_unfused", q, k, v, out, ws)
     assert np.array_equal(out, oracle.seq_to_head_qkv(q, k, v, mode, N, B, S, Hq, Hkv, d, layout))
+
+
+@pytest.mark.parametrize("seed", range(random_cases.COUNT))
+def test_random_shapes_and_tunings(emu, seed):
+    """The GPU tests' seeded random cases: every access inside its
+    descriptor and the oracle's result, both element sizes."""
+    shape, mode, layout, tuning = random_cases.case(seed)
+    m = 1 if mode == "basp" else 0
+    for es in (2, 4):
+        check_s2h(emu, shape, m, layout, es, tuning)
+        check_h2s(emu, shape, m, layout, es, tuning)
