@@ -332,6 +332,34 @@ def copy_loop(b, s_bytes, h_bytes, steps, every):
             "h2s_bytes_gbs": rate(h_bytes, h_t), "steps": steps}
 
 
+def graph_step(b, w, steps_per_graph=10, replays=20):
+    """The same step replayed from a HIP graph: steps_per_graph steps over
+    the rotating buffer sets are captured once (the entry points only launch
+    kernels, so they capture), then replayed; the rate over all replays,
+    between two events, against the eager loop's."""
+    import torch
+    plan, sets = w.plan, w.sets
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for i in range(steps_per_graph):
+            s = sets[i % w.R]
+            b.basp_seq_to_head(plan, s["q"], s["k"], s["v"], s["qkv_out"])
+            b.basp_head_to_seq(plan, s["o"], s["o_out"])
+    graph.replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    seconds = start.elapsed_time(stop) * 1e-3 / (replays * steps_per_graph)
+    del graph
+    return {"steps": replays * steps_per_graph, "us_per_step": seconds * 1e6,
+            "gbs": rate(w.s2h_bytes + w.h2s_bytes, seconds)}
+
+
 def detail(args, b, w):
     """Per-kernel rates of both modes, the unfused baseline, the backward
     entry points, the token-major layout and a plain device copy."""
@@ -390,6 +418,7 @@ def detail(args, b, w):
         if ww is not w:
             del ww
             torch.cuda.empty_cache()
+    out["graph_step"] = graph_step(b, w)
     # plain device copy of the same byte count (read + write), and the
     # known-size copy the PMC counters are scaled by
     nb = w.s2h_bytes // 2
