@@ -592,25 +592,11 @@ def pmc_summary(fetch_dir, write_dir):
 
 # ---------------------------------------------------------------- main ---
 
-def main(argv=None):
-    args = parse_args(argv)
-    if args.pmc_summary:
-        res = pmc_summary(*args.pmc_summary)
-        res["workload"] = parse_args([]).workload
-        with open(TRAFFIC_FILE, "w") as f:
-            json.dump(res, f, indent=1)
-        print(json.dumps(res))
-        return 0
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: the N virtual ranks of the re-layout share one "
-              "device allocation, and no multi-GPU path exists (requested --gpus %d)" % args.gpus,
-              file=sys.stderr)
-        return 2
-
-    r = run_gpu(args)
-    w = r.pop("w")
+def make_line(args, r, w, traffic):
+    """The JSON line's fields from the measurements r of run_gpu and the
+    workload w (its shape, name and mode); traffic is the HBM bytes per fused
+    launch from the committed counters, or None."""
     N, B, S, Hq, Hkv, d = w.shape
-    traffic = traffic_bytes(w.name)
     line = {
         "metric": METRIC,
         "value": r["value"],
@@ -647,6 +633,27 @@ def main(argv=None):
                         "avg_launch_us": r["h2s_avg_us"], "bytes_per_launch": r["h2s_bytes"]},
         "round_trip_bit_exact": r["round_trip_bit_exact"],
     }
+    return line
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.pmc_summary:
+        res = pmc_summary(*args.pmc_summary)
+        res["workload"] = parse_args([]).workload
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(res, f, indent=1)
+        print(json.dumps(res))
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the N virtual ranks of the re-layout share one "
+              "device allocation, and no multi-GPU path exists (requested --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        return 2
+
+    r = run_gpu(args)
+    w = r.pop("w")
+    line = make_line(args, r, w, traffic_bytes(w.name))
     if "detail" in r:
         line["detail"] = r["detail"]
     if "workloads" in r:

@@ -57,3 +57,34 @@ def test_traffic_only_for_matching_sources_and_workload(tmp_path, monkeypatch):
     path.write_text(json.dumps({"workload": "w", "kernel_sources_sha256": "0" * 64,
                                 "traffic_bytes_per_launch": 123.0}))
     assert bench.traffic_bytes("w") is None
+
+
+def test_json_line_contract():
+    """The bench line carries every field the benchmark contract names, with
+    the roofline of the fused kernel against the 8 TB/s peak (no GPU: fake
+    measurements through the same assembly code)."""
+    import types
+    import bench
+    args = bench.parse_args([])
+    sb, hb = 402653184, 268435456
+    r = {"value": 6300.0, "ms_per_step": 0.1065, "rotate_sets": 5, "step_bytes": sb + hb,
+         "tuning": {"seq_to_head": {}, "head_to_seq": {}, "autotuned": True},
+         "s2h_gbs": 6400.0, "h2s_gbs": 6370.0, "s2h_bytes": sb, "h2s_bytes": hb,
+         "s2h_avg_us": 62.9, "h2s_avg_us": 42.1, "timed_launches_per_kernel": 50,
+         "copy_ceiling": {str(sb): {"gbs": 6790.0}, str(hb): {"gbs": 6690.0}},
+         "copy_loop": {"step_gbs": 6620.0, "s2h_bytes_gbs": 6550.0, "h2s_bytes_gbs": 6590.0, "steps": 200},
+         "round_trip_bit_exact": True}
+    w = types.SimpleNamespace(shape=(8, 2, 16384, 32, 8, 64), name="llama3.2-1b_s16k_b2", mode="basp")
+    line = bench.make_line(args, r, w, 402657919.0)
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline"):
+        assert key in line, key
+    assert line["n_gpus"] == 1 and line["unit"] == "GB/s" and line["higher_is_better"] is True
+    assert line["steps"] == 500 and line["warmup"] == 50 and line["vs_baseline"] is None
+    assert line["config"]["workload"] == "llama3.2-1b_s16k_b2" and "model" not in line["config"]
+    roof = line["roofline"]
+    assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
+    assert abs(roof["frac"] - 0.8) < 1e-12 and roof["traffic"] == 402657919.0
+    assert line["copy_ceiling"]["in_timed_loop"]["step_frac_of_copy"] == 6300.0 / 6620.0
+    json.dumps(line)   # serialisable
+
