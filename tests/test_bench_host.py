@@ -1,5 +1,5 @@
 """Host-side pieces of bench.py (no GPU): the one-GPU guard, the PMC counter
-summary and its source-hash gate."""
+summary and its source-hash gate, and the fields of the JSON line."""
 import csv
 import json
 import os
@@ -29,7 +29,6 @@ def test_pmc_summary_scales_by_the_copy(tmp_path):
     other = "void basp::(anonymous namespace)::tile_kernel<16, 2, 3, false>(basp::TileDesc)"
     copy = "__amd_rocclr_copyBuffer"
     cal_kib = bench.CALIB_BYTES / 1024
-    # the fetch counter reads half of everything, the write counter all of it
     spin = "void at::cuda::(anonymous namespace)::spin_kernel(long)"
     # the fetch counter reads half of everything, the write counter all of it;
     # only launches between the two markers count
@@ -64,7 +63,6 @@ def test_json_line_contract():
     the roofline of the fused kernel against the 8 TB/s peak (no GPU: fake
     measurements through the same assembly code)."""
     import types
-    import bench
     args = bench.parse_args([])
     sb, hb = 402653184, 268435456
     r = {"value": 6300.0, "ms_per_step": 0.1065, "rotate_sets": 5, "step_bytes": sb + hb,
