@@ -226,8 +226,12 @@ def run_gpu(args):
         "timed_launches_per_kernel": len(sampled),
         "s2h_avg_us": s2h_avg * 1e6,
         "s2h_median_us": statistics.median(s2h_t) * 1e6,
+        "s2h_min_us": min(s2h_t) * 1e6,
+        "s2h_max_us": max(s2h_t) * 1e6,
         "h2s_avg_us": statistics.mean(h2s_t) * 1e6,
         "h2s_median_us": statistics.median(h2s_t) * 1e6,
+        "h2s_min_us": min(h2s_t) * 1e6,
+        "h2s_max_us": max(h2s_t) * 1e6,
         "s2h_bytes": w.s2h_bytes,
         "h2s_bytes": w.h2s_bytes,
         "s2h_gbs": rate(w.s2h_bytes, s2h_avg),
@@ -618,7 +622,8 @@ def make_line(args, r, w, traffic):
                      "achieved": r["s2h_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": r["s2h_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": r["s2h_bytes"], "avg_launch_us": r["s2h_avg_us"],
-                     "timed_launches": r["timed_launches_per_kernel"]},
+                     "median_launch_us": r.get("s2h_median_us"), "min_launch_us": r.get("s2h_min_us"),
+                     "max_launch_us": r.get("s2h_max_us"), "timed_launches": r["timed_launches_per_kernel"]},
         "copy_ceiling": {
             "kernel": "basp_stream_copy (16-byte loads/stores, same cache policy, read once, written once)",
             "s2h_bytes_gbs": r["copy_ceiling"][str(r["s2h_bytes"])]["gbs"],
@@ -630,7 +635,9 @@ def make_line(args, r, w, traffic):
                                   s2h_frac_of_copy=r["s2h_gbs"] / r["copy_loop"]["s2h_bytes_gbs"],
                                   h2s_frac_of_copy=r["h2s_gbs"] / r["copy_loop"]["h2s_bytes_gbs"])},
         "head_to_seq": {"achieved": r["h2s_gbs"], "frac": r["h2s_gbs"] / HBM_PEAK_GBS,
-                        "avg_launch_us": r["h2s_avg_us"], "bytes_per_launch": r["h2s_bytes"]},
+                        "avg_launch_us": r["h2s_avg_us"], "median_launch_us": r.get("h2s_median_us"),
+                        "min_launch_us": r.get("h2s_min_us"), "max_launch_us": r.get("h2s_max_us"),
+                        "bytes_per_launch": r["h2s_bytes"]},
         "round_trip_bit_exact": r["round_trip_bit_exact"],
     }
     return line
