@@ -659,3 +659,43 @@ def test_random_shapes_and_tunings(seed):
     print("random case", seed, shape, mode, layout, tuning, flush=True)
     run_s2h(shape, mode, dtype, layout, tuning)
     run_h2s(shape, mode, dtype, layout, tuning)
+
+
+def _wrapped_tags(n):
+    """int32 tensor whose element i holds the low 32 bits of i: distinct for
+    n <= 2^32, built on the device in two ranges."""
+    x = torch.empty(n, dtype=torch.int32, device="cuda")
+    half = min(n, 1 << 31)
+    x[:half] = torch.arange(0, half, dtype=torch.int32, device="cuda")
+    if n > half:
+        x[half:] = torch.arange(-(1 << 31), -(1 << 31) + (n - half), dtype=torch.int32, device="cuda")
+    return x
+
+
+def test_row_index_limit_sampled():
+    """Tile bases are 32-bit row indices: a tensor of 2^32 - 4 rows (the most
+    a plan allows is 2^32 - 1), moved in both directions, checked on sampled
+    destinations (including the last rows) against the oracle's one-element
+    source index."""
+    needs_gpu()
+    N, B, S, H, d = 2, 1, (1 << 31) - 2, 2, 1
+    print("row index limit", N, B, S, H, d, flush=True)
+    plan = b.basp_plan_create(N, B, S, H, H, d, b.BASP_INT32, 0)
+    n = plan.info["q_elems"]
+    assert n == (1 << 32) - 4
+    x = _wrapped_tags(n)
+    out = torch.empty(n, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(11)
+    for direction in (0, 1):
+        out.fill_(-1)
+        if direction == 0:
+            b.basp_seq_to_head_o(plan, x, out)
+        else:
+            b.basp_head_to_seq(plan, x, out)
+        torch.cuda.synchronize()
+        dst = _sample(n, rng, [n - 1 - i for i in range(64)] + [(1 << 31) + i - 32 for i in range(64)])
+        got = out[torch.from_numpy(dst).cuda()].cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+        want = oracle.source_index(direction, dst, 0, N, B, S, H, d) & 0xFFFFFFFF
+        assert np.array_equal(got, want), "direction %d" % direction
+    del x, out
+    torch.cuda.empty_cache()
