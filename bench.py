@@ -84,7 +84,8 @@ def parse_args(argv=None):
                     help="keep the built-in launch shapes instead of measuring them per plan")
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="skip the table of every named workload")
-    ap.add_argument("--workload-iters", type=int, default=30)
+    ap.add_argument("--workload-steps", type=int, default=60,
+                    help="back-to-back steps per workload in the table of every workload")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -264,7 +265,7 @@ def run_gpu(args):
     if not args.no_detail:
         res["detail"] = detail(args, b, w)
     if not args.no_workloads:
-        res["workloads"] = workload_table(b, args.workload_iters, not args.no_autotune)
+        res["workloads"] = workload_table(b, args.workload_steps, not args.no_autotune)
     res["tuning"] = {"seq_to_head": b.basp_plan_get_tuning(plan, b.BASP_SEQ_TO_HEAD),
                      "head_to_seq": b.basp_plan_get_tuning(plan, b.BASP_HEAD_TO_SEQ),
                      "autotuned": not args.no_autotune}
@@ -293,46 +294,51 @@ def copy_ceiling(b, moved, n):
     return out
 
 
-def copy_loop(b, s_bytes, h_bytes, steps, every):
-    """basp_stream_copy at the two kernels' byte counts run the way the timed
-    region runs the kernels: back to back on rotating buffers, with the
-    launches of every `every`-th step timed by their own events.  Returns the
-    step rate and the sampled launches' average rates."""
+def loop_rates(b, s_fn, h_fn, R, steps, every):
+    """Run steps of s_fn(i) then h_fn(i) back to back on rotating sets i % R,
+    as the timed region runs the kernels, with the launches of every
+    `every`-th step timed by their own events.  Returns the wall seconds per
+    step and the sampled launches' average seconds."""
     import torch
-    R = max(2, -(-(3 << 30) // (s_bytes + h_bytes)))
-    bufs = [(torch.empty(s_bytes // 2, dtype=torch.uint8, device="cuda"),
-             torch.empty(s_bytes // 2, dtype=torch.uint8, device="cuda"),
-             torch.empty(h_bytes // 2, dtype=torch.uint8, device="cuda"),
-             torch.empty(h_bytes // 2, dtype=torch.uint8, device="cuda")) for _ in range(R)]
-
-    def step(i):
-        a, c, e, f = bufs[i % R]
-        b.basp_stream_copy(c, a)
-        b.basp_stream_copy(f, e)
-
-    for i in range(10):
-        step(i)
+    for i in range(min(R, 10)):
+        s_fn(i % R)
+        h_fn(i % R)
     sampled = list(range(0, steps, every))
     ev = make_events(4 * len(sampled) + 2)
     ev[-2].record()
     for i in range(steps):
         if i % every == 0:
             j = i // every
-            a, c, e, f = bufs[i % R]
             b.basp_time_next_call(ev[4 * j], ev[4 * j + 1])
-            b.basp_stream_copy(c, a)
+            s_fn(i % R)
             b.basp_time_next_call(ev[4 * j + 2], ev[4 * j + 3])
-            b.basp_stream_copy(f, e)
+            h_fn(i % R)
         else:
-            step(i)
+            s_fn(i % R)
+            h_fn(i % R)
     ev[-1].record()
     torch.cuda.synchronize()
-    wall = ev[-2].elapsed_time(ev[-1]) * 1e-3
+    wall = ev[-2].elapsed_time(ev[-1]) * 1e-3 / steps
     s_t = statistics.mean(ev[4 * j].elapsed_time(ev[4 * j + 1]) * 1e-3 for j in range(len(sampled)))
     h_t = statistics.mean(ev[4 * j + 2].elapsed_time(ev[4 * j + 3]) * 1e-3 for j in range(len(sampled)))
+    return wall, s_t, h_t
+
+
+def copy_loop(b, s_bytes, h_bytes, steps, every):
+    """basp_stream_copy at the two kernels' byte counts run the way the timed
+    region runs the kernels (loop_rates).  Returns the step rate and the
+    sampled launches' average rates."""
+    import torch
+    R = max(2, -(-(3 << 30) // (s_bytes + h_bytes)))
+    bufs = [(torch.empty(s_bytes // 2, dtype=torch.uint8, device="cuda"),
+             torch.empty(s_bytes // 2, dtype=torch.uint8, device="cuda"),
+             torch.empty(h_bytes // 2, dtype=torch.uint8, device="cuda"),
+             torch.empty(h_bytes // 2, dtype=torch.uint8, device="cuda")) for _ in range(R)]
+    wall, s_t, h_t = loop_rates(b, lambda i: b.basp_stream_copy(bufs[i][1], bufs[i][0]),
+                                lambda i: b.basp_stream_copy(bufs[i][3], bufs[i][2]), R, steps, every)
     del bufs
     torch.cuda.empty_cache()
-    return {"step_gbs": rate(s_bytes + h_bytes, wall / steps), "s2h_bytes_gbs": rate(s_bytes, s_t),
+    return {"step_gbs": rate(s_bytes + h_bytes, wall), "s2h_bytes_gbs": rate(s_bytes, s_t),
             "h2s_bytes_gbs": rate(h_bytes, h_t), "steps": steps}
 
 
@@ -435,9 +441,12 @@ def detail(args, b, w):
     return out
 
 
-def workload_table(b, iters, autotune):
+def workload_table(b, steps, autotune):
     """Fused seq->head and head->seq rates of every named workload in both
-    modes (device-filled random bf16: the rate does not depend on values)."""
+    modes (device-filled random bf16: the rate does not depend on values),
+    measured as the timed region measures them: `steps` back-to-back steps
+    with every 5th step's launches sampled (loop_rates).  Once per workload,
+    the plain copy pair at the same byte counts, run the same way."""
     import torch
     from sequence_re_layout_amd import workloads
     out = {}
@@ -458,23 +467,25 @@ def workload_table(b, iters, autotune):
             if autotune:
                 b.basp_plan_autotune(p, sets[0]["q"], sets[0]["k"], sets[0]["v"], sets[0]["out"],
                                      sets[0]["o"], sets[0]["o_out"])
-            t = statistics.median(time_launches(b, lambda j: b.basp_seq_to_head(
-                p, sets[j]["q"], sets[j]["k"], sets[j]["v"], sets[j]["out"]), iters, R))
-            u = statistics.median(time_launches(b, lambda j: b.basp_head_to_seq(
-                p, sets[j]["o"], sets[j]["o_out"]), iters, R))
+            wall, t, u = loop_rates(
+                b, lambda j: b.basp_seq_to_head(p, sets[j]["q"], sets[j]["k"], sets[j]["v"], sets[j]["out"]),
+                lambda j: b.basp_head_to_seq(p, sets[j]["o"], sets[j]["o_out"]), R, steps, 5)
             out[name][mode] = {
                 "G": i["G"], "P": i["P"], "Bl": i["Bl"], "peers_per_rank": i["peers_per_rank"],
+                "step_gbs": rate(i["qkv_bytes_moved"] + i["o_bytes_moved"], wall),
                 "s2h_bytes": i["qkv_bytes_moved"], "s2h_us": t * 1e6,
                 "s2h_gbs": rate(i["qkv_bytes_moved"], t), "s2h_frac": rate(i["qkv_bytes_moved"], t) / HBM_PEAK_GBS,
                 "h2s_bytes": i["o_bytes_moved"], "h2s_us": u * 1e6,
-                "h2s_gbs": rate(i["o_bytes_moved"], u), "h2s_frac": rate(i["o_bytes_moved"], u) / HBM_PEAK_GBS}
-            if mode == "basp":   # both modes move the same bytes: one copy per workload
+                "h2s_gbs": rate(i["o_bytes_moved"], u), "h2s_frac": rate(i["o_bytes_moved"], u) / HBM_PEAK_GBS,
+                "launch_shape": {"seq_to_head": b.basp_plan_get_tuning(p, b.BASP_SEQ_TO_HEAD),
+                                 "head_to_seq": b.basp_plan_get_tuning(p, b.BASP_HEAD_TO_SEQ)}}
+            if mode == "basp":   # both modes move the same bytes: one copy pair per workload
                 qkv_b, o_b = i["qkv_bytes_moved"] // 2, i["o_bytes_moved"] // 2
-                tc = statistics.median(time_launches(b, lambda j: b.basp_stream_copy(
-                    sets[j]["out"], sets[j]["x"], qkv_b), iters, R))
-                uc = statistics.median(time_launches(b, lambda j: b.basp_stream_copy(
-                    sets[j]["o_out"], sets[j]["x"], o_b), iters, R))
-                out[name]["copy"] = {"s2h_bytes_gbs": rate(2 * qkv_b, tc), "h2s_bytes_gbs": rate(2 * o_b, uc)}
+                cw, tc, uc = loop_rates(b, lambda j: b.basp_stream_copy(sets[j]["out"], sets[j]["x"], qkv_b),
+                                        lambda j: b.basp_stream_copy(sets[j]["o_out"], sets[j]["x"], o_b),
+                                        R, steps, 5)
+                out[name]["copy"] = {"s2h_bytes_gbs": rate(2 * qkv_b, tc), "h2s_bytes_gbs": rate(2 * o_b, uc),
+                                     "step_gbs": rate(2 * (qkv_b + o_b), cw)}
             del sets
             torch.cuda.empty_cache()
     return out

@@ -281,9 +281,10 @@ basp_status basp_plan_get_tuning(const basp_plan *plan, basp_direction dir, basp
  * is timed for seq->head on (q, k, v -> qkv) and for head->seq on
  * (o -> o_out), in rounds that alternate the two directions, each timed
  * launch right after an untimed launch of the other direction with the
- * plan's shape on entry (as the two run back to back in a step), and the
- * shape with the lowest median time in each direction is stored in the
- * plan, replacing its tuning.  The buffers are those of basp_seq_to_head and
+ * plan's shape on entry (as the two run back to back in a step).  The best
+ * three shapes of each direction are then paired, every pair is timed as
+ * whole back-to-back steps, and the pair with the lowest median step time
+ * is stored in the plan, replacing its tuning.  The buffers are those of basp_seq_to_head and
  * basp_head_to_seq, with the same checks; qkv and o_out are overwritten.
  * Runs on stream and waits for it; creates and destroys HIP events but
  * allocates no device memory.  A pending basp_time_next_call request is

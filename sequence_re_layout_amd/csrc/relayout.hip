@@ -477,6 +477,56 @@ bool measure_rounds(basp_plan &p, const std::vector<basp_tuning> &cands,
     return true;
 }
 
+// Median seconds per step, over `rounds` rounds, of each pair (seq->head
+// shape, head->seq shape): kSteps steps run back to back, timed by events
+// recorded only before the first and after the last launch.  False on a
+// HIP error; a pair whose shapes the plan rejects gets a time < 0.
+bool measure_pairs(basp_plan &p, const std::vector<basp_tuning> &cands,
+                   const std::vector<std::pair<int, int>> &pairs, int rounds, std::vector<float> &med,
+                   const void *q, const void *k, const void *v, void *qkv, const void *o, void *o_out,
+                   void *stream, hipEvent_t *ev)
+{
+    constexpr int kSteps = 6;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    std::vector<std::vector<float>> times(pairs.size());
+    for (int r = 0; r < rounds; ++r)
+        for (size_t first = 0; first < pairs.size(); first += kPool) {
+            const size_t last = std::min(pairs.size(), first + kPool);
+            std::vector<bool> ran(last - first, false);
+            for (size_t i = first; i < last; ++i) {
+                p.tuning[BASP_SEQ_TO_HEAD] = cands[pairs[i].first];
+                p.tuning[BASP_HEAD_TO_SEQ] = cands[pairs[i].second];
+                TileLaunch ls, lh;
+                if (prepare_seq_to_head(p, q, k, v, qkv, ls) != BASP_OK ||
+                    prepare_head_to_seq(p, o, o_out, lh) != BASP_OK)
+                    continue;
+                if (hipEventRecord(ev[2 * (i - first)], st) != hipSuccess)
+                    return false;
+                for (int n = 0; n < kSteps; ++n)
+                    if (launch(ls, stream) != BASP_OK || launch(lh, stream) != BASP_OK)
+                        return false;
+                if (hipEventRecord(ev[2 * (i - first) + 1], st) != hipSuccess)
+                    return false;
+                ran[i - first] = true;
+            }
+            if (hipStreamSynchronize(st) != hipSuccess)
+                return false;
+            for (size_t i = first; i < last; ++i) {
+                float ms = -1.f;
+                if (ran[i - first] &&
+                    hipEventElapsedTime(&ms, ev[2 * (i - first)], ev[2 * (i - first) + 1]) != hipSuccess)
+                    return false;
+                times[i].push_back(ms / kSteps);
+            }
+        }
+    med.clear();
+    for (std::vector<float> &t : times) {
+        std::nth_element(t.begin(), t.begin() + t.size() / 2, t.end());
+        med.push_back(t[t.size() / 2]);
+    }
+    return true;
+}
+
 }  // namespace
 }  // namespace basp
 
@@ -497,7 +547,7 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
     if (s != BASP_OK || p->S == 0)
         return record(basp_status(s));
 
-    constexpr int kCoarse = 3, kFine = 7, kKeep = 6;
+    constexpr int kCoarse = 3, kFine = 7, kKeep = 6, kPairs = 3, kPairRounds = 5;
     hipEvent_t ev[2 * basp::kPool];
     int made = 0;
     for (; made < 2 * basp::kPool; ++made)
@@ -526,14 +576,36 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
             pick[dir].push_back(order[i].second);
     }
     ok = ok && basp::measure_rounds(*p, cands, pick, kFine, med, partner, q, k, v, qkv, o, o_out, stream, ev);
-    basp_tuning chosen[2] = {saved[0], saved[1]};
+    // the best few of each direction, then every pair of them timed as whole
+    // back-to-back steps: the shapes of the two directions affect each other
+    std::vector<int> top[2];
     for (int dir = 0; dir < 2 && ok; ++dir) {
-        int best = -1;
+        std::vector<std::pair<float, int>> order;
         for (size_t i = 0; i < pick[dir].size(); ++i)
-            if (med[dir][i] > 0.f && (best < 0 || med[dir][i] < med[dir][best]))
-                best = int(i);
-        if (best >= 0)
-            chosen[dir] = cands[pick[dir][best]];
+            if (med[dir][i] > 0.f)
+                order.push_back({med[dir][i], pick[dir][i]});
+        std::sort(order.begin(), order.end());
+        for (size_t i = 0; i < order.size() && int(i) < kPairs; ++i)
+            top[dir].push_back(order[i].second);
+    }
+    std::vector<std::pair<int, int>> pairs;
+    for (int a : top[0])
+        for (int c : top[1])
+            pairs.push_back({a, c});
+    std::vector<float> step;
+    ok = ok && basp::measure_pairs(*p, cands, pairs, kPairRounds, step, q, k, v, qkv, o, o_out, stream, ev);
+    basp_tuning chosen[2] = {saved[0], saved[1]};
+    int best = -1;
+    for (size_t i = 0; ok && i < pairs.size(); ++i)
+        if (step[i] > 0.f && (best < 0 || step[i] < step[best]))
+            best = int(i);
+    if (best >= 0) {
+        chosen[BASP_SEQ_TO_HEAD] = cands[pairs[best].first];
+        chosen[BASP_HEAD_TO_SEQ] = cands[pairs[best].second];
+    } else {   // no pair measured: each direction's own best, where it has one
+        for (int dir = 0; dir < 2; ++dir)
+            if (!top[dir].empty())
+                chosen[dir] = cands[top[dir][0]];
     }
     p->tuning[0] = chosen[0];
     p->tuning[1] = chosen[1];
