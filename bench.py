@@ -124,10 +124,13 @@ class Workload:
             s["o_out"] = torch.empty(i["q_elems"], dtype=torch.bfloat16, device="cuda")
             self.sets.append(s)
         torch.cuda.synchronize()
+        self.autotune_seconds = None
         if autotune:   # plan-time measurement, before anything is timed
             s = self.sets[0]
+            t0 = time.perf_counter()
             b.basp_plan_autotune(self.plan, s["q"], s["k"], s["v"], s["qkv_out"], s["o"], s["o_out"])
             torch.cuda.synchronize()
+            self.autotune_seconds = time.perf_counter() - t0
 
 
 def make_events(n):
@@ -268,7 +271,7 @@ def run_gpu(args):
         res["workloads"] = workload_table(b, args.workload_steps, not args.no_autotune)
     res["tuning"] = {"seq_to_head": b.basp_plan_get_tuning(plan, b.BASP_SEQ_TO_HEAD),
                      "head_to_seq": b.basp_plan_get_tuning(plan, b.BASP_HEAD_TO_SEQ),
-                     "autotuned": not args.no_autotune}
+                     "autotuned": not args.no_autotune, "autotune_seconds": w.autotune_seconds}
     res["w"] = w
     return res
 
