@@ -49,8 +49,11 @@
  * - stream is a hipStream_t passed as void*; NULL is the null stream.  Every
  *   call that launches work is asynchronous on that stream and does not
  *   synchronise.
- * - A plan is immutable host memory.  It may be used from several threads
- *   and streams at once.
+ * - A plan is host memory.  The re-layout and query calls only read it and
+ *   may use one plan from several threads and streams at once.  The calls
+ *   that change its launch shape (basp_plan_set_tuning,
+ *   basp_plan_set_direction_tuning, basp_plan_autotune) must not overlap any
+ *   other call on the same plan.
  * - Every call returns a basp_status (0 = BASP_OK) and also stores it for
  *   basp_last_error() in the calling thread.  Calls that return a pointer
  *   return NULL on error.
