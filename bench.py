@@ -25,8 +25,9 @@ three-pass baseline, the backward entry points, the token-major layout and
 torch's device copy; ``workloads`` the fused seq->head and head->seq rates of
 every named workload in both modes.  ``copy_ceiling`` is basp_stream_copy,
 a plain copy with the kernels' access rules, at the same byte counts: the
-rate a read-once, write-once kernel reaches on this part.  ``cpu_baseline`` is the CPU oracle
-doing the same step on the host, repeated for about --cpu-seconds.
+rate a read-once, write-once kernel reaches on this part.  ``cpu_baseline``
+is the CPU oracle doing the same step on the host, repeated for about
+--cpu-seconds.
 
     python bench.py --pmc-summary FETCH_DIR WRITE_DIR
 
