@@ -287,8 +287,10 @@ basp_status basp_plan_get_tuning(const basp_plan *plan, basp_direction dir, basp
  * plan's shape on entry (as the two run back to back in a step).  The best
  * three shapes of each direction are then paired, every pair is timed as
  * whole back-to-back steps, and the pair with the lowest median step time
- * is stored in the plan, replacing its tuning.  The buffers are those of basp_seq_to_head and
- * basp_head_to_seq, with the same checks; qkv and o_out are overwritten.
+ * is stored in the plan, replacing its tuning.  The buffers are those of
+ * basp_seq_to_head and basp_head_to_seq, with the same checks.  Every
+ * candidate computes the same re-layout, so on BASP_OK qkv and o_out hold
+ * the results of the two calls.
  * Runs on stream and waits for it; creates and destroys HIP events but
  * allocates no device memory.  A pending basp_time_next_call request is
  * dropped.  Errors as for the two calls; on BASP_ERR_HIP the plan keeps its
