@@ -86,7 +86,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="skip the table of every named workload")
     ap.add_argument("--workload-steps", type=int, default=60,
-                    help="back-to-back steps per workload in the table of every workload")
+                    help="least launches per HIP graph in the table of every workload")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -445,12 +445,37 @@ def detail(args, b, w):
     return out
 
 
+def graph_seconds(fn, calls, reps=5):
+    """Seconds per call of `calls` back-to-back calls fn(i), captured once in a
+    HIP graph so that no host gap falls between the kernels (a small call runs
+    for less time than a Python call takes); median over `reps` replays."""
+    import torch
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(calls):
+            fn(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    start, stop = make_events(2)
+    t = []
+    for _ in range(reps):
+        start.record()
+        graph.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        t.append(start.elapsed_time(stop) * 1e-3 / calls)
+    del graph
+    return statistics.median(t)
+
+
 def workload_table(b, steps, autotune):
     """Fused seq->head and head->seq rates of every named workload in both
-    modes (device-filled random bf16: the rate does not depend on values),
-    measured as the timed region measures them: `steps` back-to-back steps
-    with every 5th step's launches sampled (loop_rates).  Once per workload,
-    the plain copy pair at the same byte counts, run the same way."""
+    modes (device-filled random bf16: the rate does not depend on values).
+    Each rate is a HIP graph of back-to-back launches on rotating buffer sets
+    (graph_seconds): whole steps, then each direction alone; at least `steps`
+    launches per graph, more for small calls.  Once per workload, the plain
+    copy pair at the same byte counts, run the same way."""
     import torch
     from sequence_re_layout_amd import workloads
     out = {}
@@ -459,7 +484,9 @@ def workload_table(b, steps, autotune):
         for mode, code in (("basp", b.BASP_MODE_BASP), ("ulysses", b.BASP_MODE_ULYSSES)):
             p = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, code)
             i = p.info
-            R = max(2, -(-(3 << 30) // (i["qkv_bytes_moved"] + i["o_bytes_moved"])))
+            sb, hb = i["qkv_bytes_moved"], i["o_bytes_moved"]
+            R = max(2, -(-(3 << 30) // (sb + hb)))
+            n = max(steps, min(10 * steps, steps * (400 << 20) // sb))
             sets = []
             for _ in range(R):
                 x = torch.empty(2 * i["q_elems"] + 2 * i["kv_elems"], dtype=torch.bfloat16, device="cuda").normal_()
@@ -471,23 +498,35 @@ def workload_table(b, steps, autotune):
             if autotune:
                 b.basp_plan_autotune(p, sets[0]["q"], sets[0]["k"], sets[0]["v"], sets[0]["out"],
                                      sets[0]["o"], sets[0]["o_out"])
-            wall, t, u = loop_rates(
-                b, lambda j: b.basp_seq_to_head(p, sets[j]["q"], sets[j]["k"], sets[j]["v"], sets[j]["out"]),
-                lambda j: b.basp_head_to_seq(p, sets[j]["o"], sets[j]["o_out"]), R, steps, 5)
+
+            def s2h(j):
+                s = sets[j % R]
+                b.basp_seq_to_head(p, s["q"], s["k"], s["v"], s["out"])
+
+            def h2s(j):
+                s = sets[j % R]
+                b.basp_head_to_seq(p, s["o"], s["o_out"])
+
+            wall = graph_seconds(lambda j: (s2h(j), h2s(j)), n)
+            t, u = graph_seconds(s2h, n), graph_seconds(h2s, n)
             out[name][mode] = {
                 "G": i["G"], "P": i["P"], "Bl": i["Bl"], "peers_per_rank": i["peers_per_rank"],
-                "step_gbs": rate(i["qkv_bytes_moved"] + i["o_bytes_moved"], wall),
-                "s2h_bytes": i["qkv_bytes_moved"], "s2h_us": t * 1e6,
-                "s2h_gbs": rate(i["qkv_bytes_moved"], t), "s2h_frac": rate(i["qkv_bytes_moved"], t) / HBM_PEAK_GBS,
-                "h2s_bytes": i["o_bytes_moved"], "h2s_us": u * 1e6,
-                "h2s_gbs": rate(i["o_bytes_moved"], u), "h2s_frac": rate(i["o_bytes_moved"], u) / HBM_PEAK_GBS,
+                "launches_per_graph": n, "step_gbs": rate(sb + hb, wall),
+                "s2h_bytes": sb, "s2h_us": t * 1e6, "s2h_gbs": rate(sb, t), "s2h_frac": rate(sb, t) / HBM_PEAK_GBS,
+                "h2s_bytes": hb, "h2s_us": u * 1e6, "h2s_gbs": rate(hb, u), "h2s_frac": rate(hb, u) / HBM_PEAK_GBS,
                 "launch_shape": {"seq_to_head": b.basp_plan_get_tuning(p, b.BASP_SEQ_TO_HEAD),
                                  "head_to_seq": b.basp_plan_get_tuning(p, b.BASP_HEAD_TO_SEQ)}}
             if mode == "basp":   # both modes move the same bytes: one copy pair per workload
-                qkv_b, o_b = i["qkv_bytes_moved"] // 2, i["o_bytes_moved"] // 2
-                cw, tc, uc = loop_rates(b, lambda j: b.basp_stream_copy(sets[j]["out"], sets[j]["x"], qkv_b),
-                                        lambda j: b.basp_stream_copy(sets[j]["o_out"], sets[j]["x"], o_b),
-                                        R, steps, 5)
+                qkv_b, o_b = sb // 2, hb // 2
+
+                def cs(j):
+                    b.basp_stream_copy(sets[j % R]["out"], sets[j % R]["x"], qkv_b)
+
+                def ch(j):
+                    b.basp_stream_copy(sets[j % R]["o_out"], sets[j % R]["x"], o_b)
+
+                cw = graph_seconds(lambda j: (cs(j), ch(j)), n)
+                tc, uc = graph_seconds(cs, n), graph_seconds(ch, n)
                 out[name]["copy"] = {"s2h_bytes_gbs": rate(2 * qkv_b, tc), "h2s_bytes_gbs": rate(2 * o_b, uc),
                                      "step_gbs": rate(2 * (qkv_b + o_b), cw)}
             del sets

@@ -280,19 +280,21 @@ basp_status basp_plan_get_tuning(const basp_plan *plan, basp_direction dir, basp
 
 /*
  * Choose the launch shape of both directions by measurement on the caller's
- * buffers (as a planner that times candidates): a fixed set of launch shapes
- * is timed for seq->head on (q, k, v -> qkv) and for head->seq on
- * (o -> o_out), in rounds that alternate the two directions, each timed
- * launch right after an untimed launch of the other direction with the
- * plan's shape on entry (as the two run back to back in a step).  The best
- * three shapes of each direction are then paired, every pair is timed as
- * whole back-to-back steps, and the pair with the lowest median step time
- * is stored in the plan, replacing its tuning.  The buffers are those of
- * basp_seq_to_head and basp_head_to_seq, with the same checks.  Every
- * candidate computes the same re-layout, so on BASP_OK qkv and o_out hold
- * the results of the two calls.
- * Runs on stream and waits for it; creates and destroys HIP events but
- * allocates no device memory.  A pending basp_time_next_call request is
+ * buffers (as a planner that times candidates).  A fixed set of launch
+ * shapes (larger when the fused seq->head call moves at most 64 MiB: 4 and
+ * 8 vectors per lane as well as 1 and 2) is timed for seq->head on
+ * (q, k, v -> qkv) and for head->seq on (o -> o_out), in rounds that
+ * alternate the two directions, each timed launch right after an untimed
+ * launch of the other direction with the plan's shape on entry (as the two
+ * run back to back in a step).  The best three shapes of each direction are
+ * then paired, and every pair is timed as whole back-to-back steps, together
+ * with the pair of the plan's shapes on entry.  The pair with the lowest
+ * median step time is stored in the plan, replacing its tuning (the shapes
+ * on entry stay when they win).  The buffers are those of basp_seq_to_head
+ * and basp_head_to_seq, with the same checks.  Every candidate computes the
+ * same re-layout, so on BASP_OK qkv and o_out hold the results of the two
+ * calls.  Runs on stream and waits for it; creates and destroys HIP events
+ * but allocates no device memory.  A pending basp_time_next_call request is
  * dropped.  Errors as for the two calls; on BASP_ERR_HIP the plan keeps its
  * previous tuning.  The plan must not be used by another thread meanwhile.
  */

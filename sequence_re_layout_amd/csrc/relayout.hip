@@ -363,22 +363,28 @@ basp_status timed_call(F f)
 // non-temporal device-scope stores (the policy the sweeps preferred), over
 // batch order x work-group size (64, 128, 256) x tile order x vectors per
 // lane x heads per tile x XCD order, each direct with both lane orders and
-// LDS-staged.
-std::vector<basp_tuning> autotune_candidates()
+// LDS-staged.  Vectors per lane: 1 and 2, and also 4 and 8 when the fused
+// seq->head call moves at most kWideVectorBytes: only such small calls ran
+// faster with the larger tiles (fewer work-groups to dispatch), and their
+// launches are short, so measuring the extra shapes costs little.
+constexpr int64_t kWideVectorBytes = int64_t{64} << 20;
+
+std::vector<basp_tuning> autotune_candidates(const basp_plan &p)
 {
     std::vector<basp_tuning> c;
-    const int blocks[] = {64, 128, 256}, heads[] = {1, 2, 4, 8};
+    const int blocks[] = {64, 128, 256}, heads[] = {1, 2, 4, 8}, vpts[] = {1, 2, 4, 8};
+    const int nvpt = 2 * (p.q_elems + 2 * p.kv_elems) * p.es <= kWideVectorBytes ? 4 : 2;
     for (int bo = 1; bo <= 2; ++bo)
         for (int block : blocks)
             for (int to = 1; to <= 2; ++to)
-                for (int vpt = 1; vpt <= 2; ++vpt)
+                for (int iv = 0; iv < nvpt; ++iv)
                     for (int th : heads)
                         for (int xcd = 1; xcd <= 2; ++xcd) {
                             basp_tuning t = {};
                             t.batch_order = bo;
                             t.block_size = block;
                             t.tile_order = to;
-                            t.vectors_per_thread = vpt;
+                            t.vectors_per_thread = vpts[iv];
                             t.tile_heads = th;
                             t.xcd_remap = xcd;
                             t.cache_policy = 4;
@@ -555,7 +561,7 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
             break;
     const basp_tuning saved[2] = {p->tuning[0], p->tuning[1]};
     bool ok = made == 2 * basp::kPool;
-    const std::vector<basp_tuning> cands = basp::autotune_candidates();
+    const std::vector<basp_tuning> cands = basp::autotune_candidates(*p);
     std::vector<int> pick[2];
     for (int dir = 0; dir < 2; ++dir)
         for (int i = 0; i < int(cands.size()); ++i)
@@ -588,20 +594,27 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
         for (size_t i = 0; i < order.size() && int(i) < kPairs; ++i)
             top[dir].push_back(order[i].second);
     }
+    // the plan's shapes on entry compete as one more pair, so that a pick
+    // which the single-launch rounds misjudged cannot replace a faster pair
+    std::vector<basp_tuning> shapes = cands;
+    shapes.push_back(saved[BASP_SEQ_TO_HEAD]);
+    shapes.push_back(saved[BASP_HEAD_TO_SEQ]);
+    const int entry = int(cands.size());
     std::vector<std::pair<int, int>> pairs;
     for (int a : top[0])
         for (int c : top[1])
             pairs.push_back({a, c});
+    pairs.push_back({entry, entry + 1});
     std::vector<float> step;
-    ok = ok && basp::measure_pairs(*p, cands, pairs, kPairRounds, step, q, k, v, qkv, o, o_out, stream, ev);
+    ok = ok && basp::measure_pairs(*p, shapes, pairs, kPairRounds, step, q, k, v, qkv, o, o_out, stream, ev);
     basp_tuning chosen[2] = {saved[0], saved[1]};
     int best = -1;
     for (size_t i = 0; ok && i < pairs.size(); ++i)
         if (step[i] > 0.f && (best < 0 || step[i] < step[best]))
             best = int(i);
     if (best >= 0) {
-        chosen[BASP_SEQ_TO_HEAD] = cands[pairs[best].first];
-        chosen[BASP_HEAD_TO_SEQ] = cands[pairs[best].second];
+        chosen[BASP_SEQ_TO_HEAD] = shapes[pairs[best].first];
+        chosen[BASP_HEAD_TO_SEQ] = shapes[pairs[best].second];
     } else {   // no pair measured: each direction's own best, where it has one
         for (int dir = 0; dir < 2; ++dir)
             if (!top[dir].empty())
