@@ -243,6 +243,15 @@ def _torch_dtype(code):
             BASP_FP32: torch.float32, BASP_INT32: torch.int32}[code]
 
 
+def _check_device(x, name: str) -> None:
+    """The library launches on the current device: a tensor elsewhere is an
+    error, not a cross-device access."""
+    import torch
+    if x.device.index != torch.cuda.current_device():
+        raise ValueError("%s is on %s, the current device is cuda:%d"
+                         % (name, x.device, torch.cuda.current_device()))
+
+
 def _ptr(x, plan: Plan, numel: int, name: str):
     """Device address of a tensor checked against the plan, or an int as is."""
     if x is None:
@@ -253,6 +262,7 @@ def _ptr(x, plan: Plan, numel: int, name: str):
         raise TypeError("%s: dtype %s does not match the plan" % (name, x.dtype))
     if not x.is_cuda:
         raise ValueError("%s must be a device tensor" % name)
+    _check_device(x, name)
     if not x.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     if x.numel() != numel:
@@ -304,6 +314,7 @@ def basp_seq_to_head_unfused(plan: Plan, q, k, v, out, ws, stream=None) -> None:
     if ws is not None and not isinstance(ws, int):
         if not ws.is_cuda or not ws.is_contiguous():
             raise ValueError("ws must be a contiguous device tensor")
+        _check_device(ws, "ws")
         if ws.numel() * ws.element_size() < basp_unfused_workspace_bytes(plan):
             raise ValueError("ws holds %d bytes, the plan needs %d"
                              % (ws.numel() * ws.element_size(), basp_unfused_workspace_bytes(plan)))
@@ -323,9 +334,12 @@ def basp_stream_copy(dst, src, nbytes=None, stream=None) -> None:
             return x
         if not x.is_cuda or not x.is_contiguous():
             raise ValueError("%s must be a contiguous device tensor" % name)
+        _check_device(x, name)
         return x.data_ptr()
 
     if nbytes is None:
+        if isinstance(src, int) or src is None:
+            raise ValueError("nbytes is needed when src is a raw address")
         nbytes = src.numel() * src.element_size()
     for x, name in ((dst, "dst"), (src, "src")):
         if not isinstance(x, int) and x is not None and x.numel() * x.element_size() < nbytes:

@@ -197,6 +197,14 @@ def test_stream_copy_checks_before_launch():
     assert b.basp_last_error() == b.BASP_ERR_UNSUPPORTED
 
 
+def test_binding_copy_needs_a_byte_count_for_raw_addresses():
+    """With raw addresses the binding cannot infer the size: it raises
+    before calling the library."""
+    base = 1 << 40
+    with pytest.raises(ValueError, match="nbytes"):
+        b.basp_stream_copy(base + (1 << 20), base)
+
+
 def test_row_count_limit():
     """Tile bases are 32-bit row indices: a tensor of 2^32 or more rows
     (B*S*max(Hq, Hkv)) is rejected at plan creation, 2^32 - 8 is not."""
