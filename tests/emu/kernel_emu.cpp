@@ -3,7 +3,8 @@
 // It compiles the library's own launch planning (launch.cpp), plan code
 // (plan.cpp) and per-lane index arithmetic (launch.hpp) with g++, then runs
 // every launch on the host: each work-group's tile loop, each lane's vector
-// offsets, and each vector access as a memcpy under the rule of the raw
+// offsets (of the masked lanes past a tile's last vector, the first and the
+// last), and each vector access as a memcpy under the rule of the raw
 // buffer descriptors (an access is performed only when it lies inside the
 // descriptor's range).  A lane that the kernel treats as present but whose
 // access falls outside its descriptor is counted in *bad: a correct plan
@@ -78,7 +79,15 @@ void run(const TileLaunch &L, uint64_t *bad)
             const uint32_t nvec = sg.Ts.d * sg.Th.d * D.A.d;
             const uint32_t step = L.block * L.vpt;
             const uint32_t vend = (nvec + step - 1) / step * step;
-            for (uint32_t v = 0; v < vend; ++v) {
+            // lanes of the last pass past the tile's vectors must be masked;
+            // the mask's first term (v < Ts*Th*A) is monotonic in v, so the
+            // first and the last such lane stand for all of them
+            for (uint32_t v : {nvec, vend - 1}) {
+                uint32_t so, ho;
+                if (v >= nvec && v < vend && lane_offsets(D, sg, o.ns, o.nh, v, L.vw, so, ho))
+                    ++*bad;
+            }
+            for (uint32_t v = 0; v < nvec; ++v) {
                 uint32_t so, ho;
                 if (!lane_offsets(D, sg, o.ns, o.nh, v, L.vw, so, ho))
                     continue;

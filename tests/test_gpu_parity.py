@@ -231,6 +231,21 @@ def test_degenerate(shape, mode):
         run_h2s(shape, mode, "int32", layout)
 
 
+@pytest.mark.parametrize("shape,mode", [
+    ((1, 65535, 3, 2, 1, 8), "basp"),             # data-parallel fallback: 65535 batch indices along z
+    ((5, 65535, 5, 5, 5, 8), "ulysses"),          # z = 65535, y = 5 members
+    ((4096, 1, 4096, 4096, 4096, 1), "ulysses"),  # 4096 members along y, 2-byte rows
+], ids=["z65535-dp", "z65535-ulysses", "y4096-ulysses"])
+def test_grid_limits(shape, mode):
+    """The launch grid at its extents (the largest batch count the grid's z
+    coordinate takes; thousands of members along y), with the batch index
+    along z or folded into x."""
+    needs_gpu()
+    for tuning in (None, {"batch_order": 2}):
+        run_s2h(shape, mode, "bf16", 0, tuning)
+        run_h2s(shape, mode, "bf16", 0, tuning)
+
+
 def test_b1_basp_equals_ulysses():
     needs_gpu()
     shape = (8, 1, 8192, 32, 8, 64)

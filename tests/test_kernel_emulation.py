@@ -254,3 +254,20 @@ def test_random_shapes_and_tunings(emu, seed):
     for es in (2, 4):
         check_s2h(emu, shape, m, layout, es, tuning)
         check_h2s(emu, shape, m, layout, es, tuning)
+
+
+GRID_LIMITS = [  # (N, B, S, Hq, Hkv, d), mode
+    ((1, 65535, 3, 2, 1, 8), 1),            # data-parallel fallback: 65535 batch indices along z
+    ((5, 65535, 5, 5, 5, 8), 0),            # Ulysses: z = 65535, y = 5 members
+    ((4096, 1, 4096, 4096, 4096, 1), 0),    # Ulysses: 4096 members along y, 2-byte rows
+]
+
+
+@pytest.mark.parametrize("shape,mode", GRID_LIMITS, ids=lambda x: "x".join(map(str, x)) if isinstance(x, tuple) else str(x))
+def test_grid_limits(emu, shape, mode):
+    """The launch grid at its extents: the largest batch count the grid's z
+    coordinate takes, and thousands of group members along y, with the batch
+    index along z or folded into x."""
+    for tuning in (None, {"batch_order": 2}):
+        check_s2h(emu, shape, mode, 0, 2, tuning)
+        check_h2s(emu, shape, mode, 0, 2, tuning)
