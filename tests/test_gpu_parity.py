@@ -154,6 +154,61 @@ def test_tiny_int32_tagged(mode):
     run_h2s(shape, mode, dtype="int32")
 
 
+def _pack(t, b, s, h, e):
+    """(tensor, b, s, h, e) in bit fields of an int32: e bits 0-7, h 8-15,
+    s 16-27, b 28, tensor 29-30 (fields wide enough for the tiny shape)."""
+    return (t << 29) | (b << 28) | (s << 16) | (h << 8) | e
+
+
+def _seq_tags(t, N, B, S, H, d, G, P, Bl):
+    """Sequence-sharded buffer [N][Bl][St][H][d]: rank r = g*P + j holds
+    sequences g*Bl + bl and tokens j*St + t."""
+    St = S // P
+    r, bl, tt, h, e = np.indices((N, Bl, St, H, d), dtype=np.int64)
+    return _pack(t, (r // P) * Bl + bl, (r % P) * St + tt, h, e).astype(np.int32).ravel()
+
+
+def _head_tags(t, N, B, S, H, d, G, P, Bl, layout):
+    """Head-sharded buffer [N][Bl][Hl][S][d] (or [N][Bl][S][Hl][d]): rank
+    r = g*P + j holds sequences g*Bl + bl and heads j*Hl + hl."""
+    Hl = H // P
+    if layout == 0:
+        r, bl, hl, s, e = np.indices((N, Bl, Hl, S, d), dtype=np.int64)
+    else:
+        r, bl, s, hl, e = np.indices((N, Bl, S, Hl, d), dtype=np.int64)
+    return _pack(t, (r // P) * Bl + bl, s, (r % P) * Hl + hl, e).astype(np.int32).ravel()
+
+
+@pytest.mark.parametrize("layout", [0, 1], ids=["head_major", "token_major"])
+@pytest.mark.parametrize("mode", ["basp", "ulysses"])
+def test_tiny_tags_decode(mode, layout):
+    """Every element of the tiny workload's Q/K/V/O carries its own (tensor,
+    b, s, h, e) in bit fields; after the GPU re-layout each output position
+    must hold the element the ownership rules put there (checked field by
+    field from the layout definitions, independently of the oracle)."""
+    needs_gpu()
+    N, B, S, Hq, Hkv, d = workloads.TINY[1:]
+    plan = b.basp_plan_create_ex(N, B, S, Hq, Hkv, d, b.BASP_INT32, MODE[mode], layout)
+    i = plan.info
+    G, P, Bl = i["G"], i["P"], i["Bl"]
+    ins = [torch.from_numpy(_seq_tags(t, N, B, S, H, d, G, P, Bl)).cuda()
+           for t, H in ((0, Hq), (1, Hkv), (2, Hkv))]
+    out = torch.full((i["qkv_elems"],), -1, dtype=torch.int32, device="cuda")
+    b.basp_seq_to_head(plan, *ins, out)
+    o = torch.from_numpy(_head_tags(3, N, B, S, Hq, d, G, P, Bl, layout)).cuda()
+    back = torch.full((i["q_elems"],), -1, dtype=torch.int32, device="cuda")
+    b.basp_head_to_seq(plan, o, back)
+    torch.cuda.synchronize()
+    want = np.concatenate([_head_tags(t, N, B, S, H, d, G, P, Bl, layout)
+                           for t, H in ((0, Hq), (1, Hkv), (2, Hkv))])
+    got = out.cpu().numpy()
+    for name, shift, mask in (("tensor", 29, 3), ("b", 28, 1), ("s", 16, 0xfff), ("h", 8, 0xff), ("e", 0, 0xff)):
+        bad = np.flatnonzero(((got >> shift) & mask) != ((want >> shift) & mask))
+        assert bad.size == 0, "seq->head: field %s wrong at %s" % (name, bad[:8])
+    want_back = _seq_tags(3, N, B, S, Hq, d, G, P, Bl)
+    assert np.array_equal(back.cpu().numpy(), want_back), "head->seq: tags out of place"
+
+
 # -------------------------------------------------- ragged, tunings, dtypes --
 
 RAGGED = [  # N, B, S, Hq, Hkv, d
