@@ -243,7 +243,8 @@ basp_status basp_seq_to_head_unfused(const basp_plan *plan, const void *q, const
  *                        run along the source's contiguous axis, stores along
  *                        the destination's (used with 16-byte vectors and
  *                        tiles of one pass of the work-group)
- *   block_size           threads per work-group: 64, 128 or 256 (built-in)
+ *   block_size           threads per work-group: 64, 128 or 256 (built-in
+ *                        256)
  *   batch_order          1 = the batch indices one after another (built-in),
  *                        2 = batch indices interleaved with the tiles, so
  *                        that neighbouring work-groups alternate sequences
