@@ -28,7 +28,7 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     from sequence_re_layout_amd import binding as b
-else:  # collected off the GPU machine: every test here is skipped
+else:  # collected on a machine without a GPU: every test here is skipped
     b = None
 
 MODE = {"basp": 1, "ulysses": 0}
