@@ -266,15 +266,27 @@ def run_gpu(args):
     torch.cuda.synchronize()
     del cal_src, cal_dst
 
+    # the legs after the timed region are reported, not required: an error in
+    # one is recorded in its place and the line is still printed
     if not args.no_detail:
-        res["detail"] = detail(args, b, w)
+        res["detail"] = optional_leg(lambda: detail(args, b, w))
     if not args.no_workloads:
-        res["workloads"] = workload_table(b, args.workload_steps, not args.no_autotune)
+        res["workloads"] = optional_leg(lambda: workload_table(b, args.workload_steps, not args.no_autotune))
     res["tuning"] = {"seq_to_head": b.basp_plan_get_tuning(plan, b.BASP_SEQ_TO_HEAD),
                      "head_to_seq": b.basp_plan_get_tuning(plan, b.BASP_HEAD_TO_SEQ),
                      "autotuned": not args.no_autotune, "autotune_seconds": w.autotune_seconds}
     res["w"] = w
     return res
+
+
+def optional_leg(fn):
+    """fn(), or {"error": ...} when it raises (after reporting it on stderr)."""
+    try:
+        return fn()
+    except Exception as e:   # noqa: BLE001 -- recorded in the JSON line
+        import traceback
+        traceback.print_exc()
+        return {"error": "%s: %s" % (type(e).__name__, e)}
 
 
 def copy_ceiling(b, moved, n):
@@ -720,7 +732,7 @@ def main(argv=None):
     if "workloads" in r:
         line["workloads"] = r["workloads"]
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args, w)
+        line["cpu_baseline"] = optional_leg(lambda: cpu_baseline(args, w))
     print(json.dumps(line), flush=True)
     return 0
 

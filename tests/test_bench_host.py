@@ -86,3 +86,13 @@ def test_json_line_contract():
     assert line["copy_ceiling"]["in_timed_loop"]["step_frac_of_copy"] == 6300.0 / 6620.0
     json.dumps(line)   # serialisable
 
+
+
+def test_optional_leg_records_errors(capsys):
+    """A leg after the timed region that raises is recorded in the JSON line
+    instead of ending the run; one that works is returned as is."""
+    assert bench.optional_leg(lambda: {"x": 1}) == {"x": 1}
+    out = bench.optional_leg(lambda: 1 / 0)
+    assert out == {"error": "ZeroDivisionError: division by zero"}
+    assert "ZeroDivisionError" in capsys.readouterr().err
+    json.dumps(out)
