@@ -489,6 +489,15 @@ def test_timed_call_records_kernel_time_and_keeps_results():
     torch.cuda.synchronize()
     assert ev[0].elapsed_time(ev[1]) > 0
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    # a call that fails its checks also consumes the request
+    before = ev[2].elapsed_time(ev[3])
+    b.basp_time_next_call(ev[2], ev[3])
+    lib = b.library()
+    assert lib.basp_seq_to_head(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                out.data_ptr() + 1, None) == b.BASP_ERR_ALIGN
+    b.basp_seq_to_head(plan, q, k, v, out)
+    torch.cuda.synchronize()
+    assert ev[2].elapsed_time(ev[3]) == before
 
 
 @pytest.mark.parametrize("shape,mode", [(workloads.LLAMA_1B[1:], 1), ((6, 3, 6 * 37, 12, 6, 40), 0)],
