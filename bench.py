@@ -594,15 +594,17 @@ def cpu_model():
 
 # ------------------------------------------------------------ roofline ---
 
-def traffic_bytes(workload):
+def traffic_bytes(workload, mode):
     """HBM bytes per fused seq->head launch from committed PMC counters, or
-    None when they are missing or were taken on other kernel sources."""
+    None when they are missing, were taken on other kernel sources, or on
+    another workload or mode."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sources_sha256") != kernel_sources_sha256() or t.get("workload") != workload:
+    if (t.get("kernel_sources_sha256") != kernel_sources_sha256() or t.get("workload") != workload
+            or t.get("mode") != mode):
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -713,7 +715,8 @@ def main(argv=None):
     args = parse_args(argv)
     if args.pmc_summary:
         res = pmc_summary(*args.pmc_summary)
-        res["workload"] = parse_args([]).workload
+        defaults = parse_args([])   # the counter runs use the default workload and mode
+        res["workload"], res["mode"] = defaults.workload, defaults.mode
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(res, f, indent=1)
         print(json.dumps(res))
@@ -726,7 +729,7 @@ def main(argv=None):
 
     r = run_gpu(args)
     w = r.pop("w")
-    line = make_line(args, r, w, traffic_bytes(w.name))
+    line = make_line(args, r, w, traffic_bytes(w.name, w.mode))
     if "detail" in r:
         line["detail"] = r["detail"]
     if "workloads" in r:

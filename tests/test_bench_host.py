@@ -48,14 +48,15 @@ def test_pmc_summary_scales_by_the_copy(tmp_path):
 def test_traffic_only_for_matching_sources_and_workload(tmp_path, monkeypatch):
     path = tmp_path / "t.json"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
-    assert bench.traffic_bytes("w") is None
-    path.write_text(json.dumps({"workload": "w", "kernel_sources_sha256": bench.kernel_sources_sha256(),
+    assert bench.traffic_bytes("w", "basp") is None
+    path.write_text(json.dumps({"workload": "w", "mode": "basp", "kernel_sources_sha256": bench.kernel_sources_sha256(),
                                 "traffic_bytes_per_launch": 123.0}))
-    assert bench.traffic_bytes("w") == 123.0
-    assert bench.traffic_bytes("other") is None
-    path.write_text(json.dumps({"workload": "w", "kernel_sources_sha256": "0" * 64,
+    assert bench.traffic_bytes("w", "basp") == 123.0
+    assert bench.traffic_bytes("other", "basp") is None
+    assert bench.traffic_bytes("w", "ulysses") is None   # counters of the other mode
+    path.write_text(json.dumps({"workload": "w", "mode": "basp", "kernel_sources_sha256": "0" * 64,
                                 "traffic_bytes_per_launch": 123.0}))
-    assert bench.traffic_bytes("w") is None
+    assert bench.traffic_bytes("w", "basp") is None
 
 
 def test_json_line_contract():
