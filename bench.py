@@ -178,6 +178,9 @@ def run_gpu(args):
     from sequence_re_layout_amd import binding as b
 
     torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    device = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+              "compute_units": props.multi_processor_count, "memory_bytes": props.total_memory}
     w = Workload(b, args.workload, args.mode, args.rotate, not args.no_autotune)
     plan, sets = w.plan, w.sets
 
@@ -276,6 +279,7 @@ def run_gpu(args):
                      "head_to_seq": b.basp_plan_get_tuning(plan, b.BASP_HEAD_TO_SEQ),
                      "autotuned": not args.no_autotune, "autotune_seconds": w.autotune_seconds}
     res["w"] = w
+    res["device"] = device
     return res
 
 
@@ -551,6 +555,8 @@ def workload_table(b, steps, autotune):
 def cpu_baseline(args, w):
     """The oracle doing one step (fused Q/K/V seq->head, O head->seq) on the
     host bytes of the same workload, repeated for about --cpu-seconds."""
+    import numpy as np
+
     import oracle
     from sequence_re_layout_amd import inputs
     N, B, S, Hq, Hkv, d = w.shape
@@ -565,6 +571,15 @@ def cpu_baseline(args, w):
         spent += (time.perf_counter_ns() - t0) * 1e-9
         reps += 1
     step_bytes = w.s2h_bytes + w.h2s_bytes
+    # for information: the same step as one NumPy transpose per tensor
+    reps_np, spent_np = 0, 0.0
+    while reps_np == 0 or spent_np < args.cpu_seconds / 4:
+        t0 = time.perf_counter_ns()
+        np.concatenate([oracle.numpy_seq_to_head(x, mode, N, B, S, H, d)
+                        for x, H in ((q, Hq), (k, Hkv), (v, Hkv))])
+        oracle.numpy_head_to_seq(o, mode, N, B, S, Hq, d)
+        spent_np += (time.perf_counter_ns() - t0) * 1e-9
+        reps_np += 1
     # the same loop on one thread, for a shorter while
     reps1, spent1 = 0, 0.0
     while reps1 == 0 or spent1 < args.cpu_seconds / 4:
@@ -578,7 +593,10 @@ def cpu_baseline(args, w):
                       "%.1f s on the host, OpenMP over destination blocks" % (reps, spent),
             "seconds_per_step": spent / reps, "cpu_model": cpu_model(),
             "one_thread": {"value": rate(step_bytes * reps1, spent1), "unit": "GB/s",
-                           "seconds_per_step": spent1 / reps1, "steps": reps1}}
+                           "seconds_per_step": spent1 / reps1, "steps": reps1},
+            "numpy_transpose": {"value": rate(step_bytes * reps_np, spent_np), "unit": "GB/s",
+                                "seconds_per_step": spent_np / reps_np, "steps": reps_np,
+                                "note": "the same step as one NumPy transpose per tensor, for information"}}
 
 
 def cpu_model():
@@ -708,6 +726,8 @@ def make_line(args, r, w, traffic):
                         "bytes_per_launch": r["h2s_bytes"]},
         "round_trip_bit_exact": r["round_trip_bit_exact"],
     }
+    if "device" in r:
+        line["device"] = r["device"]
     return line
 
 

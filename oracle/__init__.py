@@ -138,3 +138,43 @@ def head_to_seq_qkv(x, mode, N, B, S, Hq, Hkv, d, layout=HEAD_MAJOR, threads=Non
     return (head_to_seq(x[:nq], mode, N, B, S, Hq, d, layout, threads=threads),
             head_to_seq(x[nq:nq + nkv], mode, N, B, S, Hkv, d, layout, threads=threads),
             head_to_seq(x[nq + nkv:], mode, N, B, S, Hkv, d, layout, threads=threads))
+
+
+# ---------------------------------------------------------------- NumPy ---
+# The same two re-layouts as one NumPy transpose each, for the benchmark's
+# CPU comparison only (timing information; the element loop above is the
+# oracle).  tests/test_oracle_pins.py checks them against the element loop.
+#
+# With G groups of P members and St = S/P, Hl = H/P (readings R1-R3 above):
+#   sequence-sharded buffer  (g, js, bl, t, jh, hl, e)   shape (G, P, Bl, St, P, Hl, d)
+#   head-major buffer        (g, jh, bl, hl, js, t, e)   shape (G, P, Bl, Hl, P, St, d)
+#   token-major buffer       (g, jh, bl, js, t, hl, e)   shape (G, P, Bl, P, St, Hl, d)
+# where member js holds tokens js*St + t and member jh holds heads jh*Hl + hl.
+
+def _numpy_shapes(mode, N, B, S, H, d):
+    gpb = groups(mode, N, B)
+    if gpb is None or S % gpb[1] or H % gpb[1]:
+        raise ValueError("the pages' conditions do not hold for mode=%d N=%d B=%d S=%d H=%d"
+                         % (mode, N, B, S, H))
+    G, P, Bl = gpb
+    return G, P, Bl, S // P, H // P
+
+
+def numpy_seq_to_head(x, mode, N, B, S, H, d, layout=HEAD_MAJOR):
+    """Sequence-sharded -> head-sharded as one transpose of the rank-major buffer."""
+    G, P, Bl, St, Hl = _numpy_shapes(mode, N, B, S, H, d)
+    a = np.asarray(x).reshape(G, P, Bl, St, P, Hl, d)
+    axes = (0, 4, 2, 5, 1, 3, 6) if layout == HEAD_MAJOR else (0, 4, 2, 1, 3, 5, 6)
+    return np.ascontiguousarray(a.transpose(axes)).reshape(-1)
+
+
+def numpy_head_to_seq(x, mode, N, B, S, H, d, layout=HEAD_MAJOR):
+    """Head-sharded -> sequence-sharded, the inverse transpose."""
+    G, P, Bl, St, Hl = _numpy_shapes(mode, N, B, S, H, d)
+    if layout == HEAD_MAJOR:
+        a = np.asarray(x).reshape(G, P, Bl, Hl, P, St, d)
+        axes = (0, 4, 2, 5, 1, 3, 6)
+    else:
+        a = np.asarray(x).reshape(G, P, Bl, P, St, Hl, d)
+        axes = (0, 3, 2, 4, 1, 5, 6)
+    return np.ascontiguousarray(a.transpose(axes)).reshape(-1)

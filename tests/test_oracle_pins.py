@@ -85,3 +85,21 @@ def test_page_facts():
     pb, tok, _ = _observed(BASP, f["N"], f["B"], f["S"], H=2, d=1)
     assert set(pb.values()) == {f["peers_basp"]}
     assert set(tok.values()) == {f["tokens_per_gpu_S"]}
+
+
+@pytest.mark.parametrize("mode", [ULYSSES, BASP], ids=["ulysses", "basp"])
+@pytest.mark.parametrize("layout", [oracle.HEAD_MAJOR, oracle.TOKEN_MAJOR], ids=["head_major", "token_major"])
+def test_numpy_transpose_forms_match_the_element_loop(mode, layout):
+    """The NumPy transpose forms the benchmark times for comparison compute
+    the same permutation as the element loop, both directions."""
+    rng = np.random.default_rng(7)
+    for (N, B, S, H, d) in [(8, 2, 32, 8, 4), (6, 3, 18, 12, 3), (4, 8, 4, 4, 2), (1, 3, 5, 2, 3),
+                            (8, 1, 16, 16, 2), (2, 4, 6, 2, 5)]:
+        gpb = oracle.groups(mode, N, B)
+        if gpb is None or S % gpb[1] or H % gpb[1]:
+            continue
+        x = rng.integers(0, 1 << 16, size=B * S * H * d, dtype=np.uint16)
+        assert np.array_equal(oracle.numpy_seq_to_head(x, mode, N, B, S, H, d, layout),
+                              oracle.seq_to_head(x, mode, N, B, S, H, d, layout))
+        assert np.array_equal(oracle.numpy_head_to_seq(x, mode, N, B, S, H, d, layout),
+                              oracle.head_to_seq(x, mode, N, B, S, H, d, layout))
