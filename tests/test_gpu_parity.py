@@ -543,6 +543,56 @@ def _sample(n, rng, extra=()):
     return np.unique(np.array(pts, dtype=np.int64))
 
 
+def _check_sampled(out, ins, heads, direction, mode, N, B, S, d, rng):
+    """out (one buffer: the parts of ins re-laid one after another) against
+    the oracle's one-element source index on sampled destinations, bit for
+    bit, gathered on the device."""
+    o16 = out.view(torch.int16)
+    base = 0
+    for x, H in zip(ins, heads):
+        n = x.numel()
+        dst = _sample(n, rng)
+        src = oracle.source_index(direction, dst, mode, N, B, S, H, d)
+        got = o16[torch.from_numpy(dst + base).cuda()]
+        want = x.view(torch.int16)[torch.from_numpy(src).cuda()]
+        assert torch.equal(got, want), "part at element offset %d" % base
+        base += n
+
+
+@pytest.mark.parametrize("mode", ["basp", "ulysses"])
+@pytest.mark.parametrize("w", workloads.ALL + workloads.EXTRA, ids=lambda w: w[0])
+def test_workload_autotuned_sampled(w, mode):
+    """Every named workload with the launch shapes autotune picks for it, as
+    the bench's table of every workload runs it: the outputs autotune leaves
+    and a fresh call of each direction, checked on sampled destinations
+    against the oracle's one-element source index."""
+    needs_gpu()
+    _, N, B, S, Hq, Hkv, d = w
+    print("autotuned", w[0], mode, flush=True)
+    m = MODE[mode]
+    plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, m)
+    i = plan.info
+    g = torch.Generator(device="cuda").manual_seed(5)
+    q, k, v, o = (torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+                  for n in (i["q_elems"], i["kv_elems"], i["kv_elems"], i["q_elems"]))
+    qkv = torch.empty(i["qkv_elems"], dtype=torch.bfloat16, device="cuda")
+    o_out = torch.empty(i["q_elems"], dtype=torch.bfloat16, device="cuda")
+    b.basp_plan_autotune(plan, q, k, v, qkv, o, o_out)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(13)
+    _check_sampled(qkv, (q, k, v), (Hq, Hkv, Hkv), 0, m, N, B, S, d, rng)
+    _check_sampled(o_out, (o,), (Hq,), 1, m, N, B, S, d, rng)
+    qkv.view(torch.int16).fill_(-1)
+    o_out.view(torch.int16).fill_(-1)
+    b.basp_seq_to_head(plan, q, k, v, qkv)
+    b.basp_head_to_seq(plan, o, o_out)
+    torch.cuda.synchronize()
+    _check_sampled(qkv, (q, k, v), (Hq, Hkv, Hkv), 0, m, N, B, S, d, rng)
+    _check_sampled(o_out, (o,), (Hq,), 1, m, N, B, S, d, rng)
+    del q, k, v, o, qkv, o_out
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("mode,layout", [(1, 0), (0, 0), (1, 1)], ids=["basp", "ulysses", "basp-token-major"])
 def test_beyond_4gib_sampled(mode, layout):
     """Buffers larger than 2^31 and 2^32 bytes (int32, S = 98304): the fused
