@@ -1,40 +1,48 @@
 #!/usr/bin/env python3
 """Benchmark of the BASP attention-boundary re-layout on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--mode basp|ulysses]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Workload: by default the largest named attention shape that fits one GPU,
+Llama-3.2-3B-shaped at S = 32768 (N = 8 virtual ranks, B = 2, Hq = 24,
+Hkv = 8, d = 128, bf16): 1.34 GB moved per fused seq->head call.
 
 One step is one pass of the attention-boundary re-layout of a layer: the
 fused Q/K/V seq->head exchange before attention and the O head->seq exchange
-after it, on the Llama-3.2-1B-shaped workload by default (N = 8 virtual
-ranks, B = 2, S = 16384, Hq = 32, Hkv = 8, d = 64, bf16, BASP mode: 2 groups
-of K = 4).  Inputs are seeded synthetic N(0, 1) bf16 values resident in HBM
-before timing starts; R buffer sets rotate so that no step finds its bytes in
-the 256 MB Infinity Cache.  Each plan's launch shapes are chosen by
-basp_plan_autotune before anything is timed (--no-autotune keeps the
-built-in ones).
+after it.  Inputs are one seeded global tensor per activation (Q, K, V, O:
+N(0, 1) bf16 from seeds 0-3), scattered into each mode's own rank-sharded
+buffers before timing, so BASP and Ulysses re-lay the same logical tensors.
+R buffer sets rotate so that no step finds its bytes in the 256 MB Infinity
+Cache.  Launch shapes come from the measured table
+``sequence_re_layout_amd/launch_shapes.json`` (``--autotune`` measures them
+anew with ``basp_plan_autotune``).
 
-Printed: one JSON line.  ``value`` is effective HBM GB/s of the whole step
-(algorithmic bytes: every input byte read once, every output byte written
-once) over wall time of K steps bracketed by device synchronisation.
-``roofline`` is the fused seq->head kernel (the larger of the two) against
-the 8 TB/s HBM peak, its duration taken from HIP events that its own launch
-records (hipExtLaunchKernel start/stop timestamps, via basp_time_next_call)
-on the stream it runs on, on every --sample-every'th step of the timed
-region.  ``detail`` holds per-kernel rates of both modes, the unfused
-three-pass baseline, the backward entry points, the token-major layout and
-torch's device copy; ``workloads`` the fused seq->head and head->seq rates of
-every named workload in both modes.  ``copy_ceiling`` is basp_stream_copy,
-a plain copy with the kernels' access rules, at the same byte counts: the
-rate a read-once, write-once kernel reaches on this part.  ``cpu_baseline``
-is the CPU oracle doing the same step on the host, repeated for about
---cpu-seconds.
+Timing.  K steps of the headline mode (BASP) are timed by wall clock between
+device synchronisations (``ms_per_step``).  The kernels of every 10th step
+carry start/stop events recorded by their own dispatches
+(``basp_time_next_call``, hipExtLaunchKernel timestamps on the stream they
+run on); the loop goes on past the K steps, the same way, until at least
+--min-launches launches of each kernel are sampled.  ``value`` and
+``roofline.achieved`` are the fused seq->head call's algorithmic bytes over
+its average sampled duration.  Ulysses runs the same loop on its own
+buffers; ``basp_vs_ulysses`` gives both modes and both directions.
 
+Printed: one compact JSON line (last line of stdout).  Everything else --
+the per-mode detail, the unfused three-pass baseline, the backward entries,
+the token-major layout, the general-G plans, torch's device copy and the
+table of every named workload -- goes to --detail-out.
+
+Other modes:
+
+    python bench.py --tune-shapes OUT.json
+        measure the launch-shape table (every named workload, both modes)
     python bench.py --pmc-summary FETCH_DIR WRITE_DIR
-
-reads the CSV output of two ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc
-WRITE_SIZE`` runs of this script and writes ``profiles/pmc_traffic.json``
-(HBM bytes per launch of the fused kernel, scaled by the same counters on a
-plain copy of known size).
+        HBM bytes per launch from two rocprofv3 counter runs of this script,
+        scaled by the same counters on a plain copy of known size, into
+        profiles/pmc_traffic.json
+    python bench.py --trace-summary TRACE_DIR
+        per-mode average kernel durations of a rocprofv3 kernel trace of
+        this script (the sampled loops, found by their marker kernels)
 """
 from __future__ import annotations
 
@@ -59,7 +67,9 @@ KERNEL_SOURCES = ["sequence_re_layout_amd/csrc/relayout.hip", "sequence_re_layou
                   "sequence_re_layout_amd/csrc/launch.cpp", "sequence_re_layout_amd/csrc/fastdiv.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 CALIB_BYTES = 256 << 20   # plain copy used to scale the PMC byte counters
-MARKER_CYCLES = 1000      # torch's spin kernel, brackets the timed region
+MARKER_CYCLES = 1000      # torch's spin kernel: brackets each mode's sampled loop
+DEFAULT_WORKLOAD = "llama3.2-3b_s32k_b2"
+MODES = ("basp", "ulysses")
 
 
 def kernel_sources_sha256() -> str:
@@ -73,66 +83,119 @@ def kernel_sources_sha256() -> str:
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sample-every", type=int, default=10,
-                    help="time the kernels of every n-th timed step with their own events")
-    ap.add_argument("--workload", default="llama3.2-1b_s16k_b2")
-    ap.add_argument("--mode", choices=["basp", "ulysses"], default="basp")
+                    help="time the kernels of every n-th step with their own events")
+    ap.add_argument("--min-launches", type=int, default=50,
+                    help="least sampled launches per kernel and mode (the loop continues past --steps)")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough for > 1 GiB reuse distance)")
-    ap.add_argument("--detail-iters", type=int, default=100)
-    ap.add_argument("--no-autotune", action="store_true",
-                    help="keep the built-in launch shapes instead of measuring them per plan")
+    ap.add_argument("--autotune", action="store_true",
+                    help="measure launch shapes per plan instead of reading the table")
+    ap.add_argument("--builtin-shapes", action="store_true", help="the library's built-in launch shapes")
+    ap.add_argument("--detail-out", default=os.path.join("gpurun_out", "bench_detail.json"))
+    ap.add_argument("--detail-iters", type=int, default=60)
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="skip the table of every named workload")
     ap.add_argument("--workload-steps", type=int, default=60,
                     help="least launches per HIP graph in the table of every workload")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tune-shapes", metavar="OUT")
+    ap.add_argument("--tune-autotunes", type=int, default=3, help="autotune runs per plan for --tune-shapes")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR")
     return ap.parse_args(argv)
 
 
-# ------------------------------------------------------------------ GPU ---
+def rate(nbytes, seconds):
+    return nbytes / seconds / 1e9
 
-class Workload:
-    """Device buffers of one workload: R rotating sets of Q/K/V/out and
-    O/out, filled from the same seeded host data."""
 
-    def __init__(self, b, name, mode, rotate, autotune=True):
+# ------------------------------------------------------------- inputs ---
+
+def scatter_seq(x, G, P, Bl, S, H, d):
+    """Sequence-sharded buffer of a global [B][S][H][d] tensor: rank (g, j)
+    holds sequences [g*Bl, (g+1)*Bl) and tokens [j*St, (j+1)*St), as
+    [Bl][St][H][d], ranks in order.  (Input preparation: a reshape and a
+    permute of the global tensor.)"""
+    return x.view(G, Bl, P, S // P, H, d).permute(0, 2, 1, 3, 4, 5).contiguous().view(-1)
+
+
+def scatter_head(x, G, P, Bl, S, H, d):
+    """Head-sharded (head-major) buffer of a global [B][S][H][d] tensor: rank
+    (g, j) holds sequences [g*Bl, (g+1)*Bl) and heads [j*Hl, (j+1)*Hl), as
+    [Bl][Hl][S][d], ranks in order."""
+    return x.view(G, Bl, S, P, H // P, d).permute(0, 3, 1, 4, 2, 5).contiguous().view(-1)
+
+
+class Inputs:
+    """The global Q, K, V, O tensors of a workload on the host: N(0, 1)
+    bf16 from seeds 0, 1, 2, 3."""
+
+    def __init__(self, shape):
+        from sequence_re_layout_amd import inputs
+        N, B, S, Hq, Hkv, d = shape
+        self.x = {"q": inputs.normal_bf16(B * S * Hq * d, inputs.SEED_Q).view(B, S, Hq, d),
+                  "k": inputs.normal_bf16(B * S * Hkv * d, inputs.SEED_K).view(B, S, Hkv, d),
+                  "v": inputs.normal_bf16(B * S * Hkv * d, inputs.SEED_V).view(B, S, Hkv, d),
+                  "o": inputs.normal_bf16(B * S * Hq * d, inputs.SEED_O).view(B, S, Hq, d)}
+
+
+class ModeRun:
+    """Plan and R rotating device buffer sets of one mode: q, k, v
+    sequence-sharded and o head-sharded, scattered from the same global
+    tensors, plus the two outputs."""
+
+    def __init__(self, b, name, shape, mode, inp, rotate, shapes):
         import torch
-        from sequence_re_layout_amd import inputs, workloads
-        self.name, N, B, S, Hq, Hkv, d = workloads.BY_NAME[name]
-        self.shape = (N, B, S, Hq, Hkv, d)
-        self.mode = mode
+        from sequence_re_layout_amd import launch_shapes
+        N, B, S, Hq, Hkv, d = shape
+        self.name, self.shape, self.mode = name, shape, mode
         code = b.BASP_MODE_BASP if mode == "basp" else b.BASP_MODE_ULYSSES
         self.plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, code)
         i = self.plan.info
-        self.s2h_bytes = i["qkv_bytes_moved"]
-        self.h2s_bytes = i["o_bytes_moved"]
-        self.host = {
-            "q": inputs.normal_bf16(i["q_elems"], inputs.SEED_Q),
-            "k": inputs.normal_bf16(i["kv_elems"], inputs.SEED_K),
-            "v": inputs.normal_bf16(i["kv_elems"], inputs.SEED_V),
-            "o": inputs.normal_bf16(i["q_elems"], inputs.SEED_O),
+        G, P, Bl = i["G"], i["P"], i["Bl"]
+        self.s2h_bytes, self.h2s_bytes = i["qkv_bytes_moved"], i["o_bytes_moved"]
+        dev = {
+            "q": scatter_seq(inp.x["q"].cuda(), G, P, Bl, S, Hq, d),
+            "k": scatter_seq(inp.x["k"].cuda(), G, P, Bl, S, Hkv, d),
+            "v": scatter_seq(inp.x["v"].cuda(), G, P, Bl, S, Hkv, d),
+            "o": scatter_head(inp.x["o"].cuda(), G, P, Bl, S, Hq, d),
         }
-        set_bytes = self.s2h_bytes + self.h2s_bytes
-        self.R = rotate or max(2, -(-(3 << 30) // set_bytes))   # > 1 GiB between reuses
+        self.R = rotate or max(2, -(-(3 << 30) // (self.s2h_bytes + self.h2s_bytes)))
         self.sets = []
-        for _ in range(self.R):
-            s = {n: t.cuda() for n, t in self.host.items()}
+        for r in range(self.R):
+            s = {n: (t if r == 0 else t.clone()) for n, t in dev.items()}
             s["qkv_out"] = torch.empty(i["qkv_elems"], dtype=torch.bfloat16, device="cuda")
             s["o_out"] = torch.empty(i["q_elems"], dtype=torch.bfloat16, device="cuda")
             self.sets.append(s)
         torch.cuda.synchronize()
         self.autotune_seconds = None
-        if autotune:   # plan-time measurement, before anything is timed
+        self.shape_source = "built-in"
+        if shapes == "table" and launch_shapes.apply(b, self.plan, name, mode):
+            self.shape_source = "table"
+        elif shapes in ("table", "autotune"):
             s = self.sets[0]
             t0 = time.perf_counter()
             b.basp_plan_autotune(self.plan, s["q"], s["k"], s["v"], s["qkv_out"], s["o"], s["o_out"])
             torch.cuda.synchronize()
             self.autotune_seconds = time.perf_counter() - t0
+            self.shape_source = "autotuned"
+        self.tuning = {"seq_to_head": b.basp_plan_get_tuning(self.plan, b.BASP_SEQ_TO_HEAD),
+                       "head_to_seq": b.basp_plan_get_tuning(self.plan, b.BASP_HEAD_TO_SEQ)}
 
+    def s2h(self, b, i):
+        s = self.sets[i % self.R]
+        b.basp_seq_to_head(self.plan, s["q"], s["k"], s["v"], s["qkv_out"])
+
+    def h2s(self, b, i):
+        s = self.sets[i % self.R]
+        b.basp_head_to_seq(self.plan, s["o"], s["o_out"])
+
+
+# ------------------------------------------------------------- timing ---
 
 def make_events(n):
     """n timing events whose handles exist (torch creates them on first record)."""
@@ -144,9 +207,58 @@ def make_events(n):
     return ev
 
 
+def stats_us(t):
+    return {"avg_us": statistics.mean(t) * 1e6, "median_us": statistics.median(t) * 1e6,
+            "min_us": min(t) * 1e6, "max_us": max(t) * 1e6, "launches": len(t)}
+
+
+def step_loop(b, s_fn, h_fn, steps, warmup, every, min_launches, marker=True):
+    """Steps of s_fn(i) then h_fn(i) back to back.  The first `steps` steps
+    are timed by wall clock between device synchronisations; the launches of
+    every `every`-th step carry their own start/stop events; the loop goes on
+    the same way past `steps` until `min_launches` launches of each are
+    sampled.  A marker kernel before and after the sampled loop lets a
+    profiler trace find its launches.  Returns (wall seconds of the first
+    `steps` steps, sampled s_fn durations, sampled h_fn durations)."""
+    import torch
+    for i in range(warmup):
+        s_fn(i)
+        h_fn(i)
+    torch.cuda.synchronize()
+    every = max(1, every)
+    total = max(steps, every * max(1, min_launches))
+    nsamp = -(-total // every)
+    ev = make_events(4 * nsamp)
+    if marker:
+        torch.cuda._sleep(MARKER_CYCLES)
+    torch.cuda.synchronize()
+    wall = None
+    t0 = time.perf_counter()
+    for i in range(total):
+        if i == steps:
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        j = i // every if i % every == 0 else -1
+        if j >= 0:
+            b.basp_time_next_call(ev[4 * j], ev[4 * j + 1])
+        s_fn(i)
+        if j >= 0:
+            b.basp_time_next_call(ev[4 * j + 2], ev[4 * j + 3])
+        h_fn(i)
+    torch.cuda.synchronize()
+    if wall is None:
+        wall = time.perf_counter() - t0
+    if marker:
+        torch.cuda._sleep(MARKER_CYCLES)
+        torch.cuda.synchronize()
+    s_t = [ev[4 * j].elapsed_time(ev[4 * j + 1]) * 1e-3 for j in range(nsamp)]
+    h_t = [ev[4 * j + 2].elapsed_time(ev[4 * j + 3]) * 1e-3 for j in range(nsamp)]
+    return wall, s_t, h_t
+
+
 def time_launches(b, fn, n, rotate):
-    """Durations (s) of n calls of fn(set_index), each timed from its kernels'
-    own dispatch timestamps (basp_time_next_call) on the launch stream."""
+    """Durations (s) of n calls of fn(i), each timed alone from its kernels'
+    own dispatch timestamps (basp_time_next_call)."""
     import torch
     ev = make_events(2 * n)
     for i in range(n):
@@ -167,298 +279,6 @@ def time_torch(fn, n, rotate):
         ev[i][1].record()
     torch.cuda.synchronize()
     return [a.elapsed_time(z) * 1e-3 for a, z in ev]
-
-
-def rate(nbytes, seconds):
-    return nbytes / seconds / 1e9
-
-
-def run_gpu(args):
-    import torch
-    from sequence_re_layout_amd import binding as b
-
-    torch.cuda.set_device(0)
-    props = torch.cuda.get_device_properties(0)
-    device = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
-              "compute_units": props.multi_processor_count, "memory_bytes": props.total_memory}
-    w = Workload(b, args.workload, args.mode, args.rotate, not args.no_autotune)
-    plan, sets = w.plan, w.sets
-
-    def s2h(i):
-        s = sets[i]
-        b.basp_seq_to_head(plan, s["q"], s["k"], s["v"], s["qkv_out"])
-
-    def h2s(i):
-        s = sets[i]
-        b.basp_head_to_seq(plan, s["o"], s["o_out"])
-
-    for i in range(args.warmup):
-        s2h(i % w.R)
-        h2s(i % w.R)
-    torch.cuda.synchronize()
-
-    # timed region: K steps.  Every --sample-every'th step carries start/stop
-    # events recorded by its kernels' own dispatches (basp_time_next_call):
-    # such a launch costs the stream about 5 us more, so timing every launch
-    # would slow the step the bench reports.  A tiny marker kernel before and
-    # after the region lets a profiler trace find the timed launches among
-    # the plan-time measurements.
-    every = max(1, args.sample_every)
-    sampled = list(range(0, args.steps, every))
-    ev = make_events(4 * len(sampled))
-    torch.cuda._sleep(MARKER_CYCLES)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        j = i // every if i % every == 0 else -1
-        if j >= 0:
-            b.basp_time_next_call(ev[4 * j], ev[4 * j + 1])
-        s2h(i % w.R)
-        if j >= 0:
-            b.basp_time_next_call(ev[4 * j + 2], ev[4 * j + 3])
-        h2s(i % w.R)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    torch.cuda._sleep(MARKER_CYCLES)
-    s2h_t = [ev[4 * j].elapsed_time(ev[4 * j + 1]) * 1e-3 for j in range(len(sampled))]
-    h2s_t = [ev[4 * j + 2].elapsed_time(ev[4 * j + 3]) * 1e-3 for j in range(len(sampled))]
-
-    ms_per_step = wall / args.steps * 1e3
-    step_bytes = w.s2h_bytes + w.h2s_bytes
-    s2h_avg = statistics.mean(s2h_t)
-    res = {
-        "ms_per_step": ms_per_step,
-        "value": rate(step_bytes, wall / args.steps),
-        "step_bytes": step_bytes,
-        "rotate_sets": w.R,
-        "timed_launches_per_kernel": len(sampled),
-        "s2h_avg_us": s2h_avg * 1e6,
-        "s2h_median_us": statistics.median(s2h_t) * 1e6,
-        "s2h_min_us": min(s2h_t) * 1e6,
-        "s2h_max_us": max(s2h_t) * 1e6,
-        "h2s_avg_us": statistics.mean(h2s_t) * 1e6,
-        "h2s_median_us": statistics.median(h2s_t) * 1e6,
-        "h2s_min_us": min(h2s_t) * 1e6,
-        "h2s_max_us": max(h2s_t) * 1e6,
-        "s2h_bytes": w.s2h_bytes,
-        "h2s_bytes": w.h2s_bytes,
-        "s2h_gbs": rate(w.s2h_bytes, s2h_avg),
-        "h2s_gbs": rate(w.h2s_bytes, statistics.mean(h2s_t)),
-    }
-
-    # the ceiling: basp_stream_copy (a plain read-once/write-once copy with
-    # the same access rules) at the byte counts of the two kernels, timed the
-    # same way on rotating buffers: each launch alone, and as the timed
-    # region runs them (back to back, every --sample-every'th step sampled)
-    res["copy_ceiling"] = copy_ceiling(b, (w.s2h_bytes, w.h2s_bytes), 100)
-    res["copy_loop"] = copy_loop(b, w.s2h_bytes, w.h2s_bytes, 200, every)
-
-    # device round trip of the timed buffers: head->seq of the Q part of the
-    # fused output must give Q back bit for bit
-    s = sets[0]
-    back = torch.empty_like(s["q"])
-    b.basp_seq_to_head(plan, s["q"], s["k"], s["v"], s["qkv_out"])
-    b.basp_head_to_seq(plan, s["qkv_out"][: plan.info["q_elems"]], back)
-    torch.cuda.synchronize()
-    res["round_trip_bit_exact"] = bool(torch.equal(back.view(torch.int16), s["q"].view(torch.int16)))
-
-    # a plain copy of known size: the PMC byte counters are scaled by it
-    cal_src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
-    cal_dst = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
-    cal_dst.copy_(cal_src)
-    torch.cuda.synchronize()
-    del cal_src, cal_dst
-
-    # the legs after the timed region are reported, not required: an error in
-    # one is recorded in its place and the line is still printed
-    if not args.no_detail:
-        res["detail"] = optional_leg(lambda: detail(args, b, w))
-    if not args.no_workloads:
-        res["workloads"] = optional_leg(lambda: workload_table(b, args.workload_steps, not args.no_autotune))
-    res["tuning"] = {"seq_to_head": b.basp_plan_get_tuning(plan, b.BASP_SEQ_TO_HEAD),
-                     "head_to_seq": b.basp_plan_get_tuning(plan, b.BASP_HEAD_TO_SEQ),
-                     "autotuned": not args.no_autotune, "autotune_seconds": w.autotune_seconds}
-    res["w"] = w
-    res["device"] = device
-    return res
-
-
-def optional_leg(fn):
-    """fn(), or {"error": ...} when it raises (after reporting it on stderr)."""
-    try:
-        return fn()
-    except Exception as e:   # noqa: BLE001 -- recorded in the JSON line
-        import traceback
-        traceback.print_exc()
-        return {"error": "%s: %s" % (type(e).__name__, e)}
-
-
-def copy_ceiling(b, moved, n):
-    """Average duration and rate of basp_stream_copy moving each byte count
-    in `moved` (read + write: a copy of moved/2 bytes), n timed launches each
-    on buffer sets more than 1 GiB apart."""
-    import torch
-    out = {}
-    for m in moved:
-        nb = m // 2
-        R = max(2, -(-(3 << 30) // m))
-        src = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(R)]
-        dst = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(R)]
-        for i in range(R):
-            b.basp_stream_copy(dst[i], src[i])
-        t = time_launches(b, lambda i: b.basp_stream_copy(dst[i], src[i]), n, R)
-        out[str(m)] = {"bytes_moved": m, "avg_us": statistics.mean(t) * 1e6,
-                       "median_us": statistics.median(t) * 1e6, "gbs": rate(m, statistics.mean(t))}
-        del src, dst
-        torch.cuda.empty_cache()
-    return out
-
-
-def loop_rates(b, s_fn, h_fn, R, steps, every):
-    """Run steps of s_fn(i) then h_fn(i) back to back on rotating sets i % R,
-    as the timed region runs the kernels, with the launches of every
-    `every`-th step timed by their own events.  Returns the wall seconds per
-    step and the sampled launches' average seconds."""
-    import torch
-    for i in range(min(R, 10)):
-        s_fn(i % R)
-        h_fn(i % R)
-    sampled = list(range(0, steps, every))
-    ev = make_events(4 * len(sampled) + 2)
-    ev[-2].record()
-    for i in range(steps):
-        if i % every == 0:
-            j = i // every
-            b.basp_time_next_call(ev[4 * j], ev[4 * j + 1])
-            s_fn(i % R)
-            b.basp_time_next_call(ev[4 * j + 2], ev[4 * j + 3])
-            h_fn(i % R)
-        else:
-            s_fn(i % R)
-            h_fn(i % R)
-    ev[-1].record()
-    torch.cuda.synchronize()
-    wall = ev[-2].elapsed_time(ev[-1]) * 1e-3 / steps
-    s_t = statistics.mean(ev[4 * j].elapsed_time(ev[4 * j + 1]) * 1e-3 for j in range(len(sampled)))
-    h_t = statistics.mean(ev[4 * j + 2].elapsed_time(ev[4 * j + 3]) * 1e-3 for j in range(len(sampled)))
-    return wall, s_t, h_t
-
-
-def copy_loop(b, s_bytes, h_bytes, steps, every):
-    """basp_stream_copy at the two kernels' byte counts run the way the timed
-    region runs the kernels (loop_rates).  Returns the step rate and the
-    sampled launches' average rates."""
-    import torch
-    R = max(2, -(-(3 << 30) // (s_bytes + h_bytes)))
-    bufs = [(torch.empty(s_bytes // 2, dtype=torch.uint8, device="cuda"),
-             torch.empty(s_bytes // 2, dtype=torch.uint8, device="cuda"),
-             torch.empty(h_bytes // 2, dtype=torch.uint8, device="cuda"),
-             torch.empty(h_bytes // 2, dtype=torch.uint8, device="cuda")) for _ in range(R)]
-    wall, s_t, h_t = loop_rates(b, lambda i: b.basp_stream_copy(bufs[i][1], bufs[i][0]),
-                                lambda i: b.basp_stream_copy(bufs[i][3], bufs[i][2]), R, steps, every)
-    del bufs
-    torch.cuda.empty_cache()
-    return {"step_gbs": rate(s_bytes + h_bytes, wall), "s2h_bytes_gbs": rate(s_bytes, s_t),
-            "h2s_bytes_gbs": rate(h_bytes, h_t), "steps": steps}
-
-
-def graph_step(b, w, steps_per_graph=10, replays=20):
-    """The same step replayed from a HIP graph: steps_per_graph steps over
-    the rotating buffer sets are captured once (the entry points only launch
-    kernels, so they capture), then replayed; the rate over all replays,
-    between two events, against the eager loop's."""
-    import torch
-    plan, sets = w.plan, w.sets
-    graph = torch.cuda.CUDAGraph()
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph):
-        for i in range(steps_per_graph):
-            s = sets[i % w.R]
-            b.basp_seq_to_head(plan, s["q"], s["k"], s["v"], s["qkv_out"])
-            b.basp_head_to_seq(plan, s["o"], s["o_out"])
-    graph.replay()
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(replays):
-        graph.replay()
-    stop.record()
-    torch.cuda.synchronize()
-    seconds = start.elapsed_time(stop) * 1e-3 / (replays * steps_per_graph)
-    del graph
-    return {"steps": replays * steps_per_graph, "us_per_step": seconds * 1e6,
-            "gbs": rate(w.s2h_bytes + w.h2s_bytes, seconds)}
-
-
-def detail(args, b, w):
-    """Per-kernel rates of both modes, the unfused baseline, the backward
-    entry points, the token-major layout and a plain device copy."""
-    import torch
-    out = {}
-    n = args.detail_iters
-    med = statistics.median
-    for mode in ("basp", "ulysses"):
-        ww = w if mode == w.mode else Workload(b, w.name, mode, w.R, not args.no_autotune)
-        p, sets = ww.plan, ww.sets
-        t = time_launches(b, lambda i: b.basp_seq_to_head(p, sets[i]["q"], sets[i]["k"], sets[i]["v"],
-                                                          sets[i]["qkv_out"]), n, ww.R)
-        u = time_launches(b, lambda i: b.basp_head_to_seq(p, sets[i]["o"], sets[i]["o_out"]), n, ww.R)
-        info = p.info
-        out[mode] = {
-            "G": info["G"], "P": info["P"], "Bl": info["Bl"], "peers_per_rank": info["peers_per_rank"],
-            "cross_rank_bytes_qkv": info["cross_rank_bytes_q"] + 2 * info["cross_rank_bytes_kv"],
-            "s2h_median_us": med(t) * 1e6,
-            "s2h_gbs": rate(ww.s2h_bytes, med(t)),
-            "s2h_frac_of_peak": rate(ww.s2h_bytes, med(t)) / HBM_PEAK_GBS,
-            "h2s_median_us": med(u) * 1e6,
-            "h2s_gbs": rate(ww.h2s_bytes, med(u)),
-            "h2s_frac_of_peak": rate(ww.h2s_bytes, med(u)) / HBM_PEAK_GBS,
-        }
-        if mode == w.mode:
-            ws = torch.empty(b.basp_unfused_workspace_bytes(p), dtype=torch.uint8, device="cuda")
-            f = time_launches(b, lambda i: b.basp_seq_to_head_unfused(
-                p, sets[i]["q"], sets[i]["k"], sets[i]["v"], sets[i]["qkv_out"], ws), max(10, n // 4), ww.R)
-            out[mode]["s2h_unfused_median_us"] = med(f) * 1e6
-            out[mode]["s2h_unfused_gbs"] = rate(ww.s2h_bytes, med(f))
-            del ws
-            # backward: dO seq->head (O-shaped, reuses the O buffers) and the
-            # fused dQ/dK/dV head->seq (reads the fused buffer, writes q/k/v-shaped)
-            grads = [{"dq": torch.empty_like(s["q"]), "dk": torch.empty_like(s["k"]),
-                      "dv": torch.empty_like(s["v"])} for s in sets]
-            bo = time_launches(b, lambda i: b.basp_seq_to_head_o(p, sets[i]["o"], sets[i]["o_out"]), n, ww.R)
-            bq = time_launches(b, lambda i: b.basp_head_to_seq_qkv(
-                p, sets[i]["qkv_out"], grads[i]["dq"], grads[i]["dk"], grads[i]["dv"]), n, ww.R)
-            out[mode]["backward"] = {
-                "do_s2h_gbs": rate(ww.h2s_bytes, med(bo)), "do_s2h_median_us": med(bo) * 1e6,
-                "dqkv_h2s_gbs": rate(ww.s2h_bytes, med(bq)), "dqkv_h2s_median_us": med(bq) * 1e6}
-            del grads
-            # head shards in token-major order ([Bl][S][Hl][d])
-            N, B, S, Hq, Hkv, d = ww.shape
-            pt = b.basp_plan_create_ex(N, B, S, Hq, Hkv, d, b.BASP_BF16,
-                                       b.BASP_MODE_BASP if mode == "basp" else b.BASP_MODE_ULYSSES,
-                                       b.BASP_LAYOUT_TOKEN_MAJOR)
-            if not args.no_autotune:
-                s0 = sets[0]
-                b.basp_plan_autotune(pt, s0["q"], s0["k"], s0["v"], s0["qkv_out"], s0["o"], s0["o_out"])
-            tt = time_launches(b, lambda i: b.basp_seq_to_head(pt, sets[i]["q"], sets[i]["k"], sets[i]["v"],
-                                                               sets[i]["qkv_out"]), n, ww.R)
-            tu = time_launches(b, lambda i: b.basp_head_to_seq(pt, sets[i]["o"], sets[i]["o_out"]), n, ww.R)
-            out[mode]["token_major"] = {"s2h_gbs": rate(ww.s2h_bytes, med(tt)),
-                                        "h2s_gbs": rate(ww.h2s_bytes, med(tu))}
-        if ww is not w:
-            del ww
-            torch.cuda.empty_cache()
-    out["graph_step"] = graph_step(b, w)
-    # plain device copy of the same byte count (read + write), and the
-    # known-size copy the PMC counters are scaled by
-    nb = w.s2h_bytes // 2
-    src = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(4)]
-    dst = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(4)]
-    c = time_torch(lambda i: dst[i].copy_(src[i]), n, 4)
-    out["device_copy"] = {"bytes_moved": 2 * nb, "median_us": med(c) * 1e6,
-                          "gbs": rate(2 * nb, med(c))}
-    del src, dst
-    return out
 
 
 def graph_seconds(fn, calls, reps=5):
@@ -485,15 +305,181 @@ def graph_seconds(fn, calls, reps=5):
     return statistics.median(t)
 
 
-def workload_table(b, steps, autotune):
-    """Fused seq->head and head->seq rates of every named workload in both
-    modes (device-filled random bf16: the rate does not depend on values).
-    Each rate is a HIP graph of back-to-back launches on rotating buffer sets
-    (graph_seconds): whole steps, then each direction alone; at least `steps`
-    launches per graph, more for small calls.  Once per workload, the plain
-    copy pair at the same byte counts, run the same way."""
+def copy_buffers(nbytes, R):
     import torch
+    return [(torch.empty(nbytes, dtype=torch.uint8, device="cuda"),
+             torch.empty(nbytes, dtype=torch.uint8, device="cuda")) for _ in range(R)]
+
+
+def copy_ceiling(b, s_bytes, h_bytes, steps, warmup, every, min_launches):
+    """basp_stream_copy (a plain read-once, write-once copy with the kernels'
+    access rules) at the two kernels' byte counts: each launch timed alone,
+    and run the way the step loop runs the kernels."""
+    import torch
+    R = max(2, -(-(3 << 30) // (s_bytes + h_bytes)))
+    sb, hb = copy_buffers(s_bytes // 2, R), copy_buffers(h_bytes // 2, R)
+    out = {}
+    for key, bufs, m in (("s2h_bytes", sb, s_bytes), ("h2s_bytes", hb, h_bytes)):
+        t = time_launches(b, lambda i: b.basp_stream_copy(bufs[i][1], bufs[i][0]), 60, R)
+        out[key + "_alone_gbs"] = rate(m, statistics.mean(t))
+    wall, s_t, h_t = step_loop(b, lambda i: b.basp_stream_copy(sb[i % R][1], sb[i % R][0]),
+                               lambda i: b.basp_stream_copy(hb[i % R][1], hb[i % R][0]),
+                               steps, warmup, every, min_launches, marker=False)
+    out["s2h_bytes_gbs"] = rate(s_bytes, statistics.mean(s_t))
+    out["h2s_bytes_gbs"] = rate(h_bytes, statistics.mean(h_t))
+    out["step_gbs"] = rate(s_bytes + h_bytes, wall / steps)
+    del sb, hb
+    torch.cuda.empty_cache()
+    return out
+
+
+# -------------------------------------------------------------- GPU run ---
+
+def shapes_mode(args):
+    return "autotune" if args.autotune else ("builtin" if args.builtin_shapes else "table")
+
+
+def run_gpu(args):
+    import torch
+    from sequence_re_layout_amd import binding as b
     from sequence_re_layout_amd import workloads
+
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    device = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+              "compute_units": props.multi_processor_count, "memory_bytes": props.total_memory}
+    name, *shape = workloads.BY_NAME[args.workload]
+    shape = tuple(shape)
+    inp = Inputs(shape)
+    res = {"device": device, "modes": {}}
+    runs = {}
+    for mode in MODES:   # BASP first: its first `steps` steps are the timed region
+        w = ModeRun(b, name, shape, mode, inp, args.rotate, shapes_mode(args))
+        runs[mode] = w
+        if mode == "basp":
+            # host bytes of the BASP buffers for the CPU baseline (the bytes
+            # the GPU consumes), copied before any marked loop
+            res["host"] = {n: w.sets[0][n].cpu() for n in ("q", "k", "v", "o")}
+        wall, s_t, h_t = step_loop(b, lambda i: w.s2h(b, i), lambda i: w.h2s(b, i), args.steps,
+                                   args.warmup, args.sample_every, args.min_launches)
+        s, h = stats_us(s_t), stats_us(h_t)
+        res["modes"][mode] = {
+            "G": w.plan.info["G"], "P": w.plan.info["P"], "Bl": w.plan.info["Bl"],
+            "peers_per_rank": w.plan.info["peers_per_rank"],
+            "cross_rank_bytes_qkv": w.plan.info["cross_rank_bytes_q"] + 2 * w.plan.info["cross_rank_bytes_kv"],
+            "ms_per_step": wall / args.steps * 1e3, "step_gbs": rate(w.s2h_bytes + w.h2s_bytes, wall / args.steps),
+            "s2h": s, "h2s": h, "s2h_bytes": w.s2h_bytes, "h2s_bytes": w.h2s_bytes,
+            "s2h_gbs": rate(w.s2h_bytes, s["avg_us"] * 1e-6), "h2s_gbs": rate(w.h2s_bytes, h["avg_us"] * 1e-6),
+            "rotate_sets": w.R, "shape_source": w.shape_source, "tuning": w.tuning,
+            "autotune_seconds": w.autotune_seconds}
+    # device round trip of the timed buffers: head->seq of the Q part of the
+    # fused output gives Q back bit for bit, in both modes
+    ok = True
+    for mode, w in runs.items():
+        s = w.sets[0]
+        back = torch.empty_like(s["q"])
+        b.basp_seq_to_head(w.plan, s["q"], s["k"], s["v"], s["qkv_out"])
+        b.basp_head_to_seq(w.plan, s["qkv_out"][: w.plan.info["q_elems"]], back)
+        torch.cuda.synchronize()
+        ok = ok and bool(torch.equal(back.view(torch.int16), s["q"].view(torch.int16)))
+        del back
+    res["round_trip_bit_exact"] = ok
+    basp = runs["basp"]
+    res["shape"], res["name"] = shape, name
+    del runs, inp
+    torch.cuda.empty_cache()
+    res["copy"] = copy_ceiling(b, basp.s2h_bytes, basp.h2s_bytes, args.steps, args.warmup,
+                               args.sample_every, args.min_launches)
+    del basp
+    torch.cuda.empty_cache()
+    # a plain copy of known size, between two more marker kernels: the PMC
+    # byte counters are scaled by it
+    cal_src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    cal_dst = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    torch.cuda._sleep(MARKER_CYCLES)
+    cal_dst.copy_(cal_src)
+    torch.cuda._sleep(MARKER_CYCLES)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+    return res
+
+
+def optional_leg(fn):
+    """fn(), or {"error": ...} when it raises (after reporting it on stderr)."""
+    try:
+        return fn()
+    except Exception as e:   # noqa: BLE001 -- recorded in the output
+        import traceback
+        traceback.print_exc()
+        return {"error": "%s: %s" % (type(e).__name__, e)}
+
+
+def detail(args, shape, name):
+    """Per-mode rates of the other entry points on the bench workload: the
+    unfused baseline, the backward calls, the token-major layout, the
+    general-G plans, the step replayed from a HIP graph, torch's device
+    copy."""
+    import torch
+    from sequence_re_layout_amd import binding as b
+    N, B, S, Hq, Hkv, d = shape
+    inp = Inputs(shape)
+    out = {}
+    n = args.detail_iters
+    med = statistics.median
+    for mode in MODES:
+        w = ModeRun(b, name, shape, mode, inp, 2, shapes_mode(args))
+        p, sets = w.plan, w.sets
+        o = {}
+        ws = torch.empty(b.basp_unfused_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+        f = time_launches(b, lambda i: b.basp_seq_to_head_unfused(
+            p, sets[i]["q"], sets[i]["k"], sets[i]["v"], sets[i]["qkv_out"], ws), max(10, n // 4), w.R)
+        o["s2h_unfused_gbs"] = rate(w.s2h_bytes, med(f))
+        del ws
+        grads = [{"dq": torch.empty_like(s["q"]), "dk": torch.empty_like(s["k"]),
+                  "dv": torch.empty_like(s["v"])} for s in sets]
+        bo = time_launches(b, lambda i: b.basp_seq_to_head_o(p, sets[i]["o"], sets[i]["o_out"]), n, w.R)
+        bq = time_launches(b, lambda i: b.basp_head_to_seq_qkv(
+            p, sets[i]["qkv_out"], grads[i]["dq"], grads[i]["dk"], grads[i]["dv"]), n, w.R)
+        o["backward"] = {"do_s2h_gbs": rate(w.h2s_bytes, med(bo)), "dqkv_h2s_gbs": rate(w.s2h_bytes, med(bq))}
+        del grads
+        pt = b.basp_plan_create_ex(N, B, S, Hq, Hkv, d, b.BASP_BF16,
+                                   b.BASP_MODE_BASP if mode == "basp" else b.BASP_MODE_ULYSSES,
+                                   b.BASP_LAYOUT_TOKEN_MAJOR)
+        s0 = sets[0]
+        if not args.builtin_shapes:
+            b.basp_plan_autotune(pt, s0["q"], s0["k"], s0["v"], s0["qkv_out"], s0["o"], s0["o_out"])
+        tt = time_launches(b, lambda i: b.basp_seq_to_head(pt, sets[i]["q"], sets[i]["k"], sets[i]["v"],
+                                                           sets[i]["qkv_out"]), n, w.R)
+        tu = time_launches(b, lambda i: b.basp_head_to_seq(pt, sets[i]["o"], sets[i]["o_out"]), n, w.R)
+        o["token_major"] = {"s2h_gbs": rate(w.s2h_bytes, med(tt)), "h2s_gbs": rate(w.h2s_bytes, med(tu))}
+        o["graph_step_gbs"] = rate(w.s2h_bytes + w.h2s_bytes,
+                                   graph_seconds(lambda i: (w.s2h(b, i), w.h2s(b, i)), 20))
+        out[mode] = o
+        del w, sets, p
+        torch.cuda.empty_cache()
+    nb = (2 * B * S * (Hq + 2 * Hkv) * d * 2) // 2
+    src = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    dst = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    c = time_torch(lambda i: dst[i].copy_(src[i]), n, 2)
+    out["torch_device_copy_gbs"] = rate(2 * nb, med(c))
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def workload_table(args):
+    """Fused seq->head and head->seq rates of every named workload in both
+    modes (device-filled random bf16: the rate does not depend on values),
+    with the launch shapes of the table.  Each rate is a HIP graph of
+    back-to-back launches on rotating buffer sets (graph_seconds): whole
+    steps, then each direction alone; at least --workload-steps launches per
+    graph, more for small calls.  Once per workload, the plain copy pair at
+    the same byte counts, run the same way."""
+    import torch
+    from sequence_re_layout_amd import binding as b
+    from sequence_re_layout_amd import launch_shapes, workloads
+    steps = args.workload_steps
     out = {}
     for (name, N, B, S, Hq, Hkv, d) in workloads.ALL + workloads.EXTRA:
         out[name] = {}
@@ -503,35 +489,18 @@ def workload_table(b, steps, autotune):
             sb, hb = i["qkv_bytes_moved"], i["o_bytes_moved"]
             R = max(2, -(-(3 << 30) // (sb + hb)))
             n = max(steps, min(10 * steps, steps * (400 << 20) // sb))
-            sets = []
-            for _ in range(R):
-                x = torch.empty(2 * i["q_elems"] + 2 * i["kv_elems"], dtype=torch.bfloat16, device="cuda").normal_()
-                sets.append({"x": x, "q": x[:i["q_elems"]], "k": x[i["q_elems"]:i["q_elems"] + i["kv_elems"]],
-                             "v": x[i["q_elems"] + i["kv_elems"]:i["q_elems"] + 2 * i["kv_elems"]],
-                             "o": x[i["q_elems"] + 2 * i["kv_elems"]:],
-                             "out": torch.empty(i["qkv_elems"], dtype=torch.bfloat16, device="cuda"),
-                             "o_out": torch.empty(i["q_elems"], dtype=torch.bfloat16, device="cuda")})
-            if autotune:
-                b.basp_plan_autotune(p, sets[0]["q"], sets[0]["k"], sets[0]["v"], sets[0]["out"],
-                                     sets[0]["o"], sets[0]["o_out"])
-
-            def s2h(j):
-                s = sets[j % R]
-                b.basp_seq_to_head(p, s["q"], s["k"], s["v"], s["out"])
-
-            def h2s(j):
-                s = sets[j % R]
-                b.basp_head_to_seq(p, s["o"], s["o_out"])
-
-            wall = graph_seconds(lambda j: (s2h(j), h2s(j)), n)
-            t, u = graph_seconds(s2h, n), graph_seconds(h2s, n)
-            out[name][mode] = {
-                "G": i["G"], "P": i["P"], "Bl": i["Bl"], "peers_per_rank": i["peers_per_rank"],
-                "launches_per_graph": n, "step_gbs": rate(sb + hb, wall),
-                "s2h_bytes": sb, "s2h_us": t * 1e6, "s2h_gbs": rate(sb, t), "s2h_frac": rate(sb, t) / HBM_PEAK_GBS,
-                "h2s_bytes": hb, "h2s_us": u * 1e6, "h2s_gbs": rate(hb, u), "h2s_frac": rate(hb, u) / HBM_PEAK_GBS,
-                "launch_shape": {"seq_to_head": b.basp_plan_get_tuning(p, b.BASP_SEQ_TO_HEAD),
-                                 "head_to_seq": b.basp_plan_get_tuning(p, b.BASP_HEAD_TO_SEQ)}}
+            sets = table_sets(i, R)
+            source = "built-in"
+            if not args.builtin_shapes:
+                if not args.autotune and launch_shapes.apply(b, p, name, mode):
+                    source = "table"
+                else:
+                    b.basp_plan_autotune(p, sets[0]["q"], sets[0]["k"], sets[0]["v"], sets[0]["out"],
+                                         sets[0]["o"], sets[0]["o_out"])
+                    source = "autotuned"
+            t = measure_pair(b, p, sets, R, n)
+            out[name][mode] = dict(t, G=i["G"], P=i["P"], Bl=i["Bl"], launches_per_graph=n, shapes=source,
+                                   s2h_frac=t["s2h_gbs"] / HBM_PEAK_GBS, h2s_frac=t["h2s_gbs"] / HBM_PEAK_GBS)
             if mode == "basp":   # both modes move the same bytes: one copy pair per workload
                 qkv_b, o_b = sb // 2, hb // 2
 
@@ -541,62 +510,136 @@ def workload_table(b, steps, autotune):
                 def ch(j):
                     b.basp_stream_copy(sets[j % R]["o_out"], sets[j % R]["x"], o_b)
 
-                cw = graph_seconds(lambda j: (cs(j), ch(j)), n)
-                tc, uc = graph_seconds(cs, n), graph_seconds(ch, n)
-                out[name]["copy"] = {"s2h_bytes_gbs": rate(2 * qkv_b, tc), "h2s_bytes_gbs": rate(2 * o_b, uc),
-                                     "step_gbs": rate(2 * (qkv_b + o_b), cw)}
+                out[name]["copy"] = {"s2h_bytes_gbs": rate(2 * qkv_b, graph_seconds(cs, n)),
+                                     "h2s_bytes_gbs": rate(2 * o_b, graph_seconds(ch, n)),
+                                     "step_gbs": rate(2 * (qkv_b + o_b), graph_seconds(lambda j: (cs(j), ch(j)), n))}
             del sets
             torch.cuda.empty_cache()
+        print("workload table: %s done" % name, file=sys.stderr, flush=True)
     return out
+
+
+def table_sets(i, R):
+    """R rotating device sets for a plan with info i: one random buffer x
+    holding q, k, v and o back to back, and the two outputs."""
+    import torch
+    sets = []
+    for _ in range(R):
+        x = torch.empty(2 * i["q_elems"] + 2 * i["kv_elems"], dtype=torch.bfloat16, device="cuda").normal_()
+        nq, nkv = i["q_elems"], i["kv_elems"]
+        sets.append({"x": x, "q": x[:nq], "k": x[nq:nq + nkv], "v": x[nq + nkv:nq + 2 * nkv],
+                     "o": x[nq + 2 * nkv:],
+                     "out": torch.empty(i["qkv_elems"], dtype=torch.bfloat16, device="cuda"),
+                     "o_out": torch.empty(nq, dtype=torch.bfloat16, device="cuda")})
+    return sets
+
+
+def measure_pair(b, p, sets, R, n):
+    """Whole back-to-back steps, then each direction alone, from HIP graphs."""
+    i = p.info
+    sb, hb = i["qkv_bytes_moved"], i["o_bytes_moved"]
+
+    def s2h(j):
+        s = sets[j % R]
+        b.basp_seq_to_head(p, s["q"], s["k"], s["v"], s["out"])
+
+    def h2s(j):
+        s = sets[j % R]
+        b.basp_head_to_seq(p, s["o"], s["o_out"])
+
+    wall = graph_seconds(lambda j: (s2h(j), h2s(j)), n)
+    t, u = graph_seconds(s2h, n), graph_seconds(h2s, n)
+    return {"step_us": wall * 1e6, "step_gbs": rate(sb + hb, wall), "s2h_us": t * 1e6, "s2h_gbs": rate(sb, t),
+            "h2s_us": u * 1e6, "h2s_gbs": rate(hb, u)}
+
+
+def tune_shapes(args):
+    """The launch-shape table: for every named workload and mode,
+    basp_plan_autotune runs --tune-autotunes times (each from the built-in
+    shapes); the distinct pairs it keeps and the built-in pair are timed as
+    whole back-to-back steps from HIP graphs in 3 interleaved rounds; the
+    pair with the lowest median step time is kept."""
+    import torch
+    from sequence_re_layout_amd import binding as b
+    from sequence_re_layout_amd import workloads
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    out = {"about": "launch shapes per named workload and mode, measured by bench.py --tune-shapes",
+           "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None)},
+           "kernel_sources_sha256": kernel_sources_sha256(), "shapes": {}}
+    dirs = (("seq_to_head", b.BASP_SEQ_TO_HEAD), ("head_to_seq", b.BASP_HEAD_TO_SEQ))
+    for (name, N, B, S, Hq, Hkv, d) in workloads.ALL + workloads.EXTRA:
+        out["shapes"][name] = {}
+        for mode, code in (("basp", b.BASP_MODE_BASP), ("ulysses", b.BASP_MODE_ULYSSES)):
+            p = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, code)
+            i = p.info
+            R = max(2, -(-(3 << 30) // (i["qkv_bytes_moved"] + i["o_bytes_moved"])))
+            n = max(args.workload_steps, min(10 * args.workload_steps,
+                                             args.workload_steps * (400 << 20) // i["qkv_bytes_moved"]))
+            sets = table_sets(i, R)
+            cands = [({}, {})]
+            for _ in range(args.tune_autotunes):
+                b.basp_plan_set_tuning(p)
+                s = sets[0]
+                b.basp_plan_autotune(p, s["q"], s["k"], s["v"], s["out"], s["o"], s["o_out"])
+                pair = tuple({k: v for k, v in b.basp_plan_get_tuning(p, dcode).items() if v}
+                             for _, dcode in dirs)
+                if pair not in cands:
+                    cands.append(pair)
+            times = [[] for _ in cands]
+            for _ in range(3):
+                for c, (ts, th) in enumerate(cands):
+                    b.basp_plan_set_direction_tuning(p, b.BASP_SEQ_TO_HEAD, **ts)
+                    b.basp_plan_set_direction_tuning(p, b.BASP_HEAD_TO_SEQ, **th)
+                    times[c].append(measure_pair(b, p, sets, R, n))
+            med = [statistics.median(t["step_us"] for t in ts) for ts in times]
+            best = min(range(len(cands)), key=lambda c: med[c])
+            pick = times[best]
+            out["shapes"][name][mode] = {
+                "seq_to_head": cands[best][0], "head_to_seq": cands[best][1],
+                "step_us": med[best], "s2h_us": statistics.median(t["s2h_us"] for t in pick),
+                "h2s_us": statistics.median(t["h2s_us"] for t in pick),
+                "candidates": len(cands), "candidate_step_us": med}
+            print("tune-shapes: %s %s: %d candidates, step %.1f us (built-in %.1f us)"
+                  % (name, mode, len(cands), med[best], med[0]), file=sys.stderr, flush=True)
+            del sets
+            torch.cuda.empty_cache()
+    with open(args.tune_shapes, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    return 0
 
 
 # ------------------------------------------------------------------ CPU ---
 
-def cpu_baseline(args, w):
-    """The oracle doing one step (fused Q/K/V seq->head, O head->seq) on the
-    host bytes of the same workload, repeated for about --cpu-seconds."""
-    import numpy as np
-
+def cpu_baseline(args, shape, mode, host):
+    """The oracle doing the bench step (fused Q/K/V seq->head, O head->seq) on
+    the host bytes the GPU consumed, repeated for about --cpu-seconds on all
+    cores OpenMP gives it, then for a quarter of that on one thread."""
     import oracle
     from sequence_re_layout_amd import inputs
-    N, B, S, Hq, Hkv, d = w.shape
-    mode = oracle.BASP if w.mode == "basp" else oracle.ULYSSES
-    q, k, v, o = (inputs.raw_bits(w.host[n]) for n in ("q", "k", "v", "o"))
+    N, B, S, Hq, Hkv, d = shape
+    m = oracle.BASP if mode == "basp" else oracle.ULYSSES
+    q, k, v, o = (inputs.raw_bits(host[n]) for n in ("q", "k", "v", "o"))
+    step_bytes = 2 * (q.nbytes + k.nbytes + v.nbytes) + 2 * o.nbytes
+
+    def loop(threads, seconds):
+        reps, spent = 0, 0.0
+        while reps == 0 or spent < seconds:
+            t0 = time.perf_counter_ns()
+            oracle.seq_to_head_qkv(q, k, v, m, N, B, S, Hq, Hkv, d, threads=threads)
+            oracle.head_to_seq(o, m, N, B, S, Hq, d, threads=threads)
+            spent += (time.perf_counter_ns() - t0) * 1e-9
+            reps += 1
+        return reps, spent
+
     threads = oracle.max_threads()
-    reps, spent = 0, 0.0
-    while reps == 0 or spent < args.cpu_seconds:
-        t0 = time.perf_counter_ns()
-        oracle.seq_to_head_qkv(q, k, v, mode, N, B, S, Hq, Hkv, d, threads=threads)
-        oracle.head_to_seq(o, mode, N, B, S, Hq, d, threads=threads)
-        spent += (time.perf_counter_ns() - t0) * 1e-9
-        reps += 1
-    step_bytes = w.s2h_bytes + w.h2s_bytes
-    # for information: the same step as one NumPy transpose per tensor
-    reps_np, spent_np = 0, 0.0
-    while reps_np == 0 or spent_np < args.cpu_seconds / 4:
-        t0 = time.perf_counter_ns()
-        np.concatenate([oracle.numpy_seq_to_head(x, mode, N, B, S, H, d)
-                        for x, H in ((q, Hq), (k, Hkv), (v, Hkv))])
-        oracle.numpy_head_to_seq(o, mode, N, B, S, Hq, d)
-        spent_np += (time.perf_counter_ns() - t0) * 1e-9
-        reps_np += 1
-    # the same loop on one thread, for a shorter while
-    reps1, spent1 = 0, 0.0
-    while reps1 == 0 or spent1 < args.cpu_seconds / 4:
-        t0 = time.perf_counter_ns()
-        oracle.seq_to_head_qkv(q, k, v, mode, N, B, S, Hq, Hkv, d, threads=1)
-        oracle.head_to_seq(o, mode, N, B, S, Hq, d, threads=1)
-        spent1 += (time.perf_counter_ns() - t0) * 1e-9
-        reps1 += 1
+    reps, spent = loop(threads, args.cpu_seconds)
+    reps1, spent1 = loop(1, args.cpu_seconds / 4)
     return {"value": rate(step_bytes * reps, spent), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "%d full step(s) of the same workload (fused QKV seq->head + O head->seq), "
-                      "%.1f s on the host, OpenMP over destination blocks" % (reps, spent),
+            "sample": "%d full step(s) of the bench workload (fused QKV seq->head + O head->seq, %s mode), "
+                      "%.1f s on the host, OpenMP over destination blocks" % (reps, mode, spent),
             "seconds_per_step": spent / reps, "cpu_model": cpu_model(),
-            "one_thread": {"value": rate(step_bytes * reps1, spent1), "unit": "GB/s",
-                           "seconds_per_step": spent1 / reps1, "steps": reps1},
-            "numpy_transpose": {"value": rate(step_bytes * reps_np, spent_np), "unit": "GB/s",
-                                "seconds_per_step": spent_np / reps_np, "steps": reps_np,
-                                "note": "the same step as one NumPy transpose per tensor, for information"}}
+            "one_thread_gbs": rate(step_bytes * reps1, spent1)}
 
 
 def cpu_model():
@@ -610,26 +653,47 @@ def cpu_model():
     return None
 
 
-# ------------------------------------------------------------ roofline ---
+# ---------------------------------------------------------- profiles ---
+
+def _regions(rows, name_key):
+    """Rows between consecutive pairs of marker kernels (torch's spin
+    kernel): the sampled loop of each mode, in run order."""
+    marks = [i for i, r in enumerate(rows) if "spin_kernel" in r[name_key]]
+    return [rows[marks[i] + 1:marks[i + 1]] for i in range(0, len(marks) - 1, 2)]
+
+
+def _is_tile(name, s2h):
+    return "tile_kernel" in name and (("true>" in name) if s2h else ("false>" in name))
+
+
+def launch_shape_key(workload, mode):
+    """The table's launch shapes of a workload and mode (what a default run
+    times), as stored beside counters taken on them."""
+    from sequence_re_layout_amd import launch_shapes
+    found = launch_shapes.lookup(workload, mode)
+    return None if found is None else {"seq_to_head": found[0], "head_to_seq": found[1]}
+
 
 def traffic_bytes(workload, mode):
     """HBM bytes per fused seq->head launch from committed PMC counters, or
-    None when they are missing, were taken on other kernel sources, or on
-    another workload or mode."""
+    None when there are none for this workload and mode, or they were taken
+    on other kernel sources or other launch shapes."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if (t.get("kernel_sources_sha256") != kernel_sources_sha256() or t.get("workload") != workload
-            or t.get("mode") != mode):
-        return None
-    return t.get("traffic_bytes_per_launch")
+    for e in t.get("entries", []):
+        if (e.get("workload") == workload and e.get("mode") == mode
+                and e.get("kernel_sources_sha256") == kernel_sources_sha256()
+                and e.get("launch_shape") == launch_shape_key(workload, mode)):
+            return e.get("traffic_bytes_per_launch")
+    return None
 
 
-def pmc_summary(fetch_dir, write_dir):
-    """Per-launch FETCH_SIZE/WRITE_SIZE of the fused kernel, scaled by the same
-    counter on the known-size copy, into profiles/pmc_traffic.json."""
+def pmc_summary(fetch_dir, write_dir, workload=DEFAULT_WORKLOAD):
+    """Per-launch FETCH_SIZE/WRITE_SIZE of both kernels in each mode's sampled
+    loop, scaled by the same counter on the known-size copy after them."""
 
     def load(d, counter):
         rows = []
@@ -640,122 +704,155 @@ def pmc_summary(fetch_dir, write_dir):
             raise SystemExit("no %s rows under %s" % (counter, d))
         return sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
 
-    out = {"workload": None, "kernel_sources_sha256": kernel_sources_sha256()}
+    entries = {m: {"workload": workload, "mode": m, "kernel_sources_sha256": kernel_sources_sha256(),
+                   "launch_shape": launch_shape_key(workload, m)} for m in MODES}
     for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
         rows = load(d, counter)
-        # the timed launches: between the two marker kernels of the run
-        marks = [i for i, r in enumerate(rows) if "spin_kernel" in r["Kernel_Name"]]
-        if len(marks) < 2:
-            raise SystemExit("no timed-region markers for %s" % counter)
-        timed = rows[marks[0] + 1:marks[1]]
-        # the fused seq->head kernel: tile_kernel<VW, VPT, POLICY, true> or
-        # tile_kernel_staged<VPT, POLICY, true>
-        fused = [r for r in timed if "tile_kernel" in r["Kernel_Name"] and "true>" in r["Kernel_Name"]]
-        copies = [r for r in rows[marks[1]:] if "copy" in r["Kernel_Name"].lower()
-                  and "stream_copy_kernel" not in r["Kernel_Name"]]
-        if not fused or not copies:
-            raise SystemExit("missing fused or copy dispatches for %s" % counter)
-        # the calibration copy: the largest copy after the timed region (small
-        # copies bring results back to the host)
-        cal_row = max(copies, key=lambda r: float(r["Counter_Value"]))
+        regions = _regions(rows, "Kernel_Name")
+        if len(regions) < len(MODES) + 1:
+            raise SystemExit("expected %d marked regions for %s, found %d"
+                             % (len(MODES) + 1, counter, len(regions)))
+        # the calibration copy: the one copy between the third pair of markers
+        copies = [r for r in regions[len(MODES)] if "copy" in r["Kernel_Name"].lower()]
+        if len(copies) != 1:
+            raise SystemExit("expected one calibration copy for %s, found %d" % (counter, len(copies)))
+        cal_row = copies[0]
         cal = float(cal_row["Counter_Value"])
         factor = (CALIB_BYTES / 1024.0) / cal
-        kib = statistics.median(float(r["Counter_Value"]) for r in fused)
-        out["kernel"] = fused[0]["Kernel_Name"]
-        out[counter] = {"kib_per_launch_raw": kib, "kernel_name": fused[0]["Kernel_Name"],
-                        "copy_kernel": cal_row["Kernel_Name"],
-                        "copy_kib_raw": cal, "scale": factor,
-                        "bytes_per_launch": kib * factor * 1024.0, "launches": len(fused)}
-        # the head->seq kernel of the same steps, for reference
-        back = [r for r in timed if "tile_kernel" in r["Kernel_Name"] and "false>" in r["Kernel_Name"]]
-        if back:
-            kb = statistics.median(float(r["Counter_Value"]) for r in back)
-            out.setdefault("head_to_seq", {})[counter] = {
-                "kib_per_launch_raw": kb, "kernel_name": back[0]["Kernel_Name"],
-                "bytes_per_launch": kb * factor * 1024.0, "launches": len(back)}
-    out["traffic_bytes_per_launch"] = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
-    if len(out.get("head_to_seq", {})) == 2:
-        h = out["head_to_seq"]
-        h["traffic_bytes_per_launch"] = h["FETCH_SIZE"]["bytes_per_launch"] + h["WRITE_SIZE"]["bytes_per_launch"]
+        for mode, region in zip(MODES, regions):
+            e = entries[mode]
+            for key, s2h in (("seq_to_head", True), ("head_to_seq", False)):
+                k = [r for r in region if _is_tile(r["Kernel_Name"], s2h)]
+                if not k:
+                    raise SystemExit("no %s launches in the %s loop" % (key, mode))
+                kib = statistics.median(float(r["Counter_Value"]) for r in k)
+                e.setdefault(key, {"kernel": k[0]["Kernel_Name"]})[counter] = {
+                    "kib_per_launch_raw": kib, "launches": len(k), "copy_kib_raw": cal,
+                    "copy_kernel": cal_row["Kernel_Name"], "scale": factor,
+                    "bytes_per_launch": kib * factor * 1024.0}
+    for e in entries.values():
+        for key in ("seq_to_head", "head_to_seq"):
+            e[key]["traffic_bytes_per_launch"] = (e[key]["FETCH_SIZE"]["bytes_per_launch"]
+                                                  + e[key]["WRITE_SIZE"]["bytes_per_launch"])
+        e["traffic_bytes_per_launch"] = e["seq_to_head"]["traffic_bytes_per_launch"]
+    return {"entries": [entries[m] for m in MODES]}
+
+
+def trace_summary(trace_dir):
+    """Average durations of both kernels in each mode's sampled loop of a
+    rocprofv3 --kernel-trace run of this script, and the gaps between
+    back-to-back dispatches there."""
+    rows = []
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    if not rows:
+        raise SystemExit("no kernel trace under %s" % trace_dir)
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    out = {}
+    for mode, region in zip(MODES, _regions(rows, "Kernel_Name")):
+        o = {}
+        for key, s2h in (("seq_to_head", True), ("head_to_seq", False)):
+            k = [r for r in region if _is_tile(r["Kernel_Name"], s2h)]
+            dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3 for r in k]
+            o[key] = {"kernel": k[0]["Kernel_Name"] if k else None, "launches": len(k),
+                      "avg_us": statistics.mean(dur) if dur else None,
+                      "median_us": statistics.median(dur) if dur else None}
+        gaps = [(int(b["Start_Timestamp"]) - int(a["End_Timestamp"])) * 1e-3 for a, b in zip(region, region[1:])]
+        o["avg_gap_us"] = statistics.mean(gaps) if gaps else None
+        out[mode] = o
     return out
 
 
 # ---------------------------------------------------------------- main ---
 
-def make_line(args, r, w, traffic):
-    """The JSON line's fields from the measurements r of run_gpu and the
-    workload w (its shape, name and mode); traffic is the HBM bytes per fused
-    launch from the committed counters, or None."""
-    N, B, S, Hq, Hkv, d = w.shape
+def make_line(args, r, traffic, cpu):
+    """The compact JSON line from the measurements r of run_gpu; traffic is
+    the HBM bytes per fused launch from the committed counters, or None."""
+    N, B, S, Hq, Hkv, d = r["shape"]
+    m = r["modes"]
+    head = m["basp"]
+    cp = r["copy"]
+
+    def brief(x):
+        return {"G": x["G"], "P": x["P"], "Bl": x["Bl"], "peers_per_rank": x["peers_per_rank"],
+                "s2h_gbs": round(x["s2h_gbs"], 1), "s2h_frac": round(x["s2h_gbs"] / HBM_PEAK_GBS, 4),
+                "s2h_avg_us": round(x["s2h"]["avg_us"], 2),
+                "h2s_gbs": round(x["h2s_gbs"], 1), "h2s_frac": round(x["h2s_gbs"] / HBM_PEAK_GBS, 4),
+                "h2s_avg_us": round(x["h2s"]["avg_us"], 2),
+                "step_gbs": round(x["step_gbs"], 1), "launches": x["s2h"]["launches"]}
+
     line = {
         "metric": METRIC,
-        "value": r["value"],
+        "value": head["s2h_gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": r["ms_per_step"],
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic: seeded N(0,1) bf16 Q/K/V/O, resident in HBM, %d rotating buffer sets" % r["rotate_sets"],
-        "config": {"workload": w.name, "N": N, "B": B, "S": S, "Hq": Hq, "Hkv": Hkv, "d": d,
-                   "mode": w.mode, "parallelism": "%d virtual ranks on 1 GPU" % N,
-                   "step": "fused QKV seq->head + O head->seq", "step_bytes": r["step_bytes"],
-                   "launch_shape": r["tuning"]},
-        "roofline": {"bound": "hbm", "kernel": "fused QKV seq->head (tile_kernel)",
-                     "achieved": r["s2h_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": r["s2h_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": r["s2h_bytes"], "avg_launch_us": r["s2h_avg_us"],
-                     "median_launch_us": r.get("s2h_median_us"), "min_launch_us": r.get("s2h_min_us"),
-                     "max_launch_us": r.get("s2h_max_us"), "timed_launches": r["timed_launches_per_kernel"]},
-        "copy_ceiling": {
-            "kernel": "basp_stream_copy (16-byte loads/stores, same cache policy, read once, written once)",
-            "s2h_bytes_gbs": r["copy_ceiling"][str(r["s2h_bytes"])]["gbs"],
-            "h2s_bytes_gbs": r["copy_ceiling"][str(r["h2s_bytes"])]["gbs"],
-            "s2h_frac_of_copy": r["s2h_gbs"] / r["copy_ceiling"][str(r["s2h_bytes"])]["gbs"],
-            "h2s_frac_of_copy": r["h2s_gbs"] / r["copy_ceiling"][str(r["h2s_bytes"])]["gbs"],
-            "in_timed_loop": dict(r["copy_loop"],
-                                  step_frac_of_copy=r["value"] / r["copy_loop"]["step_gbs"],
-                                  s2h_frac_of_copy=r["s2h_gbs"] / r["copy_loop"]["s2h_bytes_gbs"],
-                                  h2s_frac_of_copy=r["h2s_gbs"] / r["copy_loop"]["h2s_bytes_gbs"])},
-        "head_to_seq": {"achieved": r["h2s_gbs"], "frac": r["h2s_gbs"] / HBM_PEAK_GBS,
-                        "avg_launch_us": r["h2s_avg_us"], "median_launch_us": r.get("h2s_median_us"),
-                        "min_launch_us": r.get("h2s_min_us"), "max_launch_us": r.get("h2s_max_us"),
-                        "bytes_per_launch": r["h2s_bytes"]},
+        "data": ("synthetic: one seeded N(0,1) bf16 global tensor each for Q/K/V/O, scattered into each "
+                 "mode's rank-sharded buffers; resident in HBM; %d rotating sets" % head["rotate_sets"]),
+        "config": {"workload": r["name"], "N": N, "B": B, "S": S, "Hq": Hq, "Hkv": Hkv, "d": d,
+                   "mode": "basp", "parallelism": "%d virtual ranks on 1 GPU" % N,
+                   "step": "fused QKV seq->head + O head->seq", "launch_shapes": head["shape_source"],
+                   "tuning_s2h": {k: v for k, v in head["tuning"]["seq_to_head"].items() if v}},
+        "roofline": {"bound": "hbm", "kernel": "tile_kernel seq->head (fused Q/K/V)",
+                     "achieved": head["s2h_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["s2h_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": head["s2h_bytes"],
+                     "avg_launch_us": head["s2h"]["avg_us"], "median_launch_us": head["s2h"]["median_us"],
+                     "timed_launches": head["s2h"]["launches"]},
+        "basp_vs_ulysses": {mode: brief(m[mode]) for mode in MODES},
+        "copy_ceiling": {"s2h_bytes_gbs": round(cp["s2h_bytes_gbs"], 1), "h2s_bytes_gbs": round(cp["h2s_bytes_gbs"], 1),
+                         "s2h_frac_of_copy": round(head["s2h_gbs"] / cp["s2h_bytes_gbs"], 4),
+                         "h2s_frac_of_copy": round(head["h2s_gbs"] / cp["h2s_bytes_gbs"], 4)},
         "round_trip_bit_exact": r["round_trip_bit_exact"],
+        "detail_file": args.detail_out,
     }
-    if "device" in r:
-        line["device"] = r["device"]
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     return line
 
 
 def main(argv=None):
     args = parse_args(argv)
     if args.pmc_summary:
-        res = pmc_summary(*args.pmc_summary)
-        defaults = parse_args([])   # the counter runs use the default workload and mode
-        res["workload"], res["mode"] = defaults.workload, defaults.mode
+        res = pmc_summary(*args.pmc_summary, workload=args.workload)
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(res, f, indent=1)
         print(json.dumps(res))
+        return 0
+    if args.trace_summary:
+        print(json.dumps(trace_summary(args.trace_summary), indent=1))
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the N virtual ranks of the re-layout share one "
               "device allocation, and no multi-GPU path exists (requested --gpus %d)" % args.gpus,
               file=sys.stderr)
         return 2
+    if args.tune_shapes:
+        return tune_shapes(args)
 
     r = run_gpu(args)
-    w = r.pop("w")
-    line = make_line(args, r, w, traffic_bytes(w.name, w.mode))
-    if "detail" in r:
-        line["detail"] = r["detail"]
-    if "workloads" in r:
-        line["workloads"] = r["workloads"]
+    host = r.pop("host")
+    cpu = None
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = optional_leg(lambda: cpu_baseline(args, w))
+        cpu = optional_leg(lambda: cpu_baseline(args, r["shape"], "basp", host))
+    del host
+    line = make_line(args, r, traffic_bytes(r["name"], "basp"), cpu)
+    full = {"line": line, "modes": r["modes"], "copy": r["copy"], "device": r["device"]}
+    if not args.no_detail:
+        full["detail"] = optional_leg(lambda: detail(args, r["shape"], r["name"]))
+    if not args.no_workloads:
+        full["workloads"] = optional_leg(lambda: workload_table(args))
+    if args.detail_out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.detail_out)), exist_ok=True)
+        with open(args.detail_out, "w") as f:
+            json.dump(full, f, indent=1, default=str)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -107,7 +107,28 @@ typedef enum basp_layout {
 typedef struct basp_plan basp_plan;
 
 /* Everything a caller needs to size buffers and to account for traffic.
- * Element counts are in elements, byte counts in bytes. */
+ * Element counts are in elements, byte counts in bytes.  Where a field is a
+ * count the pages state, the passage is named beside it; the others are
+ * sizes that follow from the layouts above.
+ *
+ *   tokens_per_rank     B*S/N tokens stay on every rank in both schemes
+ *                       [review, Summary; Frequently asked questions]
+ *   peers_per_rank      the ranks a rank exchanges with, itself excluded:
+ *                       K-1 under BASP against N-1 under Ulysses
+ *                       [review, Summary]
+ *   q_elems_per_rank,   the per-rank work (B/G)*H*(S*G/N)*d, equal for every
+ *   kv_elems_per_rank   number of groups G [review, Strengths; paper Sec. IV.C]
+ *   per_peer_bytes_*    one member's chunk for one other member of its group:
+ *                       Bl sequences x St tokens x Hl heads x d channels
+ *   cross_rank_bytes_*  bytes that leave their rank in the group exchange
+ *                       [review, Summary]: every rank receives P chunks, P-1 of
+ *                       them from other ranks, so (P-1)/P of each tensor
+ *   tokens_per_rank_foil  tokens per rank of the alternative the pages set
+ *                       BASP against, plain Ulysses over groups of N/B ranks
+ *                       that each hold the whole micro-batch: B*B*S/N
+ *                       [review, Strengths; paper Sec. IV.E, Table I].  0 when
+ *                       N/B is not a whole number (no such configuration).
+ */
 typedef struct basp_plan_info {
     int32_t N, B, Hq, Hkv, d, elem_size;
     int64_t S;
@@ -125,6 +146,7 @@ typedef struct basp_plan_info {
     int64_t cross_rank_bytes_q, cross_rank_bytes_kv; /* (P-1)/P of each tensor    */
     int64_t qkv_bytes_moved;      /* 2*(q_elems + 2*kv_elems)*elem_size            */
     int64_t o_bytes_moved;        /* 2*q_elems*elem_size                           */
+    int64_t tokens_per_rank_foil; /* B*B*S/N, or 0 (see above)                     */
 } basp_plan_info;
 
 /*
@@ -151,10 +173,13 @@ basp_plan *basp_plan_create(int N, int B, int64_t S, int Hq, int Hkv, int d,
 basp_plan *basp_plan_create_ex(int N, int B, int64_t S, int Hq, int Hkv, int d,
                                basp_dtype dtype, basp_mode mode, basp_layout layout);
 
-/* Free a plan.  NULL is allowed. */
+/* Free a plan.  NULL is allowed.  (Host resource management: not a step of
+ * the method.) */
 void basp_plan_destroy(basp_plan *plan);
 
-/* Fill *info.  BASP_ERR_INVALID if plan or info is NULL. */
+/* Fill *info with the plan's group structure, sizes and exchange counts
+ * (fields and their passages at basp_plan_info).  Host only.
+ * BASP_ERR_INVALID if plan or info is NULL. */
 basp_status basp_plan_query(const basp_plan *plan, basp_plan_info *info);
 
 /*
@@ -194,9 +219,11 @@ basp_status basp_head_to_seq_qkv(const basp_plan *plan, const void *in, void *dq
                                  void *dv, void *stream);
 
 /*
- * Unfused three-pass seq -> head, kept as an internal baseline: the
- * collective written out as (1) pack each rank's shard by destination member,
- * (2) exchange the per-peer chunks, (3) unpack into the head-sharded layout.
+ * Unfused three-pass seq -> head, kept as an internal baseline: the group
+ * all-to-all of the pages [review, Summary] written out as the collective a
+ * communication library runs, (1) pack each rank's shard by destination
+ * member, (2) exchange the per-peer chunks, (3) unpack into the head-sharded
+ * layout.
  * Same inputs and output as basp_seq_to_head (bit-identical result), three
  * times the memory traffic.
  *   ws   device workspace of basp_unfused_workspace_bytes(plan) bytes, owned by
@@ -292,7 +319,10 @@ basp_status basp_plan_get_tuning(const basp_plan *plan, basp_direction dir, basp
  * with the pair of the plan's shapes on entry.  The pair with the lowest
  * median step time is stored in the plan, replacing its tuning (the shapes
  * on entry stay when they win).  The buffers are those of basp_seq_to_head
- * and basp_head_to_seq, with the same checks.  Every candidate computes the
+ * and basp_head_to_seq, with the same checks, and because the two calls run
+ * back to back the six are also checked together: qkv and o_out must not
+ * overlap any of q, k, v, o or each other (BASP_ERR_ALIAS, before any
+ * launch).  Every candidate computes the
  * same re-layout, so on BASP_OK qkv and o_out hold the results of the two
  * calls.  Runs on stream and waits for it; creates and destroys HIP events
  * but allocates no device memory.  A pending basp_time_next_call request is
@@ -330,7 +360,8 @@ basp_status basp_time_next_call(void *start_event, void *stop_event);
  */
 basp_status basp_stream_copy(void *dst, const void *src, uint64_t bytes, void *stream);
 
-/* Status of the last call made by this thread, and a static description. */
+/* Status of the last call made by this thread, and a static description.
+ * (Error reporting: not a step of the method.) */
 basp_status basp_last_error(void);
 const char *basp_status_str(basp_status status);
 

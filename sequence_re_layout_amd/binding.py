@@ -48,7 +48,7 @@ class basp_plan_info(ctypes.Structure):
             "q_elems", "kv_elems", "q_elems_per_rank", "kv_elems_per_rank", "qkv_elems",
             "qkv_offset_q", "qkv_offset_k", "qkv_offset_v", "per_peer_bytes_q",
             "per_peer_bytes_kv", "cross_rank_bytes_q", "cross_rank_bytes_kv",
-            "qkv_bytes_moved", "o_bytes_moved")]
+            "qkv_bytes_moved", "o_bytes_moved", "tokens_per_rank_foil")]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -423,6 +423,18 @@ int prepare_head_to_seq_qkv(const basp_plan &p, const void *in, void *dq, void *
     return build_tiles(p, segs, 3, false, L);
 }
 
+int check_autotune_buffers(const basp_plan &p, const void *q, const void *k, const void *v,
+                           void *qkv, const void *o, void *o_out)
+{
+    // autotune runs both directions back to back on these buffers, so each
+    // output must be clear of every input of either call and of the other
+    // output, not only of its own call's input
+    const uint64_t qb = uint64_t(p.q_elems) * p.es, kb = uint64_t(p.kv_elems) * p.es;
+    const Buf ins[4] = {{q, qb}, {k, kb}, {v, kb}, {o, qb}};
+    const Buf outs[2] = {{qkv, qb + 2 * kb}, {o_out, qb}};
+    return check_buffers(p, ins, 4, outs, 2);
+}
+
 int prepare_seq_to_head_unfused(const basp_plan &p, const void *q, const void *k, const void *v,
                                 void *out, void *ws, PermLaunch L[3])
 {

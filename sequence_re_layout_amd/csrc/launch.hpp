@@ -264,5 +264,9 @@ int prepare_head_to_seq_qkv(const basp_plan &p, const void *in, void *dq, void *
                             TileLaunch &L);
 int prepare_seq_to_head_unfused(const basp_plan &p, const void *q, const void *k, const void *v,
                                 void *out, void *ws, PermLaunch L[3]);
+// NULL, alignment and overlap checks of the six buffers of basp_plan_autotune
+// taken together (each output against all four inputs and the other output).
+int check_autotune_buffers(const basp_plan &p, const void *q, const void *k, const void *v,
+                           void *qkv, const void *o, void *o_out);
 
 }  // namespace basp

@@ -192,6 +192,11 @@ extern "C" basp_status basp_plan_query(const basp_plan *p, basp_plan_info *info)
     r.cross_rank_bytes_kv = int64_t{p->N} * (p->P - 1) * r.per_peer_bytes_kv;
     r.qkv_bytes_moved = 2 * r.qkv_elems * p->es;
     r.o_bytes_moved = 2 * p->q_elems * p->es;
+    // the foil: Ulysses over groups of K = N/B ranks, each group holding all B
+    // sequences, so every rank keeps B*S/K = B*B*S/N tokens.  K divides the
+    // plan's group size P, so S/K is whole whenever the plan exists.
+    if (p->B <= p->N && p->N % p->B == 0)
+        r.tokens_per_rank_foil = int64_t{p->B} * (p->S / (p->N / p->B));
     *info = r;
     return record(BASP_OK);
 }

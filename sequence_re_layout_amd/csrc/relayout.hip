@@ -547,7 +547,9 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
         return record(BASP_ERR_INVALID);
     // the partner launches: each direction with the plan's shape on entry
     basp::TileLaunch partner[2];
-    int s = basp::prepare_seq_to_head(*p, q, k, v, qkv, partner[BASP_SEQ_TO_HEAD]);
+    int s = basp::check_autotune_buffers(*p, q, k, v, qkv, o, o_out);
+    if (s == BASP_OK)
+        s = basp::prepare_seq_to_head(*p, q, k, v, qkv, partner[BASP_SEQ_TO_HEAD]);
     if (s == BASP_OK)
         s = basp::prepare_head_to_seq(*p, o, o_out, partner[BASP_HEAD_TO_SEQ]);
     if (s != BASP_OK || p->S == 0)

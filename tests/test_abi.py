@@ -172,6 +172,12 @@ def test_pointer_checks_before_launch():
     assert lib.basp_plan_autotune(p.handle, q, k, v, q + 64, q, out, None) == b.BASP_ERR_ALIAS
     assert lib.basp_plan_autotune(p.handle, q, k, v, out, q + 1, ws, None) == b.BASP_ERR_ALIGN
     assert lib.basp_plan_autotune(None, q, k, v, out, q, ws, None) == b.BASP_ERR_INVALID
+    # the two calls run back to back, so each output is also checked against
+    # the other call's buffers: o_out over q, qkv over o, o_out over qkv
+    o = ws + 8 * qb
+    assert lib.basp_plan_autotune(p.handle, q, k, v, out, o, q, None) == b.BASP_ERR_ALIAS
+    assert lib.basp_plan_autotune(p.handle, q, k, v, out, out + 64, ws, None) == b.BASP_ERR_ALIAS
+    assert lib.basp_plan_autotune(p.handle, q, k, v, out, o, out + 2 * qb, None) == b.BASP_ERR_ALIAS
     # q, k and v may alias each other (inputs only)
     e = b.basp_plan_create(4, 2, 0, 8, 8, 64)
     assert lib.basp_seq_to_head(e.handle, None, None, None, None, None) == b.BASP_OK
@@ -231,3 +237,27 @@ def test_batch_fits_the_launch_grid():
     with pytest.raises(b.BaspError) as e:
         b.basp_plan_create(1, 65536, 1, 1, 1, 8, b.BASP_BF16, b.BASP_MODE_BASP)
     assert e.value.status == b.BASP_ERR_UNSUPPORTED
+
+
+def test_foil_tokens():
+    """tokens_per_rank_foil is the token count per rank of Ulysses run over
+    groups of N/B ranks that each hold the whole micro-batch: the page's
+    value at its own setting, and the count the oracle observes for that
+    configuration on other shapes."""
+    import json
+    facts = {f["id"]: f for f in json.load(open(os.path.join(ROOT, "tests", "golden", "page_facts.json")))["facts"]}
+    f = facts["foil_tokens"]
+    for m in MODES.values():
+        info = b.basp_plan_create(f["N"], f["B"], f["S"], 32, 8, 64, b.BASP_BF16, m).info
+        assert info["tokens_per_rank_foil"] == f["tokens_per_gpu_foil"]
+        assert info["tokens_per_rank"] == f["tokens_per_gpu_basp"]
+    for (N, B, S) in [(8, 4, 64), (8, 8, 16), (6, 3, 12), (4, 1, 8), (8, 2, 32)]:
+        K = N // B
+        x = np.zeros(B * S * K, dtype=np.uint16)
+        _, tm = oracle.seq_to_head(x, oracle.ULYSSES, K, B, S, K, 1, traffic=True)
+        observed = set(int(tm[r, :].sum()) // K for r in range(K))
+        info = b.basp_plan_create(N, B, S, 8, 8, 8, b.BASP_BF16, b.BASP_MODE_BASP).info
+        assert observed == {info["tokens_per_rank_foil"]}, (N, B, S)
+    # no foil where N/B is not whole: Ulysses with N % B != 0, or B > N
+    assert b.basp_plan_create(8, 3, 24, 8, 8, 8, b.BASP_BF16, b.BASP_MODE_ULYSSES).info["tokens_per_rank_foil"] == 0
+    assert b.basp_plan_create(8, 16, 8, 8, 8, 8, b.BASP_BF16, b.BASP_MODE_BASP).info["tokens_per_rank_foil"] == 0

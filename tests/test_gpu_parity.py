@@ -543,53 +543,165 @@ def _sample(n, rng, extra=()):
     return np.unique(np.array(pts, dtype=np.int64))
 
 
-def _check_sampled(out, ins, heads, direction, mode, N, B, S, d, rng):
-    """out (one buffer: the parts of ins re-laid one after another) against
-    the oracle's one-element source index on sampled destinations, bit for
-    bit, gathered on the device."""
-    o16 = out.view(torch.int16)
-    base = 0
-    for x, H in zip(ins, heads):
-        n = x.numel()
-        dst = _sample(n, rng)
-        src = oracle.source_index(direction, dst, mode, N, B, S, H, d)
-        got = o16[torch.from_numpy(dst + base).cuda()]
-        want = x.view(torch.int16)[torch.from_numpy(src).cuda()]
-        assert torch.equal(got, want), "part at element offset %d" % base
-        base += n
+# ------------------------------------- full size, the shapes the bench times --
+
+def split_tags(sizes):
+    """Two passes of bf16 device tensors of the given element counts.  Element
+    i of the tensors taken one after another (i counted across all of them)
+    carries the low 16 bits of i in the first pass and the high 16 bits in
+    the second, so the two outputs together name the source of every output
+    element (fewer than 2^32 elements)."""
+    total = sum(sizes)
+    assert total < 2**32
+    idx = torch.arange(total, dtype=torch.int64, device="cuda")
+    passes = []
+    for shift in (0, 16):
+        t = (((idx >> shift) & 0xFFFF) - 32768).to(torch.int16).view(torch.bfloat16)
+        parts, base = [], 0
+        for n in sizes:
+            parts.append(t[base:base + n])
+            base += n
+        passes.append(parts)
+    del idx
+    return passes
+
+
+def check_s2h_full(plan, mode, shape, ins, layout=0):
+    """Fused seq->head of device tensors ins = (q, k, v) against the oracle,
+    every element."""
+    N, B, S, Hq, Hkv, d = shape
+    i = plan.info
+    out = torch.empty(i["qkv_elems"], dtype=ins[0].dtype, device="cuda")
+    out.view(torch.int16 if out.element_size() == 2 else torch.int32).fill_(-1)
+    b.basp_seq_to_head(plan, *ins, out)
+    torch.cuda.synchronize()
+    want = oracle.seq_to_head_qkv(*(bits(x) for x in ins), MODE[mode], N, B, S, Hq, Hkv, d, layout)
+    bad = np.flatnonzero(bits(out) != want)
+    assert bad.size == 0, "seq->head: %d mismatches, first at %s" % (bad.size, bad[:8])
+
+
+def check_h2s_full(plan, mode, shape, o, layout=0):
+    """O head->seq of a device tensor o against the oracle, every element."""
+    N, B, S, Hq, Hkv, d = shape
+    out = torch.empty_like(o)
+    out.view(torch.int16 if out.element_size() == 2 else torch.int32).fill_(-1)
+    b.basp_head_to_seq(plan, o, out)
+    torch.cuda.synchronize()
+    want = oracle.head_to_seq(bits(o), MODE[mode], N, B, S, Hq, d, layout)
+    bad = np.flatnonzero(bits(out) != want)
+    assert bad.size == 0, "head->seq: %d mismatches, first at %s" % (bad.size, bad[:8])
+
+
+def check_split_tags(plan, mode, shape, layout=0):
+    """Both directions with the plan's current launch shapes, on both passes
+    of split tags, every element against the oracle."""
+    i = plan.info
+    for q, k, v in split_tags([i["q_elems"], i["kv_elems"], i["kv_elems"]]):
+        check_s2h_full(plan, mode, shape, (q, k, v), layout)
+    for (o,) in split_tags([i["q_elems"]]):
+        check_h2s_full(plan, mode, shape, o, layout)
 
 
 @pytest.mark.parametrize("mode", ["basp", "ulysses"])
 @pytest.mark.parametrize("w", workloads.ALL + workloads.EXTRA, ids=lambda w: w[0])
-def test_workload_autotuned_sampled(w, mode):
-    """Every named workload with the launch shapes autotune picks for it, as
-    the bench's table of every workload runs it: the outputs autotune leaves
-    and a fresh call of each direction, checked on sampled destinations
-    against the oracle's one-element source index."""
+def test_workload_table_shapes_split_tags(w, mode):
+    """Every named workload with the launch shapes of the measured table
+    (the ones the benchmark times), at full size: both passes of split tags,
+    both directions, every output element against the oracle."""
     needs_gpu()
-    _, N, B, S, Hq, Hkv, d = w
-    print("autotuned", w[0], mode, flush=True)
+    from sequence_re_layout_amd import launch_shapes
+    name, N, B, S, Hq, Hkv, d = w
+    print("table shapes", name, mode, launch_shapes.lookup(name, mode), flush=True)
+    plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, MODE[mode])
+    if not launch_shapes.apply(b, plan, name, mode):
+        pytest.skip("no table entry for %s %s" % (name, mode))
+    check_split_tags(plan, mode, w[1:])
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode", ["basp", "ulysses"])
+@pytest.mark.parametrize("w", workloads.ALL + workloads.EXTRA, ids=lambda w: w[0])
+def test_workload_autotuned_full_size(w, mode):
+    """Every named workload with the launch shapes autotune picks for it:
+    the outputs autotune leaves behind, then fresh calls of both directions
+    on both passes of split tags, every element against the oracle."""
+    needs_gpu()
+    name, N, B, S, Hq, Hkv, d = w
+    print("autotuned", name, mode, flush=True)
     m = MODE[mode]
     plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, m)
     i = plan.info
-    g = torch.Generator(device="cuda").manual_seed(5)
-    q, k, v, o = (torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_(generator=g)
-                  for n in (i["q_elems"], i["kv_elems"], i["kv_elems"], i["q_elems"]))
+    (q, k, v), = split_tags([i["q_elems"], i["kv_elems"], i["kv_elems"]])[:1]
+    (o,), = split_tags([i["q_elems"]])[1:]
     qkv = torch.empty(i["qkv_elems"], dtype=torch.bfloat16, device="cuda")
     o_out = torch.empty(i["q_elems"], dtype=torch.bfloat16, device="cuda")
     b.basp_plan_autotune(plan, q, k, v, qkv, o, o_out)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(13)
-    _check_sampled(qkv, (q, k, v), (Hq, Hkv, Hkv), 0, m, N, B, S, d, rng)
-    _check_sampled(o_out, (o,), (Hq,), 1, m, N, B, S, d, rng)
-    qkv.view(torch.int16).fill_(-1)
-    o_out.view(torch.int16).fill_(-1)
-    b.basp_seq_to_head(plan, q, k, v, qkv)
-    b.basp_head_to_seq(plan, o, o_out)
-    torch.cuda.synchronize()
-    _check_sampled(qkv, (q, k, v), (Hq, Hkv, Hkv), 0, m, N, B, S, d, rng)
-    _check_sampled(o_out, (o,), (Hq,), 1, m, N, B, S, d, rng)
-    del q, k, v, o, qkv, o_out
+    print("  picked", b.basp_plan_get_tuning(plan, b.BASP_SEQ_TO_HEAD),
+          b.basp_plan_get_tuning(plan, b.BASP_HEAD_TO_SEQ), flush=True)
+    want = oracle.seq_to_head_qkv(bits(q), bits(k), bits(v), m, N, B, S, Hq, Hkv, d)
+    assert np.array_equal(bits(qkv), want), "seq->head result autotune left"
+    assert np.array_equal(bits(o_out), oracle.head_to_seq(bits(o), m, N, B, S, Hq, d)), \
+        "head->seq result autotune left"
+    del q, k, v, o, qkv, o_out, want
+    check_split_tags(plan, mode, w[1:])
+    torch.cuda.empty_cache()
+
+
+STAGED = [dict(stage=2, block_size=64, vectors_per_thread=1, tile_heads=2),
+          dict(stage=2, block_size=256, vectors_per_thread=2, tile_heads=4, tile_order=1, batch_order=2),
+          dict(stage=2, block_size=128, vectors_per_thread=1, tile_heads=1, xcd_remap=2)]
+
+
+@pytest.mark.parametrize("mode", ["basp", "ulysses"])
+@pytest.mark.parametrize("tuning", STAGED, ids=lambda t: ",".join("%s=%s" % kv for kv in t.items()))
+@pytest.mark.parametrize("w", [workloads.LONG_CONTEXT[-1], workloads.DP_FALLBACK], ids=lambda w: w[0])
+def test_staged_full_size(w, tuning, mode):
+    """The LDS-staged kernel at full size on the largest named workload and on
+    the data-parallel fallback, both directions, both modes, split tags."""
+    needs_gpu()
+    name, N, B, S, Hq, Hkv, d = w
+    print("staged", name, mode, tuning, flush=True)
+    plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, MODE[mode])
+    b.basp_plan_set_tuning(plan, **tuning)
+    check_split_tags(plan, mode, w[1:])
+    torch.cuda.empty_cache()
+
+
+def _global_tags(B, S, H, d, base):
+    """int32 tags of a global [B][S][H][d] tensor: base + ((b*S + s)*H + h)*d + e."""
+    return torch.arange(base, base + B * S * H * d, dtype=torch.int32, device="cuda").view(B, S, H, d)
+
+
+@pytest.mark.parametrize("mode", ["basp", "ulysses"])
+@pytest.mark.parametrize("w", [workloads.LLAMA_1B, workloads.LONG_CONTEXT[-1]], ids=lambda w: w[0])
+def test_int32_global_tags_full_size(w, mode):
+    """int32 elements tagged with their (tensor, b, s, h, e) as the linear
+    index into the global [Q||K||V] tensor (below 2^31 at every named
+    workload), scattered into the mode's sequence-sharded buffers by the
+    ownership rules, re-laid at full size in both directions with the table's
+    shapes (built-in where the table has none for int32), every element
+    against the oracle."""
+    needs_gpu()
+    name, N, B, S, Hq, Hkv, d = w
+    print("int32 global tags", name, mode, flush=True)
+    plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_INT32, MODE[mode])
+    i = plan.info
+    G, P, Bl = i["G"], i["P"], i["Bl"]
+    assert i["qkv_elems"] < 2**31
+    nq, nkv = i["q_elems"], i["kv_elems"]
+    ins = []
+    for base, H in ((0, Hq), (nq, Hkv), (nq + nkv, Hkv)):
+        x = _global_tags(B, S, H, d, base)
+        ins.append(x.view(G, Bl, P, S // P, H, d).permute(0, 2, 1, 3, 4, 5).contiguous().view(-1))
+        del x
+    check_s2h_full(plan, mode, w[1:], ins)
+    del ins
+    x = _global_tags(B, S, Hq, d, 0)
+    o = x.view(G, Bl, S, P, Hq // P, d).permute(0, 3, 1, 4, 2, 5).contiguous().view(-1)
+    del x
+    check_h2s_full(plan, mode, w[1:], o)
+    del o
     torch.cuda.empty_cache()
 
 
