@@ -28,6 +28,7 @@ from . import build as _build
 
 ULYSSES = 0
 BASP = 1
+GROUPS = 2   # the general form: G groups given explicitly (keyword G)
 HEAD_MAJOR = 0
 TOKEN_MAJOR = 1
 
@@ -41,13 +42,13 @@ def _load():
             _build.build()
         lib = ctypes.CDLL(_build.LIB)
         i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
-        lib.orc_groups.argtypes = [i32, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64),
+        lib.orc_groups.argtypes = [i32, i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64),
                                    ctypes.POINTER(i64)]
         lib.orc_groups.restype = i32
         for fn in (lib.orc_seq_to_head, lib.orc_head_to_seq):
-            fn.argtypes = [i32, i32, i64, i64, i64, i64, i64, i64, vp, vp, vp, i32]
+            fn.argtypes = [i32, i64, i32, i64, i64, i64, i64, i64, i64, vp, vp, vp, i32]
             fn.restype = i32
-        lib.orc_source_index.argtypes = [i32, i32, i32, i64, i64, i64, i64, i64, vp, vp, i64]
+        lib.orc_source_index.argtypes = [i32, i32, i64, i32, i64, i64, i64, i64, i64, vp, vp, i64]
         lib.orc_source_index.restype = i32
         lib.orc_max_threads.argtypes = []
         lib.orc_max_threads.restype = i32
@@ -69,75 +70,77 @@ def max_threads() -> int:
     return int(_load().orc_max_threads())
 
 
-def groups(mode: int, N: int, B: int):
-    """(G, P, Bl) of the scheme, or None when the pages' conditions fail."""
-    G, P, Bl = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
-    rc = _load().orc_groups(mode, N, B, ctypes.byref(G), ctypes.byref(P), ctypes.byref(Bl))
+def groups(mode: int, N: int, B: int, G: int = 0):
+    """(G, P, Bl) of the scheme (G: the number of groups of mode GROUPS), or
+    None when the pages' conditions fail."""
+    g, P, Bl = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    rc = _load().orc_groups(mode, G, N, B, ctypes.byref(g), ctypes.byref(P), ctypes.byref(Bl))
     if rc != 0:
         return None
-    return G.value, P.value, Bl.value
+    return g.value, P.value, Bl.value
 
 
 def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
-def _run(fn, x, mode, layout, N, B, S, H, d, traffic, threads):
+def _run(fn, x, mode, layout, N, B, S, H, d, traffic, threads, G):
     x = np.ascontiguousarray(x).reshape(-1)
     if x.size != B * S * H * d:
         raise ValueError("input holds %d elements, expected B*S*H*d = %d" % (x.size, B * S * H * d))
     out = np.empty_like(x)
     tm = np.zeros((N, N), dtype=np.int64) if traffic else None
     threads = max_threads() if threads is None else threads
-    rc = fn(mode, layout, N, B, S, H, d, x.itemsize, _ptr(x), _ptr(out),
+    rc = fn(mode, G, layout, N, B, S, H, d, x.itemsize, _ptr(x), _ptr(out),
             _ptr(tm) if traffic else None, threads)
     if rc != 0:
-        raise ValueError("oracle rejected mode=%d layout=%d N=%d B=%d S=%d H=%d d=%d"
-                         % (mode, layout, N, B, S, H, d))
+        raise ValueError("oracle rejected mode=%d G=%d layout=%d N=%d B=%d S=%d H=%d d=%d"
+                         % (mode, G, layout, N, B, S, H, d))
     return (out, tm) if traffic else out
 
 
-def seq_to_head(x, mode, N, B, S, H, d, layout=HEAD_MAJOR, traffic=False, threads=None):
+def seq_to_head(x, mode, N, B, S, H, d, layout=HEAD_MAJOR, traffic=False, threads=None, G=0):
     """One tensor, sequence-sharded -> head-sharded.  With ``traffic`` also
-    returns the N x N matrix of elements moved from rank i to rank j."""
-    return _run(_load().orc_seq_to_head, x, mode, layout, N, B, S, H, d, traffic, threads)
+    returns the N x N matrix of elements moved from rank i to rank j.  G is
+    the number of groups of mode GROUPS."""
+    return _run(_load().orc_seq_to_head, x, mode, layout, N, B, S, H, d, traffic, threads, G)
 
 
-def head_to_seq(x, mode, N, B, S, H, d, layout=HEAD_MAJOR, traffic=False, threads=None):
+def head_to_seq(x, mode, N, B, S, H, d, layout=HEAD_MAJOR, traffic=False, threads=None, G=0):
     """One tensor, head-sharded -> sequence-sharded (the inverse exchange)."""
-    return _run(_load().orc_head_to_seq, x, mode, layout, N, B, S, H, d, traffic, threads)
+    return _run(_load().orc_head_to_seq, x, mode, layout, N, B, S, H, d, traffic, threads, G)
 
 
-def source_index(direction, dst, mode, N, B, S, H, d, layout=HEAD_MAJOR):
+def source_index(direction, dst, mode, N, B, S, H, d, layout=HEAD_MAJOR, G=0):
     """Source element offsets of the destination element offsets ``dst`` of a
     one-tensor call (direction 0: seq->head, 1: head->seq), one element at a
     time, for sampled checks at sizes the full loop does not reach."""
     dst = np.ascontiguousarray(dst, dtype=np.int64)
     src = np.empty_like(dst)
-    rc = _load().orc_source_index(direction, mode, layout, N, B, S, H, d, _ptr(dst), _ptr(src), dst.size)
+    rc = _load().orc_source_index(direction, mode, G, layout, N, B, S, H, d, _ptr(dst), _ptr(src), dst.size)
     if rc != 0:
         raise ValueError("oracle rejected the arguments or an offset")
     return src
 
 
-def seq_to_head_qkv(q, k, v, mode, N, B, S, Hq, Hkv, d, layout=HEAD_MAJOR, threads=None):
+def seq_to_head_qkv(q, k, v, mode, N, B, S, Hq, Hkv, d, layout=HEAD_MAJOR, threads=None, G=0):
     """Fused Q/K/V seq->head: HEAD(Q) || HEAD(K) || HEAD(V) in one array."""
-    parts = [seq_to_head(q, mode, N, B, S, Hq, d, layout, threads=threads),
-             seq_to_head(k, mode, N, B, S, Hkv, d, layout, threads=threads),
-             seq_to_head(v, mode, N, B, S, Hkv, d, layout, threads=threads)]
+    parts = [seq_to_head(q, mode, N, B, S, Hq, d, layout, threads=threads, G=G),
+             seq_to_head(k, mode, N, B, S, Hkv, d, layout, threads=threads, G=G),
+             seq_to_head(v, mode, N, B, S, Hkv, d, layout, threads=threads, G=G)]
     return np.concatenate(parts)
 
 
-def head_to_seq_qkv(x, mode, N, B, S, Hq, Hkv, d, layout=HEAD_MAJOR, threads=None):
+def head_to_seq_qkv(x, mode, N, B, S, Hq, Hkv, d, layout=HEAD_MAJOR, threads=None, G=0):
     """Fused inverse for the gradients dQ/dK/dV: splits HEAD(dQ) || HEAD(dK) ||
     HEAD(dV) and returns the three sequence-sharded arrays."""
     x = np.ascontiguousarray(x).reshape(-1)
     nq, nkv = B * S * Hq * d, B * S * Hkv * d
     if x.size != nq + 2 * nkv:
         raise ValueError("fused input holds %d elements, expected %d" % (x.size, nq + 2 * nkv))
-    return (head_to_seq(x[:nq], mode, N, B, S, Hq, d, layout, threads=threads),
-            head_to_seq(x[nq:nq + nkv], mode, N, B, S, Hkv, d, layout, threads=threads),
-            head_to_seq(x[nq + nkv:], mode, N, B, S, Hkv, d, layout, threads=threads))
+    return (head_to_seq(x[:nq], mode, N, B, S, Hq, d, layout, threads=threads, G=G),
+            head_to_seq(x[nq:nq + nkv], mode, N, B, S, Hkv, d, layout, threads=threads, G=G),
+            head_to_seq(x[nq + nkv:], mode, N, B, S, Hkv, d, layout, threads=threads, G=G))
 
 
 # ---------------------------------------------------------------- NumPy ---
@@ -151,8 +154,8 @@ def head_to_seq_qkv(x, mode, N, B, S, Hq, Hkv, d, layout=HEAD_MAJOR, threads=Non
 #   token-major buffer       (g, jh, bl, js, t, hl, e)   shape (G, P, Bl, P, St, Hl, d)
 # where member js holds tokens js*St + t and member jh holds heads jh*Hl + hl.
 
-def _numpy_shapes(mode, N, B, S, H, d):
-    gpb = groups(mode, N, B)
+def _numpy_shapes(mode, N, B, S, H, d, G=0):
+    gpb = groups(mode, N, B, G)
     if gpb is None or S % gpb[1] or H % gpb[1]:
         raise ValueError("the pages' conditions do not hold for mode=%d N=%d B=%d S=%d H=%d"
                          % (mode, N, B, S, H))
@@ -160,17 +163,17 @@ def _numpy_shapes(mode, N, B, S, H, d):
     return G, P, Bl, S // P, H // P
 
 
-def numpy_seq_to_head(x, mode, N, B, S, H, d, layout=HEAD_MAJOR):
+def numpy_seq_to_head(x, mode, N, B, S, H, d, layout=HEAD_MAJOR, G=0):
     """Sequence-sharded -> head-sharded as one transpose of the rank-major buffer."""
-    G, P, Bl, St, Hl = _numpy_shapes(mode, N, B, S, H, d)
+    G, P, Bl, St, Hl = _numpy_shapes(mode, N, B, S, H, d, G)
     a = np.asarray(x).reshape(G, P, Bl, St, P, Hl, d)
     axes = (0, 4, 2, 5, 1, 3, 6) if layout == HEAD_MAJOR else (0, 4, 2, 1, 3, 5, 6)
     return np.ascontiguousarray(a.transpose(axes)).reshape(-1)
 
 
-def numpy_head_to_seq(x, mode, N, B, S, H, d, layout=HEAD_MAJOR):
+def numpy_head_to_seq(x, mode, N, B, S, H, d, layout=HEAD_MAJOR, G=0):
     """Head-sharded -> sequence-sharded, the inverse transpose."""
-    G, P, Bl, St, Hl = _numpy_shapes(mode, N, B, S, H, d)
+    G, P, Bl, St, Hl = _numpy_shapes(mode, N, B, S, H, d, G)
     if layout == HEAD_MAJOR:
         a = np.asarray(x).reshape(G, P, Bl, Hl, P, St, d)
         axes = (0, 4, 2, 5, 1, 3, 6)

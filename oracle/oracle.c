@@ -45,6 +45,11 @@
  *   Ulysses:          G = 1, P = N,   Bl = B
  *   BASP, B <= N:     G = B, P = N/B, Bl = 1
  *   BASP, B >  N:     G = N, P = 1,   Bl = B/N
+ *   G groups:         G,     P = N/G, Bl = B/G   (G divides N and B)
+ * The last line is the form the work equality is stated for: G groups of
+ * P = N/G GPUs, each group holding B/G of the sequences, so that every GPU
+ * holds (B/G) sequences x (S*G/N) tokens x H heads x d channels whatever G
+ * is.  The two schemes are its cases G = 1 and G = B.
  *
  * The re-layout moves elements without changing them (model accuracy is
  * unchanged, [abs, Abstract]), so the oracle copies raw bytes of es bytes
@@ -57,15 +62,25 @@
 #include <stdint.h>
 #include <string.h>
 
-enum { ORC_ULYSSES = 0, ORC_BASP = 1 };
+enum { ORC_ULYSSES = 0, ORC_BASP = 1, ORC_GROUPS = 2 };
 enum { ORC_HEAD_MAJOR = 0, ORC_TOKEN_MAJOR = 1 };
 
-/* Group structure of the two schemes, see the header comment.
+/* Group structure of the schemes, see the header comment.  G_req is the
+ * number of groups of ORC_GROUPS (ignored by the other modes).
  * Returns 0, or -1 when the pages' conditions do not hold. */
-int orc_groups(int mode, int64_t N, int64_t B, int64_t *G, int64_t *P, int64_t *Bl)
+int orc_groups(int mode, int64_t G_req, int64_t N, int64_t B, int64_t *G, int64_t *P, int64_t *Bl)
 {
     if (N <= 0 || B <= 0)
         return -1;
+    if (mode == ORC_GROUPS) {
+        /* G groups of N/G consecutive ranks, each owning B/G sequences */
+        if (G_req <= 0 || N % G_req != 0 || B % G_req != 0)
+            return -1;
+        *G = G_req;
+        *P = N / G_req;
+        *Bl = B / G_req;
+        return 0;
+    }
     if (mode == ORC_ULYSSES) {
         *G = 1;
         *P = N;
@@ -92,10 +107,10 @@ int orc_groups(int mode, int64_t N, int64_t B, int64_t *G, int64_t *P, int64_t *
 
 /* Shared argument check: the group structure exists, tokens and heads split
  * evenly over the P members of a group, and sizes are sane. */
-static int check(int mode, int layout, int64_t N, int64_t B, int64_t S, int64_t H,
-                 int64_t d, int64_t es, int64_t *G, int64_t *P, int64_t *Bl)
+static int check(int mode, int64_t G_req, int layout, int64_t N, int64_t B, int64_t S,
+                 int64_t H, int64_t d, int64_t es, int64_t *G, int64_t *P, int64_t *Bl)
 {
-    if (orc_groups(mode, N, B, G, P, Bl) != 0)
+    if (orc_groups(mode, G_req, N, B, G, P, Bl) != 0)
         return -1;
     if (layout != ORC_HEAD_MAJOR && layout != ORC_TOKEN_MAJOR)
         return -1;
@@ -142,12 +157,12 @@ static void copy_element(void *dst, int64_t di, const void *src, int64_t si, int
  * traffic[src_rank * N + dst_rank]; it is filled with one thread.
  * Returns 0, or -1 on invalid arguments.
  */
-int orc_seq_to_head(int mode, int layout, int64_t N, int64_t B, int64_t S, int64_t H,
-                    int64_t d, int64_t es, const void *in, void *out, int64_t *traffic,
-                    int threads)
+int orc_seq_to_head(int mode, int64_t G_req, int layout, int64_t N, int64_t B, int64_t S,
+                    int64_t H, int64_t d, int64_t es, const void *in, void *out,
+                    int64_t *traffic, int threads)
 {
     int64_t G, P, Bl;
-    if (check(mode, layout, N, B, S, H, d, es, &G, &P, &Bl) != 0)
+    if (check(mode, G_req, layout, N, B, S, H, d, es, &G, &P, &Bl) != 0)
         return -1;
     const int64_t St = S / P, Hl = H / P;
     if (traffic)
@@ -183,12 +198,12 @@ int orc_seq_to_head(int mode, int layout, int64_t N, int64_t B, int64_t S, int64
  * the token is s = j*St + t (R2), the head h sits on group member h / Hl at
  * local head h % Hl (R2), and that member is rank g*P + h/Hl (R1).
  */
-int orc_head_to_seq(int mode, int layout, int64_t N, int64_t B, int64_t S, int64_t H,
-                    int64_t d, int64_t es, const void *in, void *out, int64_t *traffic,
-                    int threads)
+int orc_head_to_seq(int mode, int64_t G_req, int layout, int64_t N, int64_t B, int64_t S,
+                    int64_t H, int64_t d, int64_t es, const void *in, void *out,
+                    int64_t *traffic, int threads)
 {
     int64_t G, P, Bl;
-    if (check(mode, layout, N, B, S, H, d, es, &G, &P, &Bl) != 0)
+    if (check(mode, G_req, layout, N, B, S, H, d, es, &G, &P, &Bl) != 0)
         return -1;
     const int64_t St = S / P, Hl = H / P;
     if (traffic)
@@ -223,11 +238,11 @@ int orc_head_to_seq(int mode, int layout, int64_t N, int64_t B, int64_t S, int64
  * outputs where the whole loop is too large.  Returns 0, or -1 on invalid
  * arguments or an offset outside the tensor.
  */
-int orc_source_index(int direction, int mode, int layout, int64_t N, int64_t B, int64_t S,
-                     int64_t H, int64_t d, const int64_t *dst, int64_t *src, int64_t n)
+int orc_source_index(int direction, int mode, int64_t G_req, int layout, int64_t N, int64_t B,
+                     int64_t S, int64_t H, int64_t d, const int64_t *dst, int64_t *src, int64_t n)
 {
     int64_t G, P, Bl;
-    if (check(mode, layout, N, B, S, H, d, 2, &G, &P, &Bl) != 0)
+    if (check(mode, G_req, layout, N, B, S, H, d, 2, &G, &P, &Bl) != 0)
         return -1;
     (void)G;
     const int64_t St = S / P, Hl = H / P, total = B * S * H * d;

@@ -17,6 +17,11 @@ What each check compares with (none re-types the oracle's formulas):
 * ``check_round_trip``: head->seq undoes seq->head and the reverse.
 * ``check_b1_is_ulysses``: BASP at B = 1 is Ulysses (the degeneracy of the
   review page, "Strengths", the paper's Fig. 8).
+* ``check_groups_special_cases``: the general G-group form (review page,
+  "Strengths"; the paper's Sec. IV.C) is Ulysses at G = 1, BASP at G = B and
+  the data-parallel fallback at G = N, bit for bit with equal exchange
+  matrices.  Its group structure itself is taken from its definition (G
+  groups of N/G ranks, B/G sequences each), not from the oracle.
 * ``check_k1_local_transpose``: BASP at B = N (K = 1) moves nothing between
   ranks; each rank's result is the textbook transpose [S][H][d] -> [H][S][d].
 * ``check_traffic``: observed exchange matrix against the pages' counts:
@@ -35,7 +40,20 @@ import itertools
 import numpy as np
 
 import oracle
-from oracle import BASP, HEAD_MAJOR, TOKEN_MAJOR, ULYSSES
+from oracle import BASP, GROUPS, HEAD_MAJOR, TOKEN_MAJOR, ULYSSES
+
+
+def structure(mode, N, B, G=0):
+    """(G, P, Bl).  For the two schemes from the oracle (their group rules
+    are pinned by check_traffic, check_rejects and the page facts); for the
+    general form straight from its definition -- G groups of N/G
+    consecutive ranks, each holding B/G sequences -- after checking that the
+    oracle agrees."""
+    if mode == GROUPS:
+        want = (G, N // G, B // G)
+        assert oracle.groups(GROUPS, N, B, G) == want, (N, B, G, oracle.groups(GROUPS, N, B, G))
+        return want
+    return oracle.groups(mode, N, B)
 
 
 # ---------------------------------------------------------------- layouts ---
@@ -57,19 +75,22 @@ def np_head_layout(X, G, P, Bl, layout=HEAD_MAJOR):
 
 
 def shapes_tiny():
-    """Exhaustive grid of tiny valid cases: (mode, N, B, S, H, d)."""
+    """Exhaustive grid of tiny valid cases: (mode, N, B, S, H, d, G), G the
+    number of groups of the general form (0 for the two schemes)."""
     out = []
     for N in (1, 2, 3, 4, 6, 8):
-        for B in (1, 2, 3, 4, 8, 16):
-            for mode in (ULYSSES, BASP):
-                g = oracle.groups(mode, N, B)
+        for B in (1, 2, 3, 4, 6, 8, 16):
+            modes = [(ULYSSES, 0), (BASP, 0)] + [(GROUPS, G) for G in range(1, N + 1)
+                                                 if N % G == 0 and B % G == 0]
+            for mode, G in modes:
+                g = oracle.groups(mode, N, B, G)
                 if g is None:
                     continue
                 P = g[1]
                 for S in sorted({P, 2 * P, 3 * P}):
                     for H in sorted({P, 2 * P}):
                         for d in (1, 3):
-                            out.append((mode, N, B, S, H, d))
+                            out.append((mode, N, B, S, H, d, G))
     return out
 
 
@@ -84,18 +105,22 @@ def check_numpy_layouts(cases=None, seed=0):
         (ULYSSES, 8, 2, 16, 8, 2), (BASP, 8, 4, 8, 6, 3), (ULYSSES, 6, 3, 12, 6, 5),
         (BASP, 6, 3, 12, 4, 2), (BASP, 4, 8, 4, 3, 2), (BASP, 8, 8, 8, 4, 2),
         (ULYSSES, 2, 1, 6, 4, 3), (BASP, 1, 1, 5, 3, 2),
+        (GROUPS, 8, 8, 8, 4, 2, 2), (GROUPS, 8, 4, 8, 4, 3, 2), (GROUPS, 6, 4, 6, 3, 2, 2),
+        (GROUPS, 12, 6, 12, 8, 2, 3), (GROUPS, 8, 16, 4, 2, 2, 4), (GROUPS, 4, 6, 4, 2, 3, 2),
     ]
-    for (mode, N, B, S, H, d) in cases:
-        G, P, Bl = oracle.groups(mode, N, B)
+    for c in cases:
+        mode, N, B, S, H, d = c[:6]
+        Gq = c[6] if len(c) > 6 else 0
+        G, P, Bl = structure(mode, N, B, Gq)
         for dtype in (np.uint16, np.uint32):
             X = _rng_array((B, S, H, d), rng, dtype)
             seq = np_seq_layout(X, G, P, Bl)
             for layout in (HEAD_MAJOR, TOKEN_MAJOR):
                 head = np_head_layout(X, G, P, Bl, layout)
-                got = oracle.seq_to_head(seq, mode, N, B, S, H, d, layout)
-                assert np.array_equal(got, head), ("s2h", mode, N, B, S, H, d, layout, dtype)
-                back = oracle.head_to_seq(head, mode, N, B, S, H, d, layout)
-                assert np.array_equal(back, seq), ("h2s", mode, N, B, S, H, d, layout, dtype)
+                got = oracle.seq_to_head(seq, mode, N, B, S, H, d, layout, G=Gq)
+                assert np.array_equal(got, head), ("s2h", c, layout, dtype)
+                back = oracle.head_to_seq(head, mode, N, B, S, H, d, layout, G=Gq)
+                assert np.array_equal(back, seq), ("h2s", c, layout, dtype)
 
 
 # ------------------------------------------------------- tagged brute force --
@@ -128,29 +153,32 @@ def _brute_shards(B, S, H, d, G, P, Bl, layout):
 
 
 def check_tagged_brute_force(cases=None):
-    for (mode, N, B, S, H, d) in (cases or shapes_tiny()):
-        G, P, Bl = oracle.groups(mode, N, B)
+    for (mode, N, B, S, H, d, Gq) in (cases or shapes_tiny()):
+        G, P, Bl = structure(mode, N, B, Gq)
         for layout in (HEAD_MAJOR, TOKEN_MAJOR):
             seq, head = _brute_shards(B, S, H, d, G, P, Bl, layout)
-            got = oracle.seq_to_head(seq, mode, N, B, S, H, d, layout)
-            assert np.array_equal(got, head), ("s2h", mode, N, B, S, H, d, layout)
-            back = oracle.head_to_seq(head, mode, N, B, S, H, d, layout)
-            assert np.array_equal(back, seq), ("h2s", mode, N, B, S, H, d, layout)
+            got = oracle.seq_to_head(seq, mode, N, B, S, H, d, layout, G=Gq)
+            assert np.array_equal(got, head), ("s2h", mode, N, B, S, H, d, Gq, layout)
+            back = oracle.head_to_seq(head, mode, N, B, S, H, d, layout, G=Gq)
+            assert np.array_equal(back, seq), ("h2s", mode, N, B, S, H, d, Gq, layout)
 
 
 # ------------------------------------------------------------- invariants ---
 
 def check_round_trip(seed=1):
     rng = np.random.default_rng(seed)
-    for (mode, N, B, S, H, d) in [(BASP, 8, 2, 32, 8, 4), (ULYSSES, 8, 2, 32, 8, 4),
+    for c in [(BASP, 8, 2, 32, 8, 4), (ULYSSES, 8, 2, 32, 8, 4),
                                   (BASP, 6, 2, 18, 9, 3), (BASP, 4, 8, 4, 2, 2),
-                                  (ULYSSES, 3, 5, 9, 6, 2)]:
+                                  (ULYSSES, 3, 5, 9, 6, 2), (GROUPS, 8, 8, 16, 4, 3, 2),
+                                  (GROUPS, 6, 4, 12, 6, 2, 2)]:
+        mode, N, B, S, H, d = c[:6]
         x = _rng_array(B * S * H * d, rng)
+        G = c[6] if len(c) > 6 else 0
         for layout in (HEAD_MAJOR, TOKEN_MAJOR):
-            y = oracle.seq_to_head(x, mode, N, B, S, H, d, layout)
-            assert np.array_equal(oracle.head_to_seq(y, mode, N, B, S, H, d, layout), x)
-            z = oracle.head_to_seq(x, mode, N, B, S, H, d, layout)
-            assert np.array_equal(oracle.seq_to_head(z, mode, N, B, S, H, d, layout), x)
+            y = oracle.seq_to_head(x, mode, N, B, S, H, d, layout, G=G)
+            assert np.array_equal(oracle.head_to_seq(y, mode, N, B, S, H, d, layout, G=G), x)
+            z = oracle.head_to_seq(x, mode, N, B, S, H, d, layout, G=G)
+            assert np.array_equal(oracle.seq_to_head(z, mode, N, B, S, H, d, layout, G=G), x)
 
 
 def check_b1_is_ulysses(seed=2):
@@ -180,19 +208,26 @@ def check_k1_local_transpose(seed=3):
 
 def check_traffic():
     """Exchange matrix observed by the oracle against the pages' counts."""
-    for (mode, N, B, S, H, d) in [(BASP, 8, 2, 16, 8, 2), (ULYSSES, 8, 2, 16, 8, 2),
-                                  (BASP, 8, 4, 8, 4, 3), (BASP, 8, 8, 8, 4, 1),
-                                  (ULYSSES, 4, 2, 8, 4, 2), (BASP, 6, 2, 6, 3, 2),
-                                  (BASP, 4, 8, 4, 2, 2)]:
-        G, P, Bl = oracle.groups(mode, N, B)
+    for c in [(BASP, 8, 2, 16, 8, 2), (ULYSSES, 8, 2, 16, 8, 2),
+              (BASP, 8, 4, 8, 4, 3), (BASP, 8, 8, 8, 4, 1),
+              (ULYSSES, 4, 2, 8, 4, 2), (BASP, 6, 2, 6, 3, 2),
+              (BASP, 4, 8, 4, 2, 2), (GROUPS, 8, 8, 16, 8, 2, 2), (GROUPS, 8, 8, 16, 8, 1, 4),
+              (GROUPS, 6, 4, 12, 6, 2, 2), (GROUPS, 8, 16, 4, 2, 1, 4)]:
+        mode, N, B, S, H, d = c[:6]
+        Gq = c[6] if len(c) > 6 else 0
+        G, P, Bl = structure(mode, N, B, Gq)
         x = np.zeros(B * S * H * d, dtype=np.uint16)
         for fn in (oracle.seq_to_head, oracle.head_to_seq):
-            _, tm = fn(x, mode, N, B, S, H, d, traffic=True)
+            _, tm = fn(x, mode, N, B, S, H, d, traffic=True, G=Gq)
             for r in range(N):
                 peers = [i for i in range(N) if i != r and tm[i, r] > 0]
-                # peers K-1 (BASP) vs N-1 (Ulysses): the group size minus one
-                expect_peers = (N // B - 1) if (mode == BASP and B <= N) else (
-                    0 if mode == BASP else N - 1)
+                # peers K-1 (BASP) vs N-1 (Ulysses): the group size minus one;
+                # G groups of N/G ranks: N/G - 1
+                if mode == GROUPS:
+                    expect_peers = N // Gq - 1
+                else:
+                    expect_peers = (N // B - 1) if (mode == BASP and B <= N) else (
+                        0 if mode == BASP else N - 1)
                 assert len(peers) == expect_peers, (mode, N, B, r, peers)
                 # all peers lie in r's group of contiguous ranks
                 assert all(i // P == r // P for i in peers)
@@ -210,13 +245,13 @@ def check_traffic():
 
 def check_bijection(seed=4):
     rng = np.random.default_rng(seed)
-    for (mode, N, B, S, H, d) in [(BASP, 8, 2, 16, 8, 3), (ULYSSES, 8, 2, 16, 8, 3),
-                                  (BASP, 4, 8, 8, 4, 2)]:
+    for (mode, N, B, S, H, d, G) in [(BASP, 8, 2, 16, 8, 3, 0), (ULYSSES, 8, 2, 16, 8, 3, 0),
+                                     (BASP, 4, 8, 8, 4, 2, 0), (GROUPS, 8, 4, 8, 4, 3, 2)]:
         n = B * S * H * d
         x = rng.permutation(n).astype(np.uint32)
         for fn in (oracle.seq_to_head, oracle.head_to_seq):
             for layout in (HEAD_MAJOR, TOKEN_MAJOR):
-                y = fn(x, mode, N, B, S, H, d, layout)
+                y = fn(x, mode, N, B, S, H, d, layout, G=G)
                 assert np.array_equal(np.sort(y), np.arange(n, dtype=np.uint32))
 
 
@@ -235,6 +270,11 @@ def check_rejects():
     assert oracle.groups(BASP, 8, 3) is None          # N not a multiple of B
     assert oracle.groups(BASP, 8, 12) is None         # B > N, not whole sequences
     assert oracle.groups(BASP, 8, 16) == (8, 1, 2)    # data-parallel fallback
+    # the general form needs G to divide both the ranks and the sequences
+    assert oracle.groups(GROUPS, 8, 8, 3) is None     # N % G
+    assert oracle.groups(GROUPS, 8, 6, 4) is None     # B % G
+    assert oracle.groups(GROUPS, 8, 8, 0) is None
+    assert oracle.groups(GROUPS, 8, 8, 16) is None    # more groups than ranks
     x = np.zeros(2 * 8 * 6 * 2, dtype=np.uint16)
     for args in [(BASP, 8, 2, 8, 6, 2),   # 6 heads over K = 4 members
                  (ULYSSES, 8, 2, 8, 6, 2)]:
@@ -250,19 +290,42 @@ def check_source_index_matches_loop(seed=6):
     """The one-element form names, for every destination, the element the
     full loop copies there (tags make the source readable from the output)."""
     rng = np.random.default_rng(seed)
-    for (mode, N, B, S, H, d) in [(BASP, 8, 2, 16, 8, 3), (ULYSSES, 6, 3, 12, 6, 2), (BASP, 4, 8, 4, 2, 5)]:
+    for (mode, N, B, S, H, d, G) in [(BASP, 8, 2, 16, 8, 3, 0), (ULYSSES, 6, 3, 12, 6, 2, 0),
+                                     (BASP, 4, 8, 4, 2, 5, 0), (GROUPS, 8, 8, 8, 4, 3, 2),
+                                     (GROUPS, 6, 4, 6, 3, 2, 2)]:
         n = B * S * H * d
         tags = np.arange(n, dtype=np.uint32)
         dst = rng.integers(0, n, size=500)
         for layout in (HEAD_MAJOR, TOKEN_MAJOR):
             for direction, fn in ((0, oracle.seq_to_head), (1, oracle.head_to_seq)):
-                out = fn(tags, mode, N, B, S, H, d, layout)
-                src = oracle.source_index(direction, dst, mode, N, B, S, H, d, layout)
+                out = fn(tags, mode, N, B, S, H, d, layout, G=G)
+                src = oracle.source_index(direction, dst, mode, N, B, S, H, d, layout, G=G)
                 assert np.array_equal(out[dst], src.astype(np.uint32)), (mode, layout, direction)
 
 
+def check_groups_special_cases(seed=7):
+    """G = 1 is Ulysses, G = B (B <= N) is BASP, G = N (B > N) is the
+    data-parallel fallback: equal outputs and equal exchange matrices, both
+    directions and layouts."""
+    rng = np.random.default_rng(seed)
+    for (N, B, S, H, d) in [(8, 2, 16, 8, 2), (8, 8, 8, 8, 3), (6, 3, 12, 6, 2), (4, 8, 4, 4, 2),
+                            (8, 4, 16, 8, 1), (2, 6, 6, 2, 3)]:
+        x = _rng_array(B * S * H * d, rng)
+        pairs = [(1, ULYSSES)]
+        if B <= N and N % B == 0:
+            pairs.append((B, BASP))
+        if B > N and B % N == 0:
+            pairs.append((N, BASP))
+        for G, mode in pairs:
+            for layout in (HEAD_MAJOR, TOKEN_MAJOR):
+                for fn in (oracle.seq_to_head, oracle.head_to_seq):
+                    a, ta = fn(x, GROUPS, N, B, S, H, d, layout, traffic=True, G=G)
+                    b, tb = fn(x, mode, N, B, S, H, d, layout, traffic=True)
+                    assert np.array_equal(a, b) and np.array_equal(ta, tb), (N, B, G, mode, layout)
+
+
 ALL_CHECKS = [check_numpy_layouts, check_tagged_brute_force, check_round_trip,
-              check_b1_is_ulysses, check_k1_local_transpose, check_traffic,
+              check_b1_is_ulysses, check_groups_special_cases, check_k1_local_transpose, check_traffic,
               check_bijection, check_bf16_patterns, check_rejects, check_source_index_matches_loop]
 
 

@@ -49,6 +49,11 @@ MUTANTS = [
      "src[i] = seq_offset(g * P + s % P, bl, s / P, j * Hl + hl, e, Bl, St, H, d);", 0),
     ("one_element_head_rule_swapped", "src[i] = head_offset(layout, g * P + h / Hl, bl, h % Hl, j * St + t, e, Bl, Hl, S, d);",
      "src[i] = head_offset(layout, g * P + h % P, bl, h / P, j * St + t, e, Bl, Hl, S, d);", 0),
+    ("groups_members_from_batch", "*P = N / G_req;", "*P = B / G_req;", 0),
+    ("groups_whole_batch_per_group", "*Bl = B / G_req;", "*Bl = B;", 0),
+    ("groups_one_sequence_per_group", "*Bl = B / G_req;", "*Bl = 1;", 0),
+    ("groups_batch_divisibility_dropped", " || B % G_req != 0", "", 0),
+    ("groups_count_from_ranks", "*G = G_req;", "*G = N / G_req;", 0),
     ("source_index_off_by_one_channel", "in, seq_offset(src_rank, bl, t, h, e, Bl, St, H, d), es);",
      "in, seq_offset(src_rank, bl, t, h, (e + 1) % d, Bl, St, H, d), es);", 0),
 ]

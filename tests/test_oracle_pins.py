@@ -74,6 +74,16 @@ def test_page_facts():
         _, _, tm = _observed(mode, f["P_total"], f["B"], f["S"] // scale, H=f["H"], d=f["d"])
         assert set(int(v) * scale for v in tm.sum(axis=0)) == {f["elements_per_gpu"]}
 
+    f = facts["work_equality_general_G"]
+    scale = 64   # received elements are linear in S: a shorter sequence keeps it quick
+    for G, peers in zip(f["G_values"], f["peers"]):
+        assert oracle.groups(oracle.GROUPS, f["N"], f["B"], G) == (G, f["N"] // G, f["B"] // G)
+        x = np.zeros(f["B"] * (f["S"] // scale) * f["H"] * f["d"], dtype=np.uint16)
+        _, tm = oracle.seq_to_head(x, oracle.GROUPS, f["N"], f["B"], f["S"] // scale, f["H"], f["d"],
+                                   traffic=True, G=G)
+        assert set(int(v) * scale for v in tm.sum(axis=0)) == {f["elements_per_gpu"]}
+        assert {sum(1 for i in range(f["N"]) if i != r and tm[i, r]) for r in range(f["N"])} == {peers}
+
     f = facts["needs_n_multiple_of_b"]
     assert (oracle.groups(BASP, f["N"], f["B"]) is not None) == f["valid"]
 
