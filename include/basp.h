@@ -237,6 +237,29 @@ basp_status basp_seq_to_head_unfused(const basp_plan *plan, const void *q, const
                                      const void *v, void *out, void *ws, void *stream);
 
 /*
+ * basp_seq_to_head_unfused for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same inputs, output, kernels and result; the workspace is an
+ * array of BASP_NOALLOC_SCRATCH_BYTES bytes that the library holds on each
+ * device it runs this call on, until the process ends.  The call allocates
+ * and frees nothing; on its first call on a device it looks up that device's
+ * copy of the array.
+ *   Limit: plans with basp_unfused_workspace_bytes(plan) above
+ *   BASP_NOALLOC_SCRATCH_BYTES are rejected with BASP_ERR_UNSUPPORTED before
+ *   any device call (the Q, K and V together may hold at most half of it).
+ *   Sharing: every call on one device uses that device's one array, so calls
+ *   that overlap on one device (other streams, other threads) race and give
+ *   undefined results; serialise them.  The array keeps the last call's
+ *   contents; nothing in it needs to start at zero (every workspace byte a
+ *   pass reads was written by the pass before it in the same call).
+ * Errors as for basp_seq_to_head_unfused; BASP_ERR_HIP when the runtime cannot
+ * name the current device or the array's address on it.
+ */
+#define BASP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+basp_status basp_seq_to_head_unfused_noalloc(const basp_plan *plan, const void *q, const void *k,
+                                             const void *v, void *out, void *stream);
+
+/*
  * Launch shape of a plan, per direction: BASP_SEQ_TO_HEAD applies to
  * basp_seq_to_head and basp_seq_to_head_o, BASP_HEAD_TO_SEQ to
  * basp_head_to_seq and basp_head_to_seq_qkv (the unfused baseline has a

@@ -100,6 +100,8 @@ _lib.basp_unfused_workspace_bytes.argtypes = [_plan_p]
 _lib.basp_unfused_workspace_bytes.restype = ctypes.c_size_t
 _lib.basp_seq_to_head_unfused.argtypes = [_plan_p, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.basp_seq_to_head_unfused.restype = _i32
+_lib.basp_seq_to_head_unfused_noalloc.argtypes = [_plan_p, _vp, _vp, _vp, _vp, _vp]
+_lib.basp_seq_to_head_unfused_noalloc.restype = _i32
 _lib.basp_plan_set_tuning.argtypes = [_plan_p, ctypes.POINTER(basp_tuning)]
 _lib.basp_plan_set_tuning.restype = _i32
 _lib.basp_plan_set_direction_tuning.argtypes = [_plan_p, _i32, ctypes.POINTER(basp_tuning)]
@@ -323,6 +325,17 @@ def basp_seq_to_head_unfused(plan: Plan, q, k, v, out, ws, stream=None) -> None:
         plan.handle, _ptr(q, plan, i["q_elems"], "q"), _ptr(k, plan, i["kv_elems"], "k"),
         _ptr(v, plan, i["kv_elems"], "v"), _ptr(out, plan, i["qkv_elems"], "out"), ws,
         _stream(stream)), "basp_seq_to_head_unfused")
+
+
+BASP_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def basp_seq_to_head_unfused_noalloc(plan: Plan, q, k, v, out, stream=None) -> None:
+    i = plan.info
+    _check(_lib.basp_seq_to_head_unfused_noalloc(
+        plan.handle, _ptr(q, plan, i["q_elems"], "q"), _ptr(k, plan, i["kv_elems"], "k"),
+        _ptr(v, plan, i["kv_elems"], "v"), _ptr(out, plan, i["qkv_elems"], "out"),
+        _stream(stream)), "basp_seq_to_head_unfused_noalloc")
 
 
 def basp_stream_copy(dst, src, nbytes=None, stream=None) -> None:

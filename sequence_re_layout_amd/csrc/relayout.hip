@@ -18,6 +18,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #define BASP_HD __host__ __device__
@@ -707,6 +708,82 @@ extern "C" basp_status basp_stream_copy(void *dst, const void *src, uint64_t byt
         const uint32_t grid = static_cast<uint32_t>(std::min<uint64_t>(chunks, basp::kCopyGridCap));
         return basp::launch_kernel(reinterpret_cast<const void *>(basp::stream_copy_kernel), dim3(grid),
                                    basp::kCopyBlock, D, stream, true, true);
+    });
+}
+
+// ------------------------------------------------- allocation-free variant --
+
+namespace basp {
+namespace {
+
+// The workspace of basp_seq_to_head_unfused_noalloc: a device array of the
+// library's own, one copy per device, which the device keeps until the
+// process ends.  Host code never passes this name to a kernel or a copy (on
+// the host it is only a stand-in for the symbol): it uses the device address
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[BASP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+struct ScratchSlot {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current), or nullptr on an error.
+void *scratch_address(basp_status &st)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        st = BASP_ERR_HIP;
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        st = BASP_ERR_UNSUPPORTED;
+        return nullptr;
+    }
+    ScratchSlot &slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot]() {
+        slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch));
+        if (slot.err != hipSuccess)
+            slot.ptr = nullptr;
+    });
+    if (slot.err != hipSuccess || !slot.ptr) {
+        st = BASP_ERR_HIP;
+        return nullptr;
+    }
+    return slot.ptr;
+}
+
+}  // namespace
+}  // namespace basp
+
+extern "C" basp_status basp_seq_to_head_unfused_noalloc(const basp_plan *p, const void *q,
+                                                        const void *k, const void *v, void *out,
+                                                        void *stream)
+{
+    return basp::timed_call([&]() -> basp_status {
+        if (!p)
+            return BASP_ERR_INVALID;
+        // the size limit is checked before any device call
+        if (basp_unfused_workspace_bytes(p) > BASP_NOALLOC_SCRATCH_BYTES)
+            return BASP_ERR_UNSUPPORTED;
+        // an empty plan touches no memory and needs no workspace
+        void *ws = nullptr;
+        if (p->S != 0) {
+            basp_status st = BASP_OK;
+            ws = basp::scratch_address(st);
+            if (!ws)
+                return st;
+        }
+        basp::PermLaunch L[3];
+        int s = basp::prepare_seq_to_head_unfused(*p, q, k, v, out, ws, L);
+        for (int i = 0; i < 3 && s == BASP_OK; ++i)
+            s = basp::launch(L[i], stream, i == 0, i == 2);
+        return basp_status(s);
     });
 }
 

@@ -261,3 +261,22 @@ def test_foil_tokens():
     # no foil where N/B is not whole: Ulysses with N % B != 0, or B > N
     assert b.basp_plan_create(8, 3, 24, 8, 8, 8, b.BASP_BF16, b.BASP_MODE_ULYSSES).info["tokens_per_rank_foil"] == 0
     assert b.basp_plan_create(8, 16, 8, 8, 8, 8, b.BASP_BF16, b.BASP_MODE_BASP).info["tokens_per_rank_foil"] == 0
+
+
+def test_noalloc_limit_checked_before_any_device_call():
+    """The allocation-free entry point rejects a NULL plan and a plan whose
+    workspace exceeds the library's array before touching the device (fake
+    addresses, never dereferenced); an empty plan needs no device at all."""
+    lib = b.library()
+    base = 1 << 40
+    assert lib.basp_seq_to_head_unfused_noalloc(None, base, base, base, base + (1 << 30), None) == b.BASP_ERR_INVALID
+    fits = b.basp_plan_create(8, 2, 4096, 16, 8, 64, b.BASP_BF16, b.BASP_MODE_BASP)
+    assert b.basp_unfused_workspace_bytes(fits) == b.BASP_NOALLOC_SCRATCH_BYTES
+    over = b.basp_plan_create(8, 2, 4104, 16, 8, 64, b.BASP_BF16, b.BASP_MODE_BASP)
+    assert lib.basp_seq_to_head_unfused_noalloc(over.handle, base, base, base, base + (1 << 30), None) \
+        == b.BASP_ERR_UNSUPPORTED
+    empty = b.basp_plan_create(8, 2, 0, 16, 8, 64, b.BASP_BF16, b.BASP_MODE_BASP)
+    assert lib.basp_seq_to_head_unfused_noalloc(empty.handle, None, None, None, None, None) == b.BASP_OK
+    header = open(HEADER).read()
+    assert "#define BASP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in header
+    assert b.BASP_NOALLOC_SCRATCH_BYTES == 64 << 20
