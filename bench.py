@@ -106,6 +106,7 @@ def parse_args(argv=None):
     ap.add_argument("--tune-autotunes", type=int, default=3, help="autotune runs per plan for --tune-shapes")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--trace-summary", metavar="TRACE_DIR")
+    ap.add_argument("--counter-summary", nargs="+", metavar="PMC_DIR")
     return ap.parse_args(argv)
 
 
@@ -320,7 +321,13 @@ def copy_ceiling(b, s_bytes, h_bytes, steps, warmup, every, min_launches):
     sb, hb = copy_buffers(s_bytes // 2, R), copy_buffers(h_bytes // 2, R)
     out = {}
     for key, bufs, m in (("s2h_bytes", sb, s_bytes), ("h2s_bytes", hb, h_bytes)):
+        # each leg between two marker kernels, so that profiler summaries can
+        # set the copy beside the kernels
+        torch.cuda.synchronize()
+        torch.cuda._sleep(MARKER_CYCLES)
         t = time_launches(b, lambda i: b.basp_stream_copy(bufs[i][1], bufs[i][0]), 60, R)
+        torch.cuda._sleep(MARKER_CYCLES)
+        torch.cuda.synchronize()
         out[key + "_alone_gbs"] = rate(m, statistics.mean(t))
     wall, s_t, h_t = step_loop(b, lambda i: b.basp_stream_copy(sb[i % R][1], sb[i % R][0]),
                                lambda i: b.basp_stream_copy(hb[i % R][1], hb[i % R][0]),
@@ -417,9 +424,9 @@ def optional_leg(fn):
 
 def detail(args, shape, name):
     """Per-mode rates of the other entry points on the bench workload: the
-    unfused baseline, the backward calls, the token-major layout, the
-    general-G plans, the step replayed from a HIP graph, torch's device
-    copy."""
+    unfused baseline, the backward calls, the token-major layout, the step
+    replayed from a HIP graph; the general-G plans at the batch-sweep shape;
+    torch's device copy."""
     import torch
     from sequence_re_layout_amd import binding as b
     N, B, S, Hq, Hkv, d = shape
@@ -458,6 +465,7 @@ def detail(args, shape, name):
         out[mode] = o
         del w, sets, p
         torch.cuda.empty_cache()
+    out["groups"] = groups_rates(args)
     nb = (2 * B * S * (Hq + 2 * Hkv) * d * 2) // 2
     src = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(2)]
     dst = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(2)]
@@ -465,6 +473,32 @@ def detail(args, shape, name):
     out["torch_device_copy_gbs"] = rate(2 * nb, med(c))
     del src, dst
     torch.cuda.empty_cache()
+    return out
+
+
+def groups_rates(args):
+    """The general G-group form at the batch-sweep shape with B = 8 (N = 8,
+    S = 8192, Llama-3.2-1B heads): G groups of 8/G ranks, for G = 1, 2, 4,
+    8, each plan autotuned (unless --builtin-shapes), timed like the table
+    of every workload (HIP graphs of back-to-back launches)."""
+    import torch
+    from sequence_re_layout_amd import binding as b
+    from sequence_re_layout_amd import workloads
+    _, N, B, S, Hq, Hkv, d = workloads.BATCH_SWEEP[-1]
+    out = {}
+    for G in (1, 2, 4, 8):
+        p = b.basp_plan_create_groups(N, B, S, Hq, Hkv, d, b.BASP_BF16, G)
+        i = p.info
+        R = max(2, -(-(3 << 30) // (i["qkv_bytes_moved"] + i["o_bytes_moved"])))
+        sets = table_sets(i, R)
+        if not args.builtin_shapes:
+            s0 = sets[0]
+            b.basp_plan_autotune(p, s0["q"], s0["k"], s0["v"], s0["out"], s0["o"], s0["o_out"])
+        t = measure_pair(b, p, sets, R, args.workload_steps)
+        out["G%d" % G] = dict(t, G=i["G"], P=i["P"], Bl=i["Bl"], peers_per_rank=i["peers_per_rank"],
+                              cross_rank_bytes_qkv=i["cross_rank_bytes_q"] + 2 * i["cross_rank_bytes_kv"])
+        del sets
+        torch.cuda.empty_cache()
     return out
 
 
@@ -666,6 +700,44 @@ def _is_tile(name, s2h):
     return "tile_kernel" in name and (("true>" in name) if s2h else ("false>" in name))
 
 
+# marked regions of a default run, in order: the two modes' sampled loops,
+# basp_stream_copy alone at seq->head's and at head->seq's byte count, the
+# calibration copy
+CAL_REGION = len(MODES) + 2
+
+
+def _region_kernels(regions):
+    """(label, rows) of the kernels each marked region of a run holds."""
+    out = []
+    for mode, region in zip(MODES, regions):
+        out.append(("%s seq->head" % mode, [r for r in region if _is_tile(r["Kernel_Name"], True)]))
+        out.append(("%s head->seq" % mode, [r for r in region if _is_tile(r["Kernel_Name"], False)]))
+    for i, label in ((len(MODES), "copy at seq->head bytes"), (len(MODES) + 1, "copy at head->seq bytes")):
+        if i < len(regions):
+            out.append((label, [r for r in regions[i] if "stream_copy_kernel" in r["Kernel_Name"]]))
+    return out
+
+
+def counter_summary(dirs):
+    """Median per dispatch of every counter in rocprofv3 --pmc runs of this
+    script, for each kernel of the marked regions (both modes' kernels and
+    the plain copy at their byte counts)."""
+    out = {}
+    for d in dirs:
+        rows = []
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                rows += list(csv.DictReader(f))
+        counters = sorted({r["Counter_Name"] for r in rows})
+        for c in counters:
+            cr = sorted((r for r in rows if r["Counter_Name"] == c), key=lambda r: int(r["Dispatch_Id"]))
+            for label, k in _region_kernels(_regions(cr, "Kernel_Name")):
+                if k:
+                    out.setdefault(label, {"kernel": k[0]["Kernel_Name"]})[c] = statistics.median(
+                        float(r["Counter_Value"]) for r in k)
+    return out
+
+
 def launch_shape_key(workload, mode):
     """The table's launch shapes of a workload and mode (what a default run
     times), as stored beside counters taken on them."""
@@ -709,11 +781,12 @@ def pmc_summary(fetch_dir, write_dir, workload=DEFAULT_WORKLOAD):
     for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
         rows = load(d, counter)
         regions = _regions(rows, "Kernel_Name")
-        if len(regions) < len(MODES) + 1:
+        if len(regions) <= CAL_REGION:
             raise SystemExit("expected %d marked regions for %s, found %d"
-                             % (len(MODES) + 1, counter, len(regions)))
-        # the calibration copy: the one copy between the third pair of markers
-        copies = [r for r in regions[len(MODES)] if "copy" in r["Kernel_Name"].lower()]
+                             % (CAL_REGION + 1, counter, len(regions)))
+        # the calibration copy: the one copy between the fifth pair of markers
+        # (after the two modes' loops and the two copy-ceiling legs)
+        copies = [r for r in regions[CAL_REGION] if "copy" in r["Kernel_Name"].lower()]
         if len(copies) != 1:
             raise SystemExit("expected one calibration copy for %s, found %d" % (counter, len(copies)))
         cal_row = copies[0]
@@ -750,7 +823,8 @@ def trace_summary(trace_dir):
         raise SystemExit("no kernel trace under %s" % trace_dir)
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     out = {}
-    for mode, region in zip(MODES, _regions(rows, "Kernel_Name")):
+    regions = _regions(rows, "Kernel_Name")
+    for mode, region in zip(MODES, regions):
         o = {}
         for key, s2h in (("seq_to_head", True), ("head_to_seq", False)):
             k = [r for r in region if _is_tile(r["Kernel_Name"], s2h)]
@@ -761,6 +835,9 @@ def trace_summary(trace_dir):
         gaps = [(int(b["Start_Timestamp"]) - int(a["End_Timestamp"])) * 1e-3 for a, b in zip(region, region[1:])]
         o["avg_gap_us"] = statistics.mean(gaps) if gaps else None
         out[mode] = o
+    for label, k in _region_kernels(regions)[2 * len(MODES):]:
+        dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3 for r in k]
+        out[label] = {"launches": len(k), "avg_us": statistics.mean(dur) if dur else None}
     return out
 
 
@@ -828,6 +905,9 @@ def main(argv=None):
         return 0
     if args.trace_summary:
         print(json.dumps(trace_summary(args.trace_summary), indent=1))
+        return 0
+    if args.counter_summary:
+        print(json.dumps(counter_summary(args.counter_summary), indent=1))
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the N virtual ranks of the re-layout share one "

@@ -21,6 +21,11 @@
  *             G = B, P = K, Bl = 1.  With more sequences than ranks (B > N)
  *             the method reverts to data parallelism [review, Frequently asked
  *             questions]: G = N, P = 1, Bl = B/N (B a multiple of N).
+ *   G groups: the general form in which the per-GPU work (B/G)*H*(S*G/N)*d
+ *             is the same for every G [review, Strengths; paper Sec. IV.C]:
+ *             G groups of P = N/G ranks, each owning Bl = B/G sequences (G
+ *             divides N and B).  G = 1 is Ulysses, G = B is BASP, G = N is
+ *             the data-parallel fallback.
  *
  * Rank r is member j = r % P of group g = r / P (groups of consecutive ranks,
  * [review, Summary]); group g owns sequences [g*Bl, (g+1)*Bl).  Member j holds
@@ -96,7 +101,10 @@ typedef enum basp_dtype {
 
 typedef enum basp_mode {
     BASP_MODE_ULYSSES = 0, /* one N-way group                              */
-    BASP_MODE_BASP = 1     /* B groups of K = N/B (or data parallel, B > N) */
+    BASP_MODE_BASP = 1,    /* B groups of K = N/B (or data parallel, B > N) */
+    BASP_MODE_GROUPS = 2   /* G groups given explicitly (basp_plan_create_groups;
+                              reported by basp_plan_query, not accepted by
+                              basp_plan_create / basp_plan_create_ex)       */
 } basp_mode;
 
 typedef enum basp_layout {
@@ -172,6 +180,20 @@ basp_plan *basp_plan_create(int N, int B, int64_t S, int Hq, int Hkv, int d,
                             basp_dtype dtype, basp_mode mode);
 basp_plan *basp_plan_create_ex(int N, int B, int64_t S, int Hq, int Hkv, int d,
                                basp_dtype dtype, basp_mode mode, basp_layout layout);
+
+/*
+ * Create a plan of the general G-group form (see "What is computed"): G
+ * groups of N/G consecutive ranks, group g owning the sequences
+ * [g*B/G, (g+1)*B/G) [review, Strengths; paper Sec. IV.C].  Other arguments
+ * and the host-only contract as for basp_plan_create_ex; the plan's mode is
+ * BASP_MODE_GROUPS.  Errors (NULL returned, code in basp_last_error()):
+ *   BASP_ERR_INVALID      G < 1, or as for basp_plan_create_ex
+ *   BASP_ERR_INDIVISIBLE  N % G or B % G != 0; S, Hq or Hkv not a multiple of
+ *                         the group size N/G
+ *   BASP_ERR_UNSUPPORTED  as for basp_plan_create_ex
+ */
+basp_plan *basp_plan_create_groups(int N, int B, int64_t S, int Hq, int Hkv, int d,
+                                   basp_dtype dtype, int G, basp_layout layout);
 
 /* Free a plan.  NULL is allowed.  (Host resource management: not a step of
  * the method.) */

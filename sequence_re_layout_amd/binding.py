@@ -31,6 +31,7 @@ BASP_INT32 = 3
 
 BASP_MODE_ULYSSES = 0
 BASP_MODE_BASP = 1
+BASP_MODE_GROUPS = 2
 
 BASP_LAYOUT_HEAD_MAJOR = 0
 BASP_LAYOUT_TOKEN_MAJOR = 1
@@ -84,6 +85,8 @@ _lib.basp_plan_create.argtypes = [_i32, _i32, _i64, _i32, _i32, _i32, _i32, _i32
 _lib.basp_plan_create.restype = _plan_p
 _lib.basp_plan_create_ex.argtypes = [_i32, _i32, _i64, _i32, _i32, _i32, _i32, _i32, _i32]
 _lib.basp_plan_create_ex.restype = _plan_p
+_lib.basp_plan_create_groups.argtypes = [_i32, _i32, _i64, _i32, _i32, _i32, _i32, _i32, _i32]
+_lib.basp_plan_create_groups.restype = _plan_p
 _lib.basp_plan_destroy.argtypes = [_plan_p]
 _lib.basp_plan_destroy.restype = None
 _lib.basp_plan_query.argtypes = [_plan_p, ctypes.POINTER(basp_plan_info)]
@@ -168,6 +171,14 @@ def basp_plan_create_ex(N, B, S, Hq, Hkv, d, dtype=BASP_BF16, mode=BASP_MODE_BAS
     h = _lib.basp_plan_create_ex(N, B, S, Hq, Hkv, d, dtype, mode, layout)
     if not h:
         raise BaspError(_lib.basp_last_error(), "basp_plan_create_ex")
+    return Plan(h)
+
+
+def basp_plan_create_groups(N, B, S, Hq, Hkv, d, dtype=BASP_BF16, G=1,
+                            layout=BASP_LAYOUT_HEAD_MAJOR) -> Plan:
+    h = _lib.basp_plan_create_groups(N, B, S, Hq, Hkv, d, dtype, G, layout)
+    if not h:
+        raise BaspError(_lib.basp_last_error(), "basp_plan_create_groups")
     return Plan(h)
 
 

@@ -139,13 +139,12 @@ constexpr uint32_t kGridYZ = 65535;   // work-groups along y and along z at most
 
 // What the tile launch grid and tile_origin assume of a plan: every tensor
 // holds fewer than 2^32 rows (tile bases are 32-bit row indices, and S fits
-// 32 bits), P and B fit the grid's y and z extents, and one of G, Bl, P is 1
-// (true of Ulysses, BASP and the data-parallel fallback).
+// 32 bits), and P and B fit the grid's y and z extents.
 bool grid_fits(const basp_plan &p)
 {
     const uint64_t H = uint64_t(std::max(p.Hq, p.Hkv));
     return uint64_t(p.S) <= 0xffffffffull / (uint64_t(p.B) * H) && uint32_t(p.P) <= kGridYZ &&
-           uint32_t(p.B) <= kGridYZ && (p.G == 1 || p.Bl == 1 || p.P == 1);
+           uint32_t(p.B) <= kGridYZ;
 }
 
 // Every offset a lane computes inside a tile stays below kI31Max.
@@ -207,7 +206,8 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
     D.heads_first = sh.heads_first;
     D.P = make_fastdiv(p.P);
     D.Bl = uint32_t(p.Bl);
-    D.bmul = p.Bl == 1 ? uint32_t(p.P) : 1u;
+    D.gstride = uint32_t(p.P - 1) * uint32_t(p.Bl);
+    D.Blf = make_fastdiv(uint32_t(p.Bl));
     D.A = make_fastdiv(A);
     uint64_t total = 0;
     for (int i = 0; i < 3; ++i) {

@@ -82,7 +82,8 @@ struct TileDesc {
     uint32_t heads_first;          // tile order: head block fastest (1) or token block (0)
     uint32_t xcd_span;             // tiles per XCD when remapped, else 0
     uint32_t Bl;                   // sequences per group
-    uint32_t bmul;                 // P when Bl == 1, else 1 (see tile_origin)
+    uint32_t gstride;              // (P - 1) * Bl (see tile_origin)
+    FastDiv Blf;                   // Bl, for the group of a batch index
     FastDiv P, A;                  // group size, vectors per row
     uint32_t batch_x;              // batch index folded into x (else blockIdx.z)
     uint32_t xbound;               // tiles along x: plane, or plane * B with batch_x
@@ -156,12 +157,15 @@ BASP_HD inline TileOrigin tile_origin(const TileDesc &D, const TileSeg &sg, uint
     o.nh = Hl - hl0 < Th ? Hl - hl0 : Th;
     // Row indices of the tile base in 32 bits (a tensor holds fewer than 2^32
     // rows; the host checks), then one widening multiply by the row size.
-    // Rank r = g*P + j holds local sequence bl of batch index b = g*Bl + bl.
-    // In every plan G, Bl or P is 1, so r*Bl + bl = b*bmul + j*Bl.
+    // Rank r = g*P + j holds local sequence bl of batch index b = g*Bl + bl,
+    // so r*Bl + bl = b + g*(P-1)*Bl + j*Bl with g = b / Bl.  (Ulysses has
+    // g = 0; BASP has Bl = 1, which gives b*P + j; the data-parallel fallback
+    // has P = 1, which gives b.)
     // Sequence-sharded: ((r*Bl + bl)*St + t)*H + h with j = js and
     // h = jh*Hl + hl; head-sharded: ((r*Bl + bl)*Hl + hl)*S + s, or
     // ((r*Bl + bl)*S + s)*Hl + hl, with j = jh and s = js*St + t.
-    const uint32_t pre_s = b * D.bmul + js * D.Bl, pre_h = b * D.bmul + jh * D.Bl;
+    const uint32_t rb = b + fastdiv(b, D.Blf) * D.gstride;
+    const uint32_t pre_s = rb + js * D.Bl, pre_h = rb + jh * D.Bl;
     const uint32_t seq_row = (pre_s * D.St + t0) * (P * Hl) + jh * Hl + hl0;
     const uint32_t s0 = js * D.St + t0;
     const uint32_t head_row = D.token_major ? (pre_h * D.S + s0) * Hl + hl0 : (pre_h * Hl + hl0) * D.S + s0;

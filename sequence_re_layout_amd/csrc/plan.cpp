@@ -7,6 +7,7 @@
 //   Ulysses            G = 1, P = N,   Bl = B
 //   BASP, B <= N       G = B, P = N/B, Bl = 1     (N = K*B, K = P)
 //   BASP, B >  N       G = N, P = 1,   Bl = B/N   (data-parallel fallback)
+//   G groups           G,     P = N/G, Bl = B/G   (G divides N and B)
 // Tokens and heads split evenly over the P members of a group.
 #include <climits>
 #include <cstring>
@@ -57,39 +58,14 @@ int64_t mul_capped(int64_t a, int64_t b)
 
 }  // namespace
 
-extern "C" basp_plan *basp_plan_create_ex(int N, int B, int64_t S, int Hq, int Hkv, int d,
-                                          basp_dtype dtype, basp_mode mode, basp_layout layout)
+namespace {
+
+// A plan with the group structure (G, P, Bl) already chosen: checks the
+// even splits of tokens and heads and the sizes, then fills the plan.
+basp_plan *make_plan(int N, int B, int64_t S, int Hq, int Hkv, int d, basp_dtype dtype, basp_mode mode,
+                     basp_layout layout, int G, int P, int Bl)
 {
     const int es = elem_size(dtype);
-    if (N < 1 || B < 1 || S < 0 || Hq < 1 || Hkv < 1 || d < 1 || es == 0 ||
-        (mode != BASP_MODE_ULYSSES && mode != BASP_MODE_BASP) ||
-        (layout != BASP_LAYOUT_HEAD_MAJOR && layout != BASP_LAYOUT_TOKEN_MAJOR)) {
-        record(BASP_ERR_INVALID);
-        return nullptr;
-    }
-
-    int G, P, Bl;
-    if (mode == BASP_MODE_ULYSSES) {
-        G = 1;
-        P = N;
-        Bl = B;
-    } else if (B <= N) {
-        if (N % B != 0) {
-            record(BASP_ERR_INDIVISIBLE);
-            return nullptr;
-        }
-        G = B;
-        P = N / B;
-        Bl = 1;
-    } else {
-        if (B % N != 0) {
-            record(BASP_ERR_INDIVISIBLE);
-            return nullptr;
-        }
-        G = N;
-        P = 1;
-        Bl = B / N;
-    }
     if (S % P != 0 || Hq % P != 0 || Hkv % P != 0) {
         record(BASP_ERR_INDIVISIBLE);
         return nullptr;
@@ -138,6 +114,65 @@ extern "C" basp_plan *basp_plan_create_ex(int N, int B, int64_t S, int Hq, int H
     }
     record(BASP_OK);
     return p;
+}
+
+bool args_valid(int N, int B, int64_t S, int Hq, int Hkv, int d, basp_dtype dtype, basp_layout layout)
+{
+    return N >= 1 && B >= 1 && S >= 0 && Hq >= 1 && Hkv >= 1 && d >= 1 && elem_size(dtype) != 0 &&
+           (layout == BASP_LAYOUT_HEAD_MAJOR || layout == BASP_LAYOUT_TOKEN_MAJOR);
+}
+
+}  // namespace
+
+extern "C" basp_plan *basp_plan_create_ex(int N, int B, int64_t S, int Hq, int Hkv, int d,
+                                          basp_dtype dtype, basp_mode mode, basp_layout layout)
+{
+    if (!args_valid(N, B, S, Hq, Hkv, d, dtype, layout) ||
+        (mode != BASP_MODE_ULYSSES && mode != BASP_MODE_BASP)) {
+        record(BASP_ERR_INVALID);
+        return nullptr;
+    }
+
+    int G, P, Bl;
+    if (mode == BASP_MODE_ULYSSES) {
+        G = 1;
+        P = N;
+        Bl = B;
+    } else if (B <= N) {
+        if (N % B != 0) {
+            record(BASP_ERR_INDIVISIBLE);
+            return nullptr;
+        }
+        G = B;
+        P = N / B;
+        Bl = 1;
+    } else {
+        if (B % N != 0) {
+            record(BASP_ERR_INDIVISIBLE);
+            return nullptr;
+        }
+        G = N;
+        P = 1;
+        Bl = B / N;
+    }
+    return make_plan(N, B, S, Hq, Hkv, d, dtype, mode, layout, G, P, Bl);
+}
+
+extern "C" basp_plan *basp_plan_create_groups(int N, int B, int64_t S, int Hq, int Hkv, int d,
+                                              basp_dtype dtype, int G, basp_layout layout)
+{
+    // the general form of the per-GPU work equality (review page,
+    // "Strengths"; the paper's Sec. IV.C): G groups of N/G consecutive ranks,
+    // each owning B/G consecutive sequences
+    if (!args_valid(N, B, S, Hq, Hkv, d, dtype, layout) || G < 1) {
+        record(BASP_ERR_INVALID);
+        return nullptr;
+    }
+    if (N % G != 0 || B % G != 0) {
+        record(BASP_ERR_INDIVISIBLE);
+        return nullptr;
+    }
+    return make_plan(N, B, S, Hq, Hkv, d, dtype, BASP_MODE_GROUPS, layout, G, N / G, B / G);
 }
 
 extern "C" basp_plan *basp_plan_create(int N, int B, int64_t S, int Hq, int Hkv, int d,

@@ -34,3 +34,32 @@ def case(seed):
 
 
 COUNT = 40
+
+
+def group_case(seed):
+    """Plan shape, number of groups G (dividing N and B, 1 < G < B and G < N
+    when possible), layout and tuning of random general-G case `seed`."""
+    rng = np.random.default_rng(5000 + seed)
+    while True:
+        N = int(rng.choice([2, 4, 6, 8, 12]))
+        B = int(rng.choice([2, 3, 4, 6, 8, 12, 16]))
+        Gs = [g for g in range(1, N + 1) if N % g == 0 and B % g == 0]
+        inner = [g for g in Gs if 1 < g < min(B, N)]
+        G = int(rng.choice(inner or Gs))
+        P = N // G
+        S = P * int(rng.integers(1, 30))
+        Hkv = P * int(rng.integers(1, 4))
+        Hq = Hkv * int(rng.integers(1, 4))
+        d = int(rng.choice([1, 3, 8, 24, 40, 64]))
+        if B * S * Hq * d <= 1_500_000:
+            break
+    tuning = dict(block_size=int(rng.choice([0, 64, 128, 256])), vectors_per_thread=int(rng.choice([0, 1, 2, 4, 8])),
+                  tile_heads=int(rng.integers(0, 5)), tile_tokens=int(rng.choice([0, 0, 1, 3, 17])),
+                  tile_order=int(rng.integers(0, 3)), lane_order=int(rng.integers(0, 3)),
+                  xcd_remap=int(rng.integers(0, 3)), stage=int(rng.integers(0, 3)),
+                  batch_order=int(rng.integers(0, 3)), cache_policy=int(rng.integers(0, 6)),
+                  max_grid=int(rng.choice([0, 0, 1, 7, 33])))
+    return (N, B, S, Hq, Hkv, d), G, int(rng.integers(0, 2)), tuning
+
+
+GROUP_COUNT = 20

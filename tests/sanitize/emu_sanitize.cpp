@@ -45,11 +45,14 @@ struct Shape {
     int Hq, Hkv, d;
     basp_mode mode;
     basp_layout layout;
+    int G;   // groups of BASP_MODE_GROUPS
 };
 
 void run_case(const Shape &s, const basp_tuning *t)
 {
-    basp_plan *p = basp_plan_create_ex(s.N, s.B, s.S, s.Hq, s.Hkv, s.d, BASP_INT32, s.mode, s.layout);
+    basp_plan *p = s.mode == BASP_MODE_GROUPS
+                       ? basp_plan_create_groups(s.N, s.B, s.S, s.Hq, s.Hkv, s.d, BASP_INT32, s.G, s.layout)
+                       : basp_plan_create_ex(s.N, s.B, s.S, s.Hq, s.Hkv, s.d, BASP_INT32, s.mode, s.layout);
     EXPECT(p != nullptr);
     if (!p)
         return;
@@ -100,6 +103,8 @@ int main()
         {8, 16, 40, 8, 8, 4, BASP_MODE_BASP, BASP_LAYOUT_HEAD_MAJOR},   // data-parallel fallback
         {8, 1, 8 * 13, 16, 8, 16, BASP_MODE_BASP, BASP_LAYOUT_TOKEN_MAJOR},
         {1, 1, 29, 3, 3, 7, BASP_MODE_ULYSSES, BASP_LAYOUT_HEAD_MAJOR},
+        {6, 4, 3 * 9, 6, 3, 40, BASP_MODE_GROUPS, BASP_LAYOUT_HEAD_MAJOR, 2},   // 3 members, 2 sequences
+        {8, 16, 2 * 7, 4, 2, 3, BASP_MODE_GROUPS, BASP_LAYOUT_TOKEN_MAJOR, 4},  // 2 members, 4 sequences
     };
     basp_tuning staged = {};
     staged.stage = 2;
@@ -125,6 +130,10 @@ int main()
     EXPECT(basp_last_error() == BASP_ERR_INVALID);
     EXPECT(basp_plan_create(8, 2, int64_t(1) << 60, 8, 8, 8, BASP_BF16, BASP_MODE_BASP) == nullptr);
     EXPECT(basp_last_error() == BASP_ERR_UNSUPPORTED);
+    EXPECT(basp_plan_create_groups(8, 6, 24, 24, 24, 8, BASP_BF16, 4, BASP_LAYOUT_HEAD_MAJOR) == nullptr);
+    EXPECT(basp_last_error() == BASP_ERR_INDIVISIBLE);
+    EXPECT(basp_plan_create_groups(8, 8, 24, 24, 24, 8, BASP_BF16, 0, BASP_LAYOUT_HEAD_MAJOR) == nullptr);
+    EXPECT(basp_last_error() == BASP_ERR_INVALID);
     EXPECT(std::strlen(basp_status_str(basp_status(99))) > 0);
     std::printf("%s (%d failures)\n", failures ? "FAILED" : "OK", failures);
     return failures ? 1 : 0;

@@ -280,3 +280,72 @@ def test_noalloc_limit_checked_before_any_device_call():
     header = open(HEADER).read()
     assert "#define BASP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in header
     assert b.BASP_NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+@pytest.mark.parametrize("args,status", [
+    ((8, 8, 64, 8, 8, 8, 0, 0, 0), b.BASP_ERR_INVALID),      # G = 0
+    ((8, 8, 64, 8, 8, 8, 0, -2, 0), b.BASP_ERR_INVALID),
+    ((8, 8, 64, 8, 8, 8, 0, 2, 3), b.BASP_ERR_INVALID),      # unknown layout
+    ((8, 8, 64, 8, 8, 8, 0, 3, 0), b.BASP_ERR_INDIVISIBLE),  # N % G
+    ((8, 6, 64, 8, 8, 8, 0, 4, 0), b.BASP_ERR_INDIVISIBLE),  # B % G
+    ((8, 8, 6, 8, 8, 8, 0, 2, 0), b.BASP_ERR_INDIVISIBLE),   # S % (N/G)
+    ((8, 8, 64, 8, 2, 8, 0, 2, 0), b.BASP_ERR_INDIVISIBLE),  # Hkv % (N/G)
+    ((8, 8, 64, 8, 8, 8, 0, 16, 0), b.BASP_ERR_INDIVISIBLE), # more groups than ranks
+    ((8, 8, 64, 8, 8, 8, 0, 2, 1), b.BASP_OK),
+    ((8, 16, 64, 8, 8, 8, 0, 8, 0), b.BASP_OK),
+])
+def test_plan_create_groups_status(args, status):
+    h = b.library().basp_plan_create_groups(*args)
+    st = b.basp_last_error()
+    if h:
+        b.library().basp_plan_destroy(h)
+    assert st == status
+
+
+GROUP_SHAPES = [  # (N, B, S, Hq, Hkv, d), G
+    ((8, 8, 8192, 32, 8, 64), 1), ((8, 8, 8192, 32, 8, 64), 2), ((8, 8, 8192, 32, 8, 64), 4),
+    ((8, 8, 8192, 32, 8, 64), 8), ((6, 4, 600, 6, 3, 40), 2), ((12, 6, 36, 12, 4, 24), 3),
+    ((8, 16, 8192, 32, 8, 64), 4),
+]
+
+
+@pytest.mark.parametrize("shape,G", GROUP_SHAPES, ids=lambda x: "x".join(map(str, x)) if isinstance(x, tuple) else "G%d" % x)
+def test_groups_plan_info_matches_oracle(shape, G):
+    """The general form's plan info against the pages' counts and the
+    oracle's observed exchange matrix (scaled down in S and d, where every
+    count is linear)."""
+    N, B, S, Hq, Hkv, d = shape
+    info = b.basp_plan_create_groups(N, B, S, Hq, Hkv, d, b.BASP_BF16, G).info
+    P = N // G
+    assert info["mode"] == b.BASP_MODE_GROUPS
+    assert (info["G"], info["P"], info["Bl"]) == oracle.groups(oracle.GROUPS, N, B, G) == (G, P, B // G)
+    assert info["tokens_per_rank"] * N == B * S
+    assert info["peers_per_rank"] == P - 1
+    assert info["q_elems_per_rank"] * N == B * Hq * S * d
+    for H, key in ((Hq, "q"), (Hkv, "kv")):
+        x = np.zeros(B * P * H, dtype=np.uint16)
+        _, tm = oracle.seq_to_head(x, oracle.GROUPS, N, B, P, H, 1, traffic=True, G=G)
+        scale = (S // P) * d * 2
+        for r in range(N):
+            peers = [i for i in range(N) if i != r and tm[i, r]]
+            assert len(peers) == info["peers_per_rank"]
+            for i in peers:
+                assert tm[i, r] * scale == info["per_peer_bytes_" + key]
+        assert (tm.sum() - np.trace(tm)) * scale == info["cross_rank_bytes_" + key]
+
+
+def test_groups_special_cases_match_the_two_schemes():
+    """G = 1 gives Ulysses' plan, G = B BASP's, G = N the data-parallel
+    fallback's: every info field but the mode."""
+    def same(a, c):
+        skip = {"mode"}
+        return {k: v for k, v in a.items() if k not in skip} == {k: v for k, v in c.items() if k not in skip}
+    g1 = b.basp_plan_create_groups(8, 2, 16384, 32, 8, 64, b.BASP_BF16, 1).info
+    assert same(g1, b.basp_plan_create(8, 2, 16384, 32, 8, 64, b.BASP_BF16, b.BASP_MODE_ULYSSES).info)
+    gb = b.basp_plan_create_groups(8, 2, 16384, 32, 8, 64, b.BASP_BF16, 2).info
+    assert same(gb, b.basp_plan_create(8, 2, 16384, 32, 8, 64, b.BASP_BF16, b.BASP_MODE_BASP).info)
+    gn = b.basp_plan_create_groups(8, 16, 8192, 32, 8, 64, b.BASP_BF16, 8).info
+    assert same(gn, b.basp_plan_create(8, 16, 8192, 32, 8, 64, b.BASP_BF16, b.BASP_MODE_BASP).info)
+    # create / create_ex do not take the general mode (it needs G)
+    assert not b.library().basp_plan_create(8, 8, 64, 8, 8, 8, 0, b.BASP_MODE_GROUPS)
+    assert b.basp_last_error() == b.BASP_ERR_INVALID

@@ -28,6 +28,7 @@ SPIN = "void at::cuda::(anonymous namespace)::spin_kernel(long)"
 S2H = "void basp::(anonymous namespace)::tile_kernel_staged<64, 1, 4, true>(basp::TileDesc)"
 H2S = "void basp::(anonymous namespace)::tile_kernel<256, 16, 2, 4, false>(basp::TileDesc)"
 COPY = "__amd_rocclr_copyBuffer"
+SCOPY = "basp::(anonymous namespace)::stream_copy_kernel(basp::(anonymous namespace)::CopyDesc)"
 
 
 def test_pmc_summary_scales_by_the_copy(tmp_path):
@@ -36,15 +37,17 @@ def test_pmc_summary_scales_by_the_copy(tmp_path):
     after, are ignored)."""
     cal_kib = bench.CALIB_BYTES / 1024
     # the fetch counter reads half of everything, the write counter all of it
+    copies = [(SPIN, 0.0), (SCOPY, 3000.0), (SCOPY, 3000.0), (SPIN, 0.0),
+              (SPIN, 0.0), (SCOPY, 2000.0), (SPIN, 0.0)]
     _write_counters(tmp_path / "f", "FETCH_SIZE",
                     [(COPY, 5.0), (S2H, 3000.0), (SPIN, 0.0), (S2H, 1000.0), (H2S, 700.0),
                      (S2H, 1002.0), (H2S, 700.0), (S2H, 998.0), (SPIN, 0.0), (COPY, 9e6),
-                     (SPIN, 0.0), (S2H, 2000.0), (H2S, 1400.0), (SPIN, 0.0),
-                     (SPIN, 0.0), (COPY, cal_kib / 2), (SPIN, 0.0), (COPY, 9e9)])
+                     (SPIN, 0.0), (S2H, 2000.0), (H2S, 1400.0), (SPIN, 0.0)] + copies +
+                    [(SPIN, 0.0), (COPY, cal_kib / 2), (SPIN, 0.0), (COPY, 9e9)])
     _write_counters(tmp_path / "w", "WRITE_SIZE",
                     [(S2H, 5.0), (SPIN, 0.0), (S2H, 2000.0), (H2S, 1400.0), (SPIN, 0.0),
-                     (SPIN, 0.0), (S2H, 4000.0), (H2S, 2800.0), (SPIN, 0.0),
-                     (SPIN, 0.0), (COPY, cal_kib), (SPIN, 0.0)])
+                     (SPIN, 0.0), (S2H, 4000.0), (H2S, 2800.0), (SPIN, 0.0)] + copies +
+                    [(SPIN, 0.0), (COPY, cal_kib), (SPIN, 0.0)])
     out = bench.pmc_summary(str(tmp_path / "f"), str(tmp_path / "w"), "w1")
     basp, uly = out["entries"]
     assert (basp["mode"], uly["mode"]) == ("basp", "ulysses") and basp["workload"] == "w1"
@@ -56,6 +59,10 @@ def test_pmc_summary_scales_by_the_copy(tmp_path):
     assert basp["head_to_seq"]["traffic_bytes_per_launch"] == pytest.approx(2800.0 * 1024)
     assert uly["traffic_bytes_per_launch"] == pytest.approx(8000.0 * 1024)
     assert basp["kernel_sources_sha256"] == bench.kernel_sources_sha256()
+    table = bench.counter_summary([str(tmp_path / "f"), str(tmp_path / "w")])
+    assert table["basp seq->head"]["FETCH_SIZE"] == 1000.0 and table["ulysses head->seq"]["WRITE_SIZE"] == 2800.0
+    assert table["copy at seq->head bytes"]["FETCH_SIZE"] == 3000.0
+    assert table["copy at head->seq bytes"]["WRITE_SIZE"] == 2000.0
 
 
 def test_trace_summary_per_mode(tmp_path):

@@ -31,7 +31,7 @@ if torch.cuda.is_available():
 else:  # collected on a machine without a GPU: every test here is skipped
     b = None
 
-MODE = {"basp": 1, "ulysses": 0}
+MODE = {"basp": 1, "ulysses": 0, "groups": 2}
 GUARD = 4096  # bytes of canary on each side of an output
 
 
@@ -81,11 +81,18 @@ TDT = {"bf16": (torch.bfloat16, 0), "int32": (torch.int32, 3), "fp16": (torch.fl
        "fp32": (torch.float32, 2)}
 
 
-def run_s2h(shape, mode, dtype="bf16", layout=0, tuning=None, cpu=None):
+def make_plan(shape, mode, code, layout=0, G=0):
+    N, B, S, Hq, Hkv, d = shape
+    if mode == "groups":
+        return b.basp_plan_create_groups(N, B, S, Hq, Hkv, d, code, G, layout)
+    return b.basp_plan_create_ex(N, B, S, Hq, Hkv, d, code, MODE[mode], layout)
+
+
+def run_s2h(shape, mode, dtype="bf16", layout=0, tuning=None, cpu=None, G=0):
     """Fused seq->head on the GPU and in the oracle; asserts bit equality."""
     N, B, S, Hq, Hkv, d = shape
     tdt, code = TDT[dtype]
-    plan = b.basp_plan_create_ex(N, B, S, Hq, Hkv, d, code, MODE[mode], layout)
+    plan = make_plan(shape, mode, code, layout, G)
     if tuning:
         b.basp_plan_set_tuning(plan, **tuning)
     q, k, v = cpu or seq_inputs(B, S, Hq, Hkv, d, "int32" if dtype == "int32" else "bf16")
@@ -95,7 +102,7 @@ def run_s2h(shape, mode, dtype="bf16", layout=0, tuning=None, cpu=None):
     torch.cuda.synchronize()
     check_guards(whole, plan.info["qkv_elems"])
     want = oracle.seq_to_head_qkv(inputs.raw_bits(q), inputs.raw_bits(k), inputs.raw_bits(v),
-                                  MODE[mode], N, B, S, Hq, Hkv, d, layout)
+                                  MODE[mode], N, B, S, Hq, Hkv, d, layout, G=G)
     got = bits(out)
     assert got.shape == want.shape
     bad = np.flatnonzero(got != want)
@@ -103,10 +110,10 @@ def run_s2h(shape, mode, dtype="bf16", layout=0, tuning=None, cpu=None):
     return plan, out
 
 
-def run_h2s(shape, mode, dtype="bf16", layout=0, tuning=None):
+def run_h2s(shape, mode, dtype="bf16", layout=0, tuning=None, G=0):
     N, B, S, Hq, Hkv, d = shape
     tdt, code = TDT[dtype]
-    plan = b.basp_plan_create_ex(N, B, S, Hq, Hkv, d, code, MODE[mode], layout)
+    plan = make_plan(shape, mode, code, layout, G)
     if tuning:
         b.basp_plan_set_tuning(plan, **tuning)
     nq = plan.info["q_elems"]
@@ -116,7 +123,7 @@ def run_h2s(shape, mode, dtype="bf16", layout=0, tuning=None):
     b.basp_head_to_seq(plan, o.cuda(), out)
     torch.cuda.synchronize()
     check_guards(whole, nq)
-    want = oracle.head_to_seq(inputs.raw_bits(o), MODE[mode], N, B, S, Hq, d, layout)
+    want = oracle.head_to_seq(inputs.raw_bits(o), MODE[mode], N, B, S, Hq, d, layout, G=G)
     bad = np.flatnonzero(bits(out) != want)
     assert bad.size == 0, "first mismatches at %s" % bad[:8]
 
@@ -566,7 +573,7 @@ def split_tags(sizes):
     return passes
 
 
-def check_s2h_full(plan, mode, shape, ins, layout=0):
+def check_s2h_full(plan, mode, shape, ins, layout=0, G=0):
     """Fused seq->head of device tensors ins = (q, k, v) against the oracle,
     every element."""
     N, B, S, Hq, Hkv, d = shape
@@ -575,31 +582,31 @@ def check_s2h_full(plan, mode, shape, ins, layout=0):
     out.view(torch.int16 if out.element_size() == 2 else torch.int32).fill_(-1)
     b.basp_seq_to_head(plan, *ins, out)
     torch.cuda.synchronize()
-    want = oracle.seq_to_head_qkv(*(bits(x) for x in ins), MODE[mode], N, B, S, Hq, Hkv, d, layout)
+    want = oracle.seq_to_head_qkv(*(bits(x) for x in ins), MODE[mode], N, B, S, Hq, Hkv, d, layout, G=G)
     bad = np.flatnonzero(bits(out) != want)
     assert bad.size == 0, "seq->head: %d mismatches, first at %s" % (bad.size, bad[:8])
 
 
-def check_h2s_full(plan, mode, shape, o, layout=0):
+def check_h2s_full(plan, mode, shape, o, layout=0, G=0):
     """O head->seq of a device tensor o against the oracle, every element."""
     N, B, S, Hq, Hkv, d = shape
     out = torch.empty_like(o)
     out.view(torch.int16 if out.element_size() == 2 else torch.int32).fill_(-1)
     b.basp_head_to_seq(plan, o, out)
     torch.cuda.synchronize()
-    want = oracle.head_to_seq(bits(o), MODE[mode], N, B, S, Hq, d, layout)
+    want = oracle.head_to_seq(bits(o), MODE[mode], N, B, S, Hq, d, layout, G=G)
     bad = np.flatnonzero(bits(out) != want)
     assert bad.size == 0, "head->seq: %d mismatches, first at %s" % (bad.size, bad[:8])
 
 
-def check_split_tags(plan, mode, shape, layout=0):
+def check_split_tags(plan, mode, shape, layout=0, G=0):
     """Both directions with the plan's current launch shapes, on both passes
     of split tags, every element against the oracle."""
     i = plan.info
     for q, k, v in split_tags([i["q_elems"], i["kv_elems"], i["kv_elems"]]):
-        check_s2h_full(plan, mode, shape, (q, k, v), layout)
+        check_s2h_full(plan, mode, shape, (q, k, v), layout, G)
     for (o,) in split_tags([i["q_elems"]]):
-        check_h2s_full(plan, mode, shape, o, layout)
+        check_h2s_full(plan, mode, shape, o, layout, G)
 
 
 @pytest.mark.parametrize("mode", ["basp", "ulysses"])
@@ -703,6 +710,104 @@ def test_int32_global_tags_full_size(w, mode):
     check_h2s_full(plan, mode, w[1:], o)
     del o
     torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------- general G groups --
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_general_groups_full_size(G):
+    """The batch-sweep shape at B = 8 (N = 8, S = 8192, Llama-3.2-1B heads)
+    in the general form with G groups of N/G ranks: the built-in launch
+    shape, the shape autotune picks, and an LDS-staged shape, each on both
+    passes of split tags in both directions, every element against the
+    oracle."""
+    needs_gpu()
+    name, N, B, S, Hq, Hkv, d = workloads.BATCH_SWEEP[-1]
+    shape = (N, B, S, Hq, Hkv, d)
+    assert B == 8
+    print("general groups", name, "G =", G, flush=True)
+    plan = b.basp_plan_create_groups(N, B, S, Hq, Hkv, d, b.BASP_BF16, G)
+    assert (plan.info["G"], plan.info["P"], plan.info["Bl"]) == (G, N // G, B // G)
+    check_split_tags(plan, "groups", shape, G=G)
+    i = plan.info
+    dev = lambda n: torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
+    q, k, v, o = dev(i["q_elems"]), dev(i["kv_elems"]), dev(i["kv_elems"]), dev(i["q_elems"])
+    b.basp_plan_autotune(plan, q, k, v, torch.empty(i["qkv_elems"], dtype=torch.bfloat16, device="cuda"), o,
+                         torch.empty_like(o))
+    del q, k, v, o
+    print("  autotuned", b.basp_plan_get_tuning(plan, 0), b.basp_plan_get_tuning(plan, 1), flush=True)
+    check_split_tags(plan, "groups", shape, G=G)
+    b.basp_plan_set_tuning(plan, stage=2, block_size=64, tile_heads=2, batch_order=2)
+    check_split_tags(plan, "groups", shape, G=G)
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("G", [2, 4])
+def test_general_groups_full_size_token_major(G):
+    needs_gpu()
+    name, N, B, S, Hq, Hkv, d = workloads.BATCH_SWEEP[-1]
+    print("general groups token-major", name, "G =", G, flush=True)
+    plan = b.basp_plan_create_groups(N, B, S, Hq, Hkv, d, b.BASP_BF16, G, b.BASP_LAYOUT_TOKEN_MAJOR)
+    check_split_tags(plan, "groups", (N, B, S, Hq, Hkv, d), layout=1, G=G)
+    torch.cuda.empty_cache()
+
+
+GROUP_CASES = [  # (N, B, S, Hq, Hkv, d), G -- also run by the CPU emulation
+    ((6, 4, 6 * 5, 6, 3, 40), 2), ((12, 6, 12 * 3, 12, 4, 24), 3),
+    ((8, 16, 8 * 4, 8, 4, 8), 4), ((4, 6, 4 * 7, 4, 2, 3), 2),
+]
+
+
+@pytest.mark.parametrize("case", GROUP_CASES, ids=lambda c: "x".join(map(str, c[0])) + "_G%d" % c[1])
+def test_general_groups_ragged(case):
+    needs_gpu()
+    shape, G = case
+    for tuning in (None, dict(batch_order=2), dict(stage=2, tile_heads=2),
+                   dict(tile_order=1, xcd_remap=2, max_grid=5)):
+        for layout in (0, 1):
+            for dtype in ("bf16", "int32"):
+                run_s2h(shape, "groups", dtype, layout, tuning, G=G)
+                run_h2s(shape, "groups", dtype, layout, tuning, G=G)
+
+
+@pytest.mark.parametrize("seed", range(random_cases.GROUP_COUNT))
+def test_random_general_groups(seed):
+    """Seeded random general-G plans and launch shapes (run first by the CPU
+    emulation with its bounds checks)."""
+    needs_gpu()
+    shape, G, layout, tuning = random_cases.group_case(seed)
+    dtype = "int32" if seed % 2 else "bf16"
+    print("random general-G case", seed, shape, G, layout, tuning, flush=True)
+    run_s2h(shape, "groups", dtype, layout, tuning, G=G)
+    run_h2s(shape, "groups", dtype, layout, tuning, G=G)
+
+
+def test_general_groups_backward():
+    needs_gpu()
+    shape, G = (6, 4, 6 * 5, 6, 3, 40), 2
+    N, B, S, Hq, Hkv, d = shape
+    for layout in (0, 1):
+        plan = b.basp_plan_create_groups(N, B, S, Hq, Hkv, d, b.BASP_BF16, G, layout)
+        i = plan.info
+        do = inputs.normal_bf16(i["q_elems"], 31)
+        out = torch.empty(i["q_elems"], dtype=torch.bfloat16, device="cuda")
+        b.basp_seq_to_head_o(plan, do.cuda(), out)
+        g = inputs.normal_bf16(i["qkv_elems"], 32)
+        dq = torch.empty(i["q_elems"], dtype=torch.bfloat16, device="cuda")
+        dk = torch.empty(i["kv_elems"], dtype=torch.bfloat16, device="cuda")
+        dv = torch.empty(i["kv_elems"], dtype=torch.bfloat16, device="cuda")
+        b.basp_head_to_seq_qkv(plan, g.cuda(), dq, dk, dv)
+        q, k, v = seq_inputs(B, S, Hq, Hkv, d, "bf16")
+        ws = torch.empty(b.basp_unfused_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
+        uf = torch.empty(i["qkv_elems"], dtype=torch.bfloat16, device="cuda")
+        b.basp_seq_to_head_unfused(plan, q.cuda(), k.cuda(), v.cuda(), uf, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), oracle.seq_to_head(inputs.raw_bits(do), 2, N, B, S, Hq, d, layout, G=G))
+        wq, wk, wv = oracle.head_to_seq_qkv(inputs.raw_bits(g), 2, N, B, S, Hq, Hkv, d, layout, G=G)
+        assert np.array_equal(bits(dq), wq) and np.array_equal(bits(dk), wk) and np.array_equal(bits(dv), wv)
+        assert np.array_equal(bits(uf), oracle.seq_to_head_qkv(inputs.raw_bits(q), inputs.raw_bits(k),
+                                                                inputs.raw_bits(v), 2, N, B, S, Hq, Hkv, d,
+                                                                layout, G=G))
 
 
 @pytest.mark.parametrize("mode,layout", [(1, 0), (0, 0), (1, 1)], ids=["basp", "ulysses", "basp-token-major"])

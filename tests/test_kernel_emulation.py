@@ -35,6 +35,8 @@ def emu(tmp_path_factory):
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     lib.basp_plan_create_ex.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32]
     lib.basp_plan_create_ex.restype = vp
+    lib.basp_plan_create_groups.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32]
+    lib.basp_plan_create_groups.restype = vp
     lib.basp_plan_destroy.argtypes = [vp]
     lib.basp_plan_set_tuning.argtypes = [vp, ctypes.POINTER(ctypes.c_int32 * 11)]
     lib.basp_plan_set_tuning.restype = i32
@@ -52,11 +54,14 @@ class Run:
     """One emulated call: checks status, the descriptor bound count and
     records the vector width used."""
 
-    def __init__(self, lib, shape, mode, layout, es, tuning=None):
+    def __init__(self, lib, shape, mode, layout, es, tuning=None, G=0):
         N, B, S, Hq, Hkv, d = shape
         self.lib = lib
         dtype = {2: 0, 4: 3}[es]
-        self.plan = lib.basp_plan_create_ex(N, B, S, Hq, Hkv, d, dtype, mode, layout)
+        if mode == oracle.GROUPS:
+            self.plan = lib.basp_plan_create_groups(N, B, S, Hq, Hkv, d, dtype, G, layout)
+        else:
+            self.plan = lib.basp_plan_create_ex(N, B, S, Hq, Hkv, d, dtype, mode, layout)
         assert self.plan, "plan rejected"
         if tuning:
             t = (ctypes.c_int32 * 11)(*[tuning.get(k, 0) for k in (
@@ -96,26 +101,26 @@ def _shifted(a, offset):
     return b
 
 
-def check_s2h(emu, shape, mode, layout, es, tuning=None, offset=0, seed=0):
+def check_s2h(emu, shape, mode, layout, es, tuning=None, offset=0, seed=0, G=0):
     N, B, S, Hq, Hkv, d = shape
     rng = np.random.default_rng(seed)
     q, k, v = (_rand(B * S * H * d, es, rng) for H in (Hq, Hkv, Hkv))
-    run = Run(emu, shape, mode, layout, es, tuning)
+    run = Run(emu, shape, mode, layout, es, tuning, G)
     out = _empty(q.size + 2 * k.size, es, offset)
     vw = run("emu_seq_to_head", _shifted(q, offset), _shifted(k, offset), _shifted(v, offset), out)
-    want = oracle.seq_to_head_qkv(q, k, v, mode, N, B, S, Hq, Hkv, d, layout)
+    want = oracle.seq_to_head_qkv(q, k, v, mode, N, B, S, Hq, Hkv, d, layout, G=G)
     assert np.array_equal(out, want)
     return vw
 
 
-def check_h2s(emu, shape, mode, layout, es, tuning=None, offset=0, seed=1):
+def check_h2s(emu, shape, mode, layout, es, tuning=None, offset=0, seed=1, G=0):
     N, B, S, Hq, Hkv, d = shape
     rng = np.random.default_rng(seed)
     o = _rand(B * S * Hq * d, es, rng)
-    run = Run(emu, shape, mode, layout, es, tuning)
+    run = Run(emu, shape, mode, layout, es, tuning, G)
     out = _empty(o.size, es, offset)
     vw = run("emu_head_to_seq", _shifted(o, offset), out)
-    assert np.array_equal(out, oracle.head_to_seq(o, mode, N, B, S, Hq, d, layout))
+    assert np.array_equal(out, oracle.head_to_seq(o, mode, N, B, S, Hq, d, layout, G=G))
     return vw
 
 
@@ -271,3 +276,70 @@ def test_grid_limits(emu, shape, mode):
     for tuning in (None, {"batch_order": 2}):
         check_s2h(emu, shape, mode, 0, 2, tuning)
         check_h2s(emu, shape, mode, 0, 2, tuning)
+
+
+# ------------------------------------------------------- general G groups --
+
+GROUP_CASES = [  # (N, B, S, Hq, Hkv, d), G
+    ((8, 8, 8 * 16, 8, 8, 64), 1), ((8, 8, 8 * 16, 8, 8, 64), 2), ((8, 8, 8 * 16, 8, 8, 64), 4),
+    ((8, 8, 8 * 16, 8, 8, 64), 8),
+    ((6, 4, 6 * 5, 6, 3, 40), 2),        # 3 members, 2 sequences per group, 80-byte rows
+    ((12, 6, 12 * 3, 12, 4, 24), 3),     # 4 members, 2 sequences per group, 48-byte rows
+    ((8, 16, 8 * 4, 8, 4, 8), 4),        # 2 members, 4 sequences per group
+    ((4, 6, 4 * 7, 4, 2, 3), 2),         # 6-byte rows: 2-byte vectors
+]
+GROUP_TUNINGS = [None, dict(batch_order=2), dict(stage=2, tile_heads=2),
+                 dict(tile_order=1, xcd_remap=2, max_grid=5), dict(batch_order=2, tile_order=1, lane_order=2)]
+
+
+@pytest.mark.parametrize("layout", [0, 1], ids=["head_major", "token_major"])
+@pytest.mark.parametrize("case", GROUP_CASES, ids=lambda c: "x".join(map(str, c[0])) + "_G%d" % c[1])
+def test_general_groups(emu, case, layout):
+    """G groups of N/G ranks owning B/G sequences each: the oracle's result
+    and every access inside its descriptor, for launch shapes that put the
+    batch index along z and along x."""
+    shape, G = case
+    for tuning in GROUP_TUNINGS:
+        for es in (2, 4):
+            check_s2h(emu, shape, oracle.GROUPS, layout, es, tuning, G=G)
+            check_h2s(emu, shape, oracle.GROUPS, layout, es, tuning, G=G)
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_general_groups_batch_sweep_scaled(emu, G):
+    """The batch-sweep shape at B = 8 (N = 8, S = 8192 / 16) for every G."""
+    shape = (8, 8, 512, 32, 8, 64)
+    check_s2h(emu, shape, oracle.GROUPS, 0, 2, G=G)
+    check_h2s(emu, shape, oracle.GROUPS, 0, 2, G=G)
+
+
+def test_general_groups_backward_and_unfused(emu):
+    shape, G = (6, 4, 6 * 5, 6, 3, 40), 2
+    N, B, S, Hq, Hkv, d = shape
+    rng = np.random.default_rng(11)
+    for layout in (0, 1):
+        run = Run(emu, shape, oracle.GROUPS, layout, 2, None, G)
+        nq, nkv = B * S * Hq * d, B * S * Hkv * d
+        do = _rand(nq, 2, rng)
+        out = _empty(nq, 2)
+        run("emu_seq_to_head_o", do, out)
+        assert np.array_equal(out, oracle.seq_to_head(do, oracle.GROUPS, N, B, S, Hq, d, layout, G=G))
+        g = _rand(nq + 2 * nkv, 2, rng)
+        dq, dk, dv = _empty(nq, 2), _empty(nkv, 2), _empty(nkv, 2)
+        run("emu_head_to_seq_qkv", g, dq, dk, dv)
+        wq, wk, wv = oracle.head_to_seq_qkv(g, oracle.GROUPS, N, B, S, Hq, Hkv, d, layout, G=G)
+        assert np.array_equal(dq, wq) and np.array_equal(dk, wk) and np.array_equal(dv, wv)
+        q, k, v = (_rand(n, 2, rng) for n in (nq, nkv, nkv))
+        out = _empty(nq + 2 * nkv, 2)
+        ws = _empty(2 * (nq + 2 * nkv), 2)
+        run("emu_seq_to_head_unfused", q, k, v, out, ws)
+        assert np.array_equal(out, oracle.seq_to_head_qkv(q, k, v, oracle.GROUPS, N, B, S, Hq, Hkv, d, layout,
+                                                          G=G))
+
+
+@pytest.mark.parametrize("seed", range(random_cases.GROUP_COUNT))
+def test_random_general_groups(emu, seed):
+    shape, G, layout, tuning = random_cases.group_case(seed)
+    for es in (2, 4):
+        check_s2h(emu, shape, oracle.GROUPS, layout, es, tuning, G=G)
+        check_h2s(emu, shape, oracle.GROUPS, layout, es, tuning, G=G)
