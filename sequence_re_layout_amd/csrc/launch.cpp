@@ -249,6 +249,7 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
     D.seg_end1 = D.seg[1].tile_end;
     D.xcd_span = sh.xcd ? uint32_t(total / kXcds) : 0;
     L.grid = uint32_t(std::min<uint64_t>(D.xbound, sh.grid_cap));
+    L.nseg = nseg;
     L.grid_y = uint32_t(p.P);
     L.grid_z = D.batch_x ? 1u : uint32_t(p.B);
     L.vw = vw;

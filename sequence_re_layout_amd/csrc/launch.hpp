@@ -244,6 +244,7 @@ BASP_HD inline uint32_t perm_source(const PermDesc &D, const PermSeg &sg, uint32
 // A tile launch ready to go: descriptor, template parameters, grid.
 struct TileLaunch {
     TileDesc D;
+    int nseg;                 // tensors in the launch: 1 or 3
     int vw, vpt, policy;
     int block;                // threads per work-group: 64, 128 or 256
     bool s2h;                 // read sequence-sharded, write head-sharded

@@ -43,7 +43,11 @@ void run(const TileLaunch &L, uint64_t *bad)
             uint32_t tile, b;
             tile_and_batch(D, x, bz, tile, b);
             const uint32_t t = xcd_tile(tile, D.xcd_span);
-            const TileSeg &sg = D.seg[tile_segment(D, t)];
+            // a one-tensor launch's kernel takes every tile as the first
+            // tensor's: every tile must be
+            if (L.nseg == 1 && tile_segment(D, t) != 0)
+                ++*bad;
+            const TileSeg &sg = D.seg[L.nseg == 1 ? 0 : tile_segment(D, t)];
             const TileOrigin o = tile_origin(D, sg, t, by, b);
             const uint64_t seq = sg.seq + o.seq_off, head = sg.head + o.head_off;
             const uint64_t nseq = range(rest(sg.seq_bytes, o.seq_off));
