@@ -579,8 +579,11 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
     constexpr int kCoarse = 3, kFine = 7, kKeep = 6, kPairs = 3, kPairRounds = 5;
     hipEvent_t ev[2 * basp::kPool];
     int made = 0;
+    // timing-only events: without the system-scope fence an event otherwise
+    // performs when it completes (a cache writeback the launches of a plain
+    // back-to-back step do not pay)
     for (; made < 2 * basp::kPool; ++made)
-        if (hipEventCreate(&ev[made]) != hipSuccess)
+        if (hipEventCreateWithFlags(&ev[made], hipEventDisableSystemFence) != hipSuccess)
             break;
     const basp_tuning saved[2] = {p->tuning[0], p->tuning[1]};
     bool ok = made == 2 * basp::kPool;

@@ -25,8 +25,19 @@ def _write_counters(d, counter, rows):
 
 
 SPIN = "void at::cuda::(anonymous namespace)::spin_kernel(long)"
-S2H = "void basp::(anonymous namespace)::tile_kernel_staged<64, 1, 4, true>(basp::TileDesc)"
-H2S = "void basp::(anonymous namespace)::tile_kernel<256, 16, 2, 4, false>(basp::TileDesc)"
+S2H = "void basp::(anonymous namespace)::tile_kernel_staged<64, 1, 4, true, false>(basp::TileDesc)"
+H2S = "void basp::(anonymous namespace)::tile_kernel<256, 16, 2, 4, false, true>(basp::TileDesc)"
+
+
+def test_kernel_direction_from_its_template_arguments():
+    """The direction is read from its position among the template arguments,
+    not from the last one (the one-tensor flag follows it)."""
+    assert bench._is_tile(S2H, True) and not bench._is_tile(S2H, False)
+    assert bench._is_tile(H2S, False) and not bench._is_tile(H2S, True)
+    fused_back = "void basp::(anonymous namespace)::tile_kernel<128, 16, 1, 4, false, false>(basp::TileDesc)"
+    do_s2h = "void basp::(anonymous namespace)::tile_kernel_staged<256, 2, 4, true, true>(basp::TileDesc)"
+    assert bench._is_tile(fused_back, False) and bench._is_tile(do_s2h, True)
+    assert not bench._is_tile("basp::(anonymous namespace)::stream_copy_kernel(basp::CopyDesc)", True)
 COPY = "__amd_rocclr_copyBuffer"
 SCOPY = "basp::(anonymous namespace)::stream_copy_kernel(basp::(anonymous namespace)::CopyDesc)"
 
