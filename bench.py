@@ -640,12 +640,13 @@ def measure_pair(b, p, sets, R, n):
 def tune_shapes(args):
     """The launch-shape table: for every named workload and mode,
     basp_plan_autotune runs --tune-autotunes times (each from the built-in
-    shapes); the distinct pairs it keeps and the built-in pair are timed as
-    whole back-to-back steps from HIP graphs in 3 interleaved rounds; the
-    pair with the lowest median step time is kept."""
+    shapes); the distinct pairs it keeps, the built-in pair and the pair the
+    current table holds are timed as whole back-to-back steps from HIP
+    graphs in 3 interleaved rounds; the pair with the lowest median step
+    time is kept."""
     import torch
     from sequence_re_layout_amd import binding as b
-    from sequence_re_layout_amd import workloads
+    from sequence_re_layout_amd import launch_shapes, workloads
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
     out = {"about": "launch shapes per named workload and mode, measured by bench.py --tune-shapes",
@@ -662,6 +663,9 @@ def tune_shapes(args):
                                              args.workload_steps * (400 << 20) // i["qkv_bytes_moved"]))
             sets = table_sets(i, R)
             cands = [({}, {})]
+            held = launch_shapes.lookup(name, mode)
+            if held is not None and tuple(held) not in cands:
+                cands.append(tuple(held))
             for _ in range(args.tune_autotunes):
                 b.basp_plan_set_tuning(p)
                 s = sets[0]

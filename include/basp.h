@@ -308,7 +308,9 @@ basp_status basp_seq_to_head_unfused_noalloc(const basp_plan *plan, const void *
  *                        of a (group member, batch index) pair
  *   tile_order           1 = token blocks fastest (the head-sharded side's
  *                        order), 2 = head blocks fastest (the sequence-sharded
- *                        side's order; built-in)
+ *                        side's order; built-in), 3 = token blocks fastest
+ *                        within one source member's token chunk, that
+ *                        member's tiles of the neighbouring heads next
  *   stage                1 = rows go straight from load to store registers
  *                        (built-in),
  *                        2 = each tile passes through LDS: loads

@@ -31,7 +31,7 @@ struct Shape {
     uint32_t tile_tokens, tile_heads;   // tile_tokens 0: derived
     bool heads_given;                   // tile_heads set by the tuning
     bool s_fast;
-    bool heads_first;
+    int order;                          // tile order 1, 2 or 3 (launch.hpp)
     uint32_t grid_cap;
     bool xcd;
     bool stage;
@@ -49,7 +49,7 @@ Shape resolve(const basp_plan &p, const basp_tuning &t)
     s.tile_heads = t.tile_heads ? uint32_t(t.tile_heads) : (short_rows ? 8 : 1);
     s.heads_given = t.tile_heads != 0;
     s.s_fast = t.lane_order == 1;
-    s.heads_first = t.tile_order != 1;
+    s.order = t.tile_order ? t.tile_order : 2;
     s.grid_cap = t.max_grid ? uint32_t(t.max_grid) : kGridCap;
     s.xcd = t.xcd_remap == 2;
     s.stage = t.stage == 2;
@@ -203,18 +203,19 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
     const bool head_major = p.layout == BASP_LAYOUT_HEAD_MAJOR;
     D.load_s_fast = s2h ? 0 : head_major;
     D.store_s_fast = s2h ? head_major : 0;
-    D.heads_first = sh.heads_first;
+    D.order = uint32_t(sh.order);
     D.P = make_fastdiv(p.P);
     D.Bl = uint32_t(p.Bl);
     D.gstride = uint32_t(p.P - 1) * uint32_t(p.Bl);
     D.Blf = make_fastdiv(uint32_t(p.Bl));
     D.A = make_fastdiv(A);
     uint64_t total = 0;
+    uint32_t end[3];                // each tensor's end in the plane's tiles
     for (int i = 0; i < 3; ++i) {
         TileSeg &sg = D.seg[i];
         if (i >= nseg) {            // unused slot: an empty range after the last tensor
             sg = D.seg[i - 1];
-            sg.tile_begin = sg.tile_end;
+            sg.tile_begin = end[i] = end[i - 1];
             continue;
         }
         const uint32_t H = segs[i].H, Hl = H / p.P;
@@ -224,20 +225,20 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
         const Strides st = strides(p, H);
         sg.seq = segs[i].seq;
         sg.head = segs[i].head;
-        sg.seq_bytes = uint64_t(p.B) * p.S * H * p.row_bytes;
-        sg.head_bytes = sg.seq_bytes;
+        sg.bytes = uint64_t(p.B) * p.S * H * p.row_bytes;
         sg.seq_tok = uint32_t(st.seq_tok);
         sg.head_tok = uint32_t(st.head_tok);
         sg.head_head_lane = ts.Th == 1 ? 0u : uint32_t(st.head_head);
         sg.Hl = Hl;
         sg.Ts = make_fastdiv(ts.Ts);
         sg.Th = make_fastdiv(ts.Th);
-        sg.fast = make_fastdiv(sh.heads_first ? ts.nhb : ts.ntb);
+        sg.fast = make_fastdiv(sh.order == 2 ? ts.nhb : ts.ntb);
+        sg.mid = make_fastdiv(sh.order == 3 ? ts.nhb : uint32_t(p.P));
         sg.tile_begin = uint32_t(total);
         total += ts.ntiles;
         if (total > kI31Max)
             return BASP_ERR_UNSUPPORTED;
-        sg.tile_end = uint32_t(total);
+        end[i] = uint32_t(total);
     }
     D.plane = uint32_t(total);
     D.batch_x = sh.batch_x && p.B > 1;
@@ -245,8 +246,8 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
     if (D.batch_x && total * uint64_t(p.B) > kI31Max)
         return BASP_ERR_UNSUPPORTED;
     D.xbound = D.batch_x ? uint32_t(total * uint64_t(p.B)) : uint32_t(total);
-    D.seg_end0 = D.seg[0].tile_end;
-    D.seg_end1 = D.seg[1].tile_end;
+    D.seg_end0 = end[0];
+    D.seg_end1 = end[1];
     D.xcd_span = sh.xcd ? uint32_t(total / kXcds) : 0;
     L.grid = uint32_t(std::min<uint64_t>(D.xbound, sh.grid_cap));
     L.nseg = nseg;

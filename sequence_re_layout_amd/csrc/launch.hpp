@@ -20,13 +20,17 @@
 // Launch grid.  blockIdx.z is the batch index b, blockIdx.y one group member
 // and blockIdx.x a tile of the (y, z) plane, Q, K and V planes one after the
 // other; optionally the batch index is folded into x instead (tile_and_batch).
-// Two tile orders:
-//   token blocks fastest (the head-sharded layout's order): y = jh and x runs
-//     over (hb, js, tb), so neighbouring tiles continue one destination head
-//     across source members;
-//   head blocks fastest (the sequence-sharded layout's order): y = js and x
-//     runs over (tb, jh, hb), so neighbouring tiles continue one source token
-//     across destination members.
+// Three tile orders, x running over (slow, middle, fast) digits:
+//   1, token blocks fastest (the head-sharded layout's order): y = jh and x
+//     runs over (hb, js, tb), so neighbouring tiles continue one destination
+//     head across source members;
+//   2, head blocks fastest (the sequence-sharded layout's order): y = js and
+//     x runs over (tb, jh, hb), so neighbouring tiles continue one source
+//     token across destination members;
+//   3, token blocks fastest within a source member: y = js and x runs over
+//     (jh, hb, tb), so neighbouring tiles continue one head through the
+//     member's token chunk, and the tiles that run at one time take the
+//     neighbouring heads of the same tokens.
 // Neighbouring tiles run at the same time and share the DRAM pages of one
 // side.  Optionally each XCD takes one contiguous eighth of a plane
 // (xcd_tile).  The staged variant passes each tile through LDS in one pass:
@@ -56,7 +60,7 @@ constexpr uint32_t kOutside = 0x80000000u;
 // One tensor of a tile launch.
 struct TileSeg {
     uint64_t seq, head;            // buffer addresses
-    uint64_t seq_bytes, head_bytes;
+    uint64_t bytes;                // bytes of the tensor (the same on both sides)
     uint32_t seq_tok;              // byte stride of a token, sequence-sharded
     uint32_t head_tok;             // byte stride of a token, head-sharded
     uint32_t head_head_lane;       // head stride inside a tile (0 when Th == 1)
@@ -64,7 +68,10 @@ struct TileSeg {
     FastDiv Ts, Th;                // tile extent in tokens and heads
     FastDiv fast;                  // blocks along the fast axis: token blocks per
                                    // member chunk, or head blocks per rank
-    uint32_t tile_begin, tile_end; // this tensor's tiles in the plane
+    FastDiv mid;                   // extent of x's middle digit: P, or head
+                                   // blocks per rank (tile order 3)
+    uint32_t tile_begin;           // this tensor's first tile in the plane (0 for
+                                   // the first, which one-tensor launches rely on)
 };
 
 // Launch-wide fields first: a kernel reads them in one batch of scalar
@@ -79,7 +86,7 @@ struct TileDesc {
     uint32_t s_fast;               // lanes along tokens (1) or heads (0)
     uint32_t load_s_fast;          // staged kernel: lane order of the loads
     uint32_t store_s_fast;         //   and of the stores
-    uint32_t heads_first;          // tile order: head block fastest (1) or token block (0)
+    uint32_t order;                // tile order 1, 2 or 3 (see above)
     uint32_t xcd_span;             // tiles per XCD when remapped, else 0
     uint32_t Bl;                   // sequences per group
     uint32_t gstride;              // (P - 1) * Bl (see tile_origin)
@@ -129,28 +136,21 @@ BASP_HD inline uint32_t tile_segment(const TileDesc &D, uint32_t tile)
     return tile < D.seg_end0 ? 0u : (tile < D.seg_end1 ? 1u : 2u);
 }
 
-// Tile `tile` (after xcd_tile) of tensor sg, in the plane of group member y
-// and batch index b.
-BASP_HD inline TileOrigin tile_origin(const TileDesc &D, const TileSeg &sg, uint32_t tile, uint32_t y,
+// Tile `local` of tensor sg (its tile of the plane, after xcd_tile, less
+// sg.tile_begin), in the plane of group member y and batch index b.
+BASP_HD inline TileOrigin tile_origin(const TileDesc &D, const TileSeg &sg, uint32_t local, uint32_t y,
                                       uint32_t b)
 {
     TileOrigin o;
     const uint32_t P = D.P.d;
-    const uint32_t local = tile - sg.tile_begin;
+    // x = (slow, m, f): order 1 (hb, js, tb), 2 (tb, jh, hb), 3 (jh, hb, tb)
     const uint32_t q = fastdiv(local, sg.fast), f = local - q * sg.fast.d;
-    const uint32_t slow = fastdiv(q, D.P), m = q - slow * P;
-    uint32_t tb, hb, js, jh;
-    if (D.heads_first) {   // x = (tb, jh, hb), y = js
-        hb = f;
-        jh = m;
-        tb = slow;
-        js = y;
-    } else {               // x = (hb, js, tb), y = jh
-        tb = f;
-        js = m;
-        hb = slow;
-        jh = y;
-    }
+    const uint32_t slow = fastdiv(q, sg.mid), m = q - slow * sg.mid.d;
+    const bool o1 = D.order == 1, o2 = D.order == 2;
+    const uint32_t tb = o2 ? slow : f;
+    const uint32_t hb = o2 ? f : (o1 ? slow : m);
+    const uint32_t js = o1 ? m : y;
+    const uint32_t jh = o1 ? y : (o2 ? m : slow);
     const uint32_t Ts = sg.Ts.d, Th = sg.Th.d, Hl = sg.Hl;
     const uint32_t t0 = tb * Ts, hl0 = hb * Th;
     o.ns = D.St - t0 < Ts ? D.St - t0 : Ts;

@@ -244,7 +244,7 @@ bool tuning_in_range(const basp_tuning &t)
     return (v == 0 || v == 1 || v == 2 || v == 4 || v == 8) && t.tile_tokens >= 0 &&
            t.tile_heads >= 0 && t.cache_policy >= 0 && t.cache_policy <= 5 && t.max_grid >= 0 &&
            t.lane_order >= 0 && t.lane_order <= 2 && t.xcd_remap >= 0 && t.xcd_remap <= 2 &&
-           t.tile_order >= 0 && t.tile_order <= 2 && t.stage >= 0 && t.stage <= 2 &&
+           t.tile_order >= 0 && t.tile_order <= 3 && t.stage >= 0 && t.stage <= 2 &&
            (t.block_size == 0 || t.block_size == 64 || t.block_size == 128 || t.block_size == 256) &&
            t.batch_order >= 0 && t.batch_order <= 2;
 }

@@ -114,10 +114,10 @@ __global__ __launch_bounds__(BS) void tile_kernel(const TileDesc D)
         tile_and_batch(D, x, blockIdx.z, tile, bz);
         const uint32_t t = xcd_tile(tile, D.xcd_span);
         const TileSeg sg = D.seg[segment_of<ONE>(D, t)];   // one batch of scalar loads
-        const TileOrigin o = tile_origin(D, sg, t, blockIdx.y, bz);
-        const __amdgpu_buffer_rsrc_t rseq = make_rsrc(sg.seq + o.seq_off, rest(sg.seq_bytes, o.seq_off));
+        const TileOrigin o = tile_origin(D, sg, ONE ? t : t - sg.tile_begin, blockIdx.y, bz);
+        const __amdgpu_buffer_rsrc_t rseq = make_rsrc(sg.seq + o.seq_off, rest(sg.bytes, o.seq_off));
         const __amdgpu_buffer_rsrc_t rhead =
-            make_rsrc(sg.head + o.head_off, rest(sg.head_bytes, o.head_off));
+            make_rsrc(sg.head + o.head_off, rest(sg.bytes, o.head_off));
         const uint32_t nvec = sg.Ts.d * sg.Th.d * D.A.d;
         for (uint32_t v0 = 0; v0 < nvec; v0 += BS * VPT) {
             uint32_t src[VPT], dst[VPT];
@@ -157,10 +157,10 @@ __global__ __launch_bounds__(BS) void tile_kernel_staged(const TileDesc D)
         tile_and_batch(D, x, blockIdx.z, tile, bz);
         const uint32_t t = xcd_tile(tile, D.xcd_span);
         const TileSeg sg = D.seg[segment_of<ONE>(D, t)];   // one batch of scalar loads
-        const TileOrigin o = tile_origin(D, sg, t, blockIdx.y, bz);
-        const __amdgpu_buffer_rsrc_t rseq = make_rsrc(sg.seq + o.seq_off, rest(sg.seq_bytes, o.seq_off));
+        const TileOrigin o = tile_origin(D, sg, ONE ? t : t - sg.tile_begin, blockIdx.y, bz);
+        const __amdgpu_buffer_rsrc_t rseq = make_rsrc(sg.seq + o.seq_off, rest(sg.bytes, o.seq_off));
         const __amdgpu_buffer_rsrc_t rhead =
-            make_rsrc(sg.head + o.head_off, rest(sg.head_bytes, o.head_off));
+            make_rsrc(sg.head + o.head_off, rest(sg.bytes, o.head_off));
         uint32_t off[VPT], slot[VPT];
         bool ok[VPT];
 #pragma unroll
@@ -397,7 +397,7 @@ std::vector<basp_tuning> autotune_candidates(const basp_plan &p)
     const int nvpt = 2 * (p.q_elems + 2 * p.kv_elems) * p.es <= kWideVectorBytes ? 4 : 2;
     for (int bo = 1; bo <= 2; ++bo)
         for (int block : blocks)
-            for (int to = 1; to <= 2; ++to)
+            for (int to = 1; to <= 3; ++to)
                 for (int iv = 0; iv < nvpt; ++iv)
                     for (int th : heads)
                         for (int xcd = 1; xcd <= 2; ++xcd) {

@@ -48,10 +48,13 @@ void run(const TileLaunch &L, uint64_t *bad)
             if (L.nseg == 1 && tile_segment(D, t) != 0)
                 ++*bad;
             const TileSeg &sg = D.seg[L.nseg == 1 ? 0 : tile_segment(D, t)];
-            const TileOrigin o = tile_origin(D, sg, t, by, b);
+            // a one-tensor launch's kernel takes its tensor's first tile as 0
+            if (L.nseg == 1 && sg.tile_begin != 0)
+                ++*bad;
+            const TileOrigin o = tile_origin(D, sg, t - sg.tile_begin, by, b);
             const uint64_t seq = sg.seq + o.seq_off, head = sg.head + o.head_off;
-            const uint64_t nseq = range(rest(sg.seq_bytes, o.seq_off));
-            const uint64_t nhead = range(rest(sg.head_bytes, o.head_off));
+            const uint64_t nseq = range(rest(sg.bytes, o.seq_off));
+            const uint64_t nhead = range(rest(sg.bytes, o.head_off));
             const uint64_t src = L.s2h ? seq : head, dst = L.s2h ? head : seq;
             const uint64_t nsrc = L.s2h ? nseq : nhead, ndst = L.s2h ? nhead : nseq;
             if (L.staged) {

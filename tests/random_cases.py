@@ -26,7 +26,7 @@ def case(seed):
             break
     tuning = dict(block_size=int(rng.choice([0, 64, 128, 256])), vectors_per_thread=int(rng.choice([0, 1, 2, 4, 8])),
                   tile_heads=int(rng.integers(0, 5)), tile_tokens=int(rng.choice([0, 0, 1, 3, 17])),
-                  tile_order=int(rng.integers(0, 3)), lane_order=int(rng.integers(0, 3)),
+                  tile_order=int(rng.integers(0, 4)), lane_order=int(rng.integers(0, 3)),
                   xcd_remap=int(rng.integers(0, 3)), stage=int(rng.integers(0, 3)),
                   batch_order=int(rng.integers(0, 3)), cache_policy=int(rng.integers(0, 6)),
                   max_grid=int(rng.choice([0, 0, 1, 7, 33])))
@@ -55,7 +55,7 @@ def group_case(seed):
             break
     tuning = dict(block_size=int(rng.choice([0, 64, 128, 256])), vectors_per_thread=int(rng.choice([0, 1, 2, 4, 8])),
                   tile_heads=int(rng.integers(0, 5)), tile_tokens=int(rng.choice([0, 0, 1, 3, 17])),
-                  tile_order=int(rng.integers(0, 3)), lane_order=int(rng.integers(0, 3)),
+                  tile_order=int(rng.integers(0, 4)), lane_order=int(rng.integers(0, 3)),
                   xcd_remap=int(rng.integers(0, 3)), stage=int(rng.integers(0, 3)),
                   batch_order=int(rng.integers(0, 3)), cache_policy=int(rng.integers(0, 6)),
                   max_grid=int(rng.choice([0, 0, 1, 7, 33])))

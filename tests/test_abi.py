@@ -135,7 +135,7 @@ def test_tuning_validation():
         b.basp_plan_set_direction_tuning(p, 2, tile_heads=1)
     assert e.value.status == b.BASP_ERR_INVALID
     with pytest.raises(b.BaspError) as e:
-        b.basp_plan_set_tuning(p, tile_order=3)
+        b.basp_plan_set_tuning(p, tile_order=4)
     assert e.value.status == b.BASP_ERR_INVALID
     with pytest.raises(TypeError):
         b.basp_plan_set_tuning(p, tile_size=3)

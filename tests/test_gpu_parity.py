@@ -248,7 +248,9 @@ TUNINGS = [dict(vectors_per_thread=1), dict(vectors_per_thread=2), dict(vectors_
            dict(stage=2, vectors_per_thread=8, tile_tokens=500, tile_order=2, max_grid=5),
            dict(block_size=64, cache_policy=4), dict(block_size=128, stage=2, vectors_per_thread=8, cache_policy=5),
            dict(block_size=64, stage=1, tile_tokens=9, max_grid=7),
-           dict(batch_order=2), dict(batch_order=2, stage=2, tile_order=1, xcd_remap=2, max_grid=9)]
+           dict(batch_order=2), dict(batch_order=2, stage=2, tile_order=1, xcd_remap=2, max_grid=9),
+           dict(tile_order=3), dict(tile_order=3, tile_heads=3, tile_tokens=5, max_grid=11),
+           dict(tile_order=3, stage=2, xcd_remap=2, batch_order=2, tile_heads=2)]
 
 
 @pytest.mark.parametrize("tuning", TUNINGS, ids=lambda t: ",".join("%s=%s" % kv for kv in t.items()))
@@ -533,7 +535,7 @@ def test_autotune_keeps_results(shape, mode):
             continue
         assert t["vectors_per_thread"] in (1, 2, 4, 8) and t["cache_policy"] == 4
         assert t["block_size"] in (64, 128, 256) and t["xcd_remap"] in (1, 2)
-        assert t["stage"] in (1, 2) and t["tile_order"] in (1, 2)   # a measured candidate
+        assert t["stage"] in (1, 2) and t["tile_order"] in (1, 2, 3)   # a measured candidate
     qkv.fill_(0)
     o_out.fill_(0)
     b.basp_seq_to_head(plan, q, k, v, qkv)

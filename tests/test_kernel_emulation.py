@@ -159,7 +159,10 @@ TUNINGS = [dict(vectors_per_thread=1), dict(vectors_per_thread=2), dict(vectors_
            dict(cache_policy=4), dict(cache_policy=5, block_size=128, stage=2),
            dict(batch_order=2), dict(batch_order=2, tile_order=1, max_grid=5),
            dict(batch_order=2, stage=2, xcd_remap=2, block_size=64, tile_heads=2),
-           dict(batch_order=1, tile_order=1, xcd_remap=2)]
+           dict(batch_order=1, tile_order=1, xcd_remap=2),
+           dict(tile_order=3), dict(tile_order=3, tile_heads=3, tile_tokens=5, max_grid=11),
+           dict(tile_order=3, stage=2, xcd_remap=2, batch_order=2, tile_heads=2),
+           dict(tile_order=3, lane_order=1, vectors_per_thread=2, block_size=64, max_grid=7)]
 
 
 @pytest.mark.parametrize("tuning", TUNINGS, ids=lambda t: ",".join("%s=%s" % kv for kv in t.items()))
