@@ -640,10 +640,11 @@ def measure_pair(b, p, sets, R, n):
 def tune_shapes(args):
     """The launch-shape table: for every named workload and mode,
     basp_plan_autotune runs --tune-autotunes times (each from the built-in
-    shapes); the distinct pairs it keeps, the built-in pair and the pair the
-    current table holds are timed as whole back-to-back steps from HIP
-    graphs in 3 interleaved rounds; the pair with the lowest median step
-    time is kept."""
+    shapes).  Then, per mode, the distinct pairs autotune kept in either
+    mode (the two plans share their tensors' sizes; with B = 1 they are the
+    same plan), the built-in pair and the pair the current table holds are
+    timed as whole back-to-back steps from HIP graphs in 3 interleaved
+    rounds; the pair with the lowest median step time is kept."""
     import torch
     from sequence_re_layout_amd import binding as b
     from sequence_re_layout_amd import launch_shapes, workloads
@@ -653,9 +654,25 @@ def tune_shapes(args):
            "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None)},
            "kernel_sources_sha256": kernel_sources_sha256(), "shapes": {}}
     dirs = (("seq_to_head", b.BASP_SEQ_TO_HEAD), ("head_to_seq", b.BASP_HEAD_TO_SEQ))
+    modes = (("basp", b.BASP_MODE_BASP), ("ulysses", b.BASP_MODE_ULYSSES))
     for (name, N, B, S, Hq, Hkv, d) in workloads.ALL + workloads.EXTRA:
         out["shapes"][name] = {}
-        for mode, code in (("basp", b.BASP_MODE_BASP), ("ulysses", b.BASP_MODE_ULYSSES)):
+        picks = {}
+        for mode, code in modes:   # autotune's picks in each mode
+            p = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, code)
+            sets = table_sets(p.info, 2)
+            picks[mode] = []
+            for _ in range(args.tune_autotunes):
+                b.basp_plan_set_tuning(p)
+                s = sets[0]
+                b.basp_plan_autotune(p, s["q"], s["k"], s["v"], s["out"], s["o"], s["o_out"])
+                pair = tuple({k: v for k, v in b.basp_plan_get_tuning(p, dcode).items() if v}
+                             for _, dcode in dirs)
+                if pair not in picks[mode]:
+                    picks[mode].append(pair)
+            del sets
+            torch.cuda.empty_cache()
+        for mode, code in modes:
             p = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, code)
             i = p.info
             R = max(2, -(-(3 << 30) // (i["qkv_bytes_moved"] + i["o_bytes_moved"])))
@@ -664,14 +681,8 @@ def tune_shapes(args):
             sets = table_sets(i, R)
             cands = [({}, {})]
             held = launch_shapes.lookup(name, mode)
-            if held is not None and tuple(held) not in cands:
-                cands.append(tuple(held))
-            for _ in range(args.tune_autotunes):
-                b.basp_plan_set_tuning(p)
-                s = sets[0]
-                b.basp_plan_autotune(p, s["q"], s["k"], s["v"], s["out"], s["o"], s["o_out"])
-                pair = tuple({k: v for k, v in b.basp_plan_get_tuning(p, dcode).items() if v}
-                             for _, dcode in dirs)
+            other = [m for m, _ in modes if m != mode][0]
+            for pair in ([tuple(held)] if held is not None else []) + picks[mode] + picks[other]:
                 if pair not in cands:
                     cands.append(pair)
             times = [[] for _ in cands]
