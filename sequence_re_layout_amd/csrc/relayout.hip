@@ -17,6 +17,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <cstdint>
 #include <mutex>
 #include <vector>
@@ -98,6 +99,46 @@ __device__ inline uint32_t segment_of(const TileDesc &D, uint32_t t)
     return ONE ? 0u : tile_segment(D, t);
 }
 
+// A fused launch reads the launch-wide fields, then its tile's tensor record
+// at an offset that depends on them: a later round of scalar loads, which
+// on a CU's first work-groups misses in the scalar cache again.  Loading
+// one word of every cache line the records occupy in the first round
+// (values discarded) makes the later rounds hits.  Lines 0x00 and 0x40 hold
+// the launch-wide fields, which every work-group loads anyway.
+static_assert(offsetof(TileDesc, seg) < 0x80 && sizeof(TileDesc) > 0x180 && sizeof(TileDesc) <= 0x1c0,
+              "touch_records() covers the descriptor's lines from 0x80 on");
+
+struct Touched {
+    uint32_t w[5];
+};
+
+__device__ inline Touched touch_records()
+{
+    Touched t{};
+#if defined(__HIP_DEVICE_COMPILE__)
+    const auto k = __builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("s_load_dword %0, %5, 0x80\n\t"
+                 "s_load_dword %1, %5, 0xc0\n\t"
+                 "s_load_dword %2, %5, 0x100\n\t"
+                 "s_load_dword %3, %5, 0x140\n\t"
+                 "s_load_dword %4, %5, 0x180"
+                 : "=s"(t.w[0]), "=s"(t.w[1]), "=s"(t.w[2]), "=s"(t.w[3]), "=s"(t.w[4])
+                 : "s"(k));
+#endif
+    return t;
+}
+
+// The touched registers stay allocated until here.  `after` is a field of
+// the tile's record: the compiler waits for the scalar loads (all of them:
+// they return out of order) before it reads it, so none of the touches is
+// still in flight once the registers are released.
+__device__ inline void release(const Touched &t, uint64_t after)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" ::"s"(t.w[0]), "s"(t.w[1]), "s"(t.w[2]), "s"(t.w[3]), "s"(t.w[4]), "s"(after));
+#endif
+}
+
 // Fused re-layout of up to three tensors: S2H reads the sequence-sharded
 // side and writes the head-sharded side, !S2H the reverse.  ONE: a launch of
 // one tensor.
@@ -109,11 +150,16 @@ __global__ __launch_bounds__(BS) void tile_kernel(const TileDesc D)
     // testing only after the first lets the first tile's scalar loads go
     // out in one batch
     uint32_t x = blockIdx.x;
+    Touched touched;
+    if constexpr (!ONE)
+        touched = touch_records();
     do {
         uint32_t tile, bz;
         tile_and_batch(D, x, blockIdx.z, tile, bz);
         const uint32_t t = xcd_tile(tile, D.xcd_span);
         const TileSeg sg = D.seg[segment_of<ONE>(D, t)];   // one batch of scalar loads
+        if constexpr (!ONE)
+            release(touched, sg.seq);
         const TileOrigin o = tile_origin(D, sg, ONE ? t : t - sg.tile_begin, blockIdx.y, bz);
         const __amdgpu_buffer_rsrc_t rseq = make_rsrc(sg.seq + o.seq_off, rest(sg.bytes, o.seq_off));
         const __amdgpu_buffer_rsrc_t rhead =
@@ -152,11 +198,16 @@ __global__ __launch_bounds__(BS) void tile_kernel_staged(const TileDesc D)
     // testing only after the first lets the first tile's scalar loads go
     // out in one batch
     uint32_t x = blockIdx.x;
+    Touched touched;
+    if constexpr (!ONE)
+        touched = touch_records();
     do {
         uint32_t tile, bz;
         tile_and_batch(D, x, blockIdx.z, tile, bz);
         const uint32_t t = xcd_tile(tile, D.xcd_span);
         const TileSeg sg = D.seg[segment_of<ONE>(D, t)];   // one batch of scalar loads
+        if constexpr (!ONE)
+            release(touched, sg.seq);
         const TileOrigin o = tile_origin(D, sg, ONE ? t : t - sg.tile_begin, blockIdx.y, bz);
         const __amdgpu_buffer_rsrc_t rseq = make_rsrc(sg.seq + o.seq_off, rest(sg.bytes, o.seq_off));
         const __amdgpu_buffer_rsrc_t rhead =
