@@ -720,9 +720,9 @@ def test_int32_global_tags_full_size(w, mode):
 def test_general_groups_full_size(G):
     """The batch-sweep shape at B = 8 (N = 8, S = 8192, Llama-3.2-1B heads)
     in the general form with G groups of N/G ranks: the built-in launch
-    shape, the shape autotune picks, and an LDS-staged shape, each on both
-    passes of split tags in both directions, every element against the
-    oracle."""
+    shape, the shape autotune picks, an LDS-staged shape and a shape in
+    tile order 3, each on both passes of split tags in both directions,
+    every element against the oracle."""
     needs_gpu()
     name, N, B, S, Hq, Hkv, d = workloads.BATCH_SWEEP[-1]
     shape = (N, B, S, Hq, Hkv, d)
@@ -740,6 +740,8 @@ def test_general_groups_full_size(G):
     print("  autotuned", b.basp_plan_get_tuning(plan, 0), b.basp_plan_get_tuning(plan, 1), flush=True)
     check_split_tags(plan, "groups", shape, G=G)
     b.basp_plan_set_tuning(plan, stage=2, block_size=64, tile_heads=2, batch_order=2)
+    check_split_tags(plan, "groups", shape, G=G)
+    b.basp_plan_set_tuning(plan, tile_order=3, block_size=128, tile_heads=2, lane_order=1)
     check_split_tags(plan, "groups", shape, G=G)
     torch.cuda.empty_cache()
 
