@@ -660,7 +660,7 @@ def tune_shapes(args):
         picks = {}
         for mode, code in modes:   # autotune's picks in each mode
             p = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, code)
-            sets = table_sets(p.info, 2)
+            sets = table_sets(p.info, 1)
             picks[mode] = []
             for _ in range(args.tune_autotunes):
                 b.basp_plan_set_tuning(p)
