@@ -94,7 +94,7 @@ def parse_args(argv=None):
     ap.add_argument("--autotune", action="store_true",
                     help="measure launch shapes per plan instead of reading the table")
     ap.add_argument("--builtin-shapes", action="store_true", help="the library's built-in launch shapes")
-    ap.add_argument("--detail-out", default=os.path.join("gpurun_out", "bench_detail.json"))
+    ap.add_argument("--detail-out", default=os.path.join("bench_out", "bench_detail.json"))
     ap.add_argument("--detail-iters", type=int, default=60)
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="skip the table of every named workload")
