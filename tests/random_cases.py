@@ -33,7 +33,7 @@ def case(seed):
     return (N, B, S, Hq, Hkv, d), ("basp" if mode else "ulysses"), int(rng.integers(0, 2)), tuning
 
 
-COUNT = 40
+COUNT = 200
 
 
 def group_case(seed):
@@ -62,4 +62,4 @@ def group_case(seed):
     return (N, B, S, Hq, Hkv, d), G, int(rng.integers(0, 2)), tuning
 
 
-GROUP_COUNT = 20
+GROUP_COUNT = 100
