@@ -65,9 +65,11 @@
  * - Pointer checks made before any launch: a NULL pointer to a non-empty
  *   buffer is BASP_ERR_INVALID; a pointer not aligned to the element size is
  *   BASP_ERR_ALIGN; an output range overlapping an input range, or another
- *   output range, is BASP_ERR_ALIAS.  Inputs may overlap each other.  Wider
- *   alignment (up to 16 bytes) of all pointers and of d*elem_size lets the
- *   kernels use wider vector accesses; the result is the same.
+ *   output range, is BASP_ERR_ALIAS.  Inputs may overlap each other.  A row
+ *   size d*elem_size that is a multiple of 16 bytes lets the kernels use
+ *   16-byte accesses (8, 4 or 2 bytes otherwise), at any element-aligned
+ *   address; buffers that start on a 16-byte boundary are faster, since
+ *   their rows do not straddle cache lines.  The result is the same.
  * - A launch failure reported by the HIP runtime is BASP_ERR_HIP.
  * - With S = 0 every buffer is empty: calls check the plan and return
  *   BASP_OK without touching memory (pointers may then be NULL).
@@ -322,8 +324,8 @@ basp_status basp_seq_to_head_unfused_noalloc(const basp_plan *plan, const void *
  *   batch_order          1 = the batch indices one after another (built-in),
  *                        2 = batch indices interleaved with the tiles, so
  *                        that neighbouring work-groups alternate sequences
- * vectors_per_thread and block_size apply to 16-byte vectors; rows or
- * pointers that need narrower vectors run 256 threads with 4 vectors each.
+ * vectors_per_thread and block_size apply to 16-byte vectors; rows that
+ * need narrower vectors run 256 threads with 4 vectors each.
  * basp_plan_set_tuning sets both directions, basp_plan_set_direction_tuning
  * one; basp_plan_get_tuning reads one.  Errors: BASP_ERR_INVALID on a NULL
  * argument, an unknown direction or an out-of-range field;

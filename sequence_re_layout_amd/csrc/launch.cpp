@@ -74,18 +74,16 @@ Shape for_vector_width(Shape sh, int vw, uint32_t A)
 uint64_t addr(const void *p) { return reinterpret_cast<uint64_t>(p); }
 
 // Widest vector (16, 8, 4 or 2 bytes, never below the element size) that
-// divides the row and every address.
-int vector_width(const basp_plan &p, const uint64_t *addrs, int n)
+// divides the row.  The addresses need only the element alignment the entry
+// points check: compute queues run in the unaligned access mode, in which a
+// buffer access of any width may start at any byte (compilers emit 16-byte
+// loads for byte-aligned copies on this target), and rows that straddle
+// cache lines cost less that way than split into narrower vectors.
+int vector_width(const basp_plan &p)
 {
     int vw = 16;
-    while (vw > p.es) {
-        bool fits = p.row_bytes % vw == 0;
-        for (int i = 0; i < n && fits; ++i)
-            fits = addrs[i] % vw == 0;
-        if (fits)
-            break;
+    while (vw > p.es && p.row_bytes % vw != 0)
         vw /= 2;
-    }
     return vw;
 }
 
@@ -182,12 +180,7 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
     std::memset(&L, 0, sizeof(L));
     if (!grid_fits(p))
         return BASP_ERR_UNSUPPORTED;
-    uint64_t addrs[6];
-    for (int i = 0; i < nseg; ++i) {
-        addrs[2 * i] = segs[i].seq;
-        addrs[2 * i + 1] = segs[i].head;
-    }
-    const int vw = vector_width(p, addrs, 2 * nseg);
+    const int vw = vector_width(p);
     const uint32_t A = uint32_t(p.row_bytes / vw);
     const Shape sh =
         for_vector_width(resolve(p, p.tuning[s2h ? BASP_SEQ_TO_HEAD : BASP_HEAD_TO_SEQ]), vw, A);
@@ -454,8 +447,7 @@ int prepare_seq_to_head_unfused(const basp_plan &p, const void *q, const void *k
     const uint64_t off[3] = {0, qb, qb + kb};
     const uint64_t bytes[3] = {qb, kb, kb};
     const uint32_t heads[3] = {uint32_t(p.Hq), uint32_t(p.Hkv), uint32_t(p.Hkv)};
-    const uint64_t addrs[6] = {src[0], src[1], src[2], o, w1, w2};
-    const int vw = vector_width(p, addrs, 6);
+    const int vw = vector_width(p);
 
     const uint32_t N = p.N, P = p.P, Bl = p.Bl, St = uint32_t(p.St), G = p.G;
     PermSpec pack[3], xchg[3], unpack[3];

@@ -3,8 +3,8 @@
 // arithmetic are in launch.hpp / launch.cpp.
 //
 // Each kernel moves (token, head) rows whole with 16-byte vector accesses
-// (8/4/2 bytes when a row or a pointer is not 16-byte aligned) and never
-// interprets values.  A lane first issues all of its VPT loads, then its
+// (8/4/2 bytes when the row size is not a multiple of 16 bytes; pointers
+// need only their element alignment) and never interprets values.  A lane first issues all of its VPT loads, then its
 // stores, with no branch in between, so the loads of a wave overlap.
 //
 // Every access is a raw buffer instruction through a descriptor that covers

@@ -319,8 +319,8 @@ def test_b1_basp_equals_ulysses():
 
 
 def test_unaligned_views():
-    """Tensors that start 2 bytes past a 16-byte boundary take the narrow
-    vector path and give the same bits."""
+    """Tensors that start 2 bytes past a 16-byte boundary take 16-byte
+    accesses at those addresses and give the same bits."""
     needs_gpu()
     N, B, S, Hq, Hkv, d = 4, 2, 4 * 20, 8, 4, 64
     plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, 1)

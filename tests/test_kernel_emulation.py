@@ -4,10 +4,10 @@ CPU and compared with the oracle (no GPU).
 ``tests/emu/kernel_emu.cpp`` compiles the library's own plan.cpp, launch.cpp
 and launch.hpp with g++ and executes every launch on the host (see its
 header).  These tests drive it over ragged shapes, all launch shapes, both
-layouts, both element sizes, narrow vector widths (misaligned pointers) and
-the degenerate cases, and require (a) the oracle's result bit for bit, with
-every destination written, and (b) no in-tile access outside the kernels'
-buffer descriptors.
+layouts, both element sizes, narrow vector widths (short rows), misaligned
+views and the degenerate cases, and require (a) the oracle's result bit for
+bit, with every destination written, and (b) no in-tile access outside the
+kernels' buffer descriptors.
 """
 import ctypes
 import os
@@ -174,21 +174,29 @@ def test_tunings(emu, tuning):
 
 
 def test_staging_used_where_it_applies(emu):
-    """The staged kernel runs for 16-byte vectors (and is emulated as such);
-    narrower vectors fall back to the direct kernel with the same result."""
+    """The staged kernel runs for 16-byte vectors (and is emulated as such),
+    also on views that start 2 bytes past a 16-byte boundary; rows that
+    need narrower vectors fall back to the direct kernel with the same
+    result."""
     shape = (8, 2, 8 * 129, 24, 8, 128)
     check_s2h(emu, shape, 1, 0, 2, dict(stage=2))
     assert emu.emu_last_staged() == 1
     check_h2s(emu, shape, 0, 1, 2, dict(stage=2, vectors_per_thread=1))
     assert emu.emu_last_staged() == 1
     check_s2h(emu, shape, 1, 0, 2, dict(stage=2), offset=1)
+    assert emu.emu_last_staged() == 1
+    assert check_s2h(emu, (8, 2, 8 * 33, 24, 8, 4), 1, 0, 2, dict(stage=2)) == 8
     assert emu.emu_last_staged() == 0
 
 
-@pytest.mark.parametrize("offset,es,expect_vw", [(0, 2, 16), (1, 2, 2), (2, 2, 4), (4, 2, 8),
-                                                  (1, 4, 4), (2, 4, 8)])
-def test_vector_width_follows_alignment(emu, offset, es, expect_vw):
-    shape = (4, 2, 4 * 21, 8, 4, 64)
+@pytest.mark.parametrize("d,es,offset,expect_vw", [
+    (64, 2, 0, 16), (64, 2, 1, 16), (64, 2, 2, 16), (64, 2, 4, 16), (64, 4, 1, 16), (64, 4, 2, 16),
+    (4, 2, 0, 8), (4, 2, 1, 8), (2, 2, 3, 4), (1, 2, 1, 2), (3, 4, 1, 4), (2, 4, 0, 8), (5, 4, 2, 4)])
+def test_vector_width_follows_row_size(emu, d, es, offset, expect_vw):
+    """The widest vector that divides the row, whatever the pointers'
+    alignment beyond the element size (views `offset` elements past an
+    allocation start)."""
+    shape = (4, 2, 4 * 21, 8, 4, d)
     assert check_s2h(emu, shape, 1, 0, es, offset=offset) == expect_vw
     assert check_h2s(emu, shape, 0, 1, es, offset=offset) == expect_vw
     # the same vector width with batch indices interleaved and a capped grid
