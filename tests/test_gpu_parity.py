@@ -318,28 +318,38 @@ def test_b1_basp_equals_ulysses():
     assert torch.equal(a.view(torch.int16), u.view(torch.int16))
 
 
-def test_unaligned_views():
-    """Tensors that start 2 bytes past a 16-byte boundary take 16-byte
-    accesses at those addresses and give the same bits."""
+@pytest.mark.parametrize("shift", [1, 2, 4], ids=["2B", "4B", "8B"])
+def test_unaligned_views(shift):
+    """Tensors that start 2, 4 or 8 bytes past a 16-byte boundary take
+    16-byte accesses at those addresses (direct and LDS-staged kernels,
+    both directions) and give the same bits."""
     needs_gpu()
     N, B, S, Hq, Hkv, d = 4, 2, 4 * 20, 8, 4, 64
     plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, 1)
     q, k, v = seq_inputs(B, S, Hq, Hkv, d, "bf16")
     def shifted(t):
-        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
-        buf[1:].copy_(t.cuda())
-        return buf[1:]
-    out_buf = torch.empty(plan.info["qkv_elems"] + 1, dtype=torch.bfloat16, device="cuda")
-    out = out_buf[1:]
+        buf = torch.empty(t.numel() + shift, dtype=t.dtype, device="cuda")
+        buf[shift:].copy_(t.cuda())
+        return buf[shift:]
+    out_buf = torch.empty(plan.info["qkv_elems"] + shift, dtype=torch.bfloat16, device="cuda")
+    out = out_buf[shift:]
+    o_buf = torch.empty(plan.info["q_elems"] + shift, dtype=torch.bfloat16, device="cuda")
+    o_out = o_buf[shift:]
     want = oracle.seq_to_head_qkv(inputs.raw_bits(q), inputs.raw_bits(k), inputs.raw_bits(v),
                                   1, N, B, S, Hq, Hkv, d)
-    for tuning in ({}, dict(batch_order=2, max_grid=5, tile_order=1)):
+    o = q   # a Q-shaped head-sharded input for head->seq
+    want_o = oracle.head_to_seq(inputs.raw_bits(o), 1, N, B, S, Hq, d)
+    for tuning in ({}, dict(batch_order=2, max_grid=5, tile_order=1), dict(stage=2, block_size=64, tile_heads=2),
+                   dict(tile_order=3, vectors_per_thread=2)):
         if tuning:
             b.basp_plan_set_tuning(plan, **tuning)
         out.fill_(0)
+        o_out.fill_(0)
         b.basp_seq_to_head(plan, shifted(q), shifted(k), shifted(v), out)
+        b.basp_head_to_seq(plan, shifted(o), o_out)
         torch.cuda.synchronize()
         assert np.array_equal(bits(out), want), tuning
+        assert np.array_equal(bits(o_out), want_o), tuning
 
 
 def test_all_bf16_patterns_round_trip():
