@@ -432,6 +432,28 @@ def test_unfused_matches_oracle(shape, layout, mode):
     assert np.array_equal(bits(out), want)
 
 
+def test_unfused_unaligned_views():
+    """The unfused baseline on views 2 bytes past a 16-byte boundary (its
+    inputs, output and workspace) keeps 16-byte accesses and gives the
+    oracle's bits."""
+    needs_gpu()
+    N, B, S, Hq, Hkv, d = 8, 2, 8 * 16, 32, 8, 64
+    plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, 1)
+    q, k, v = seq_inputs(B, S, Hq, Hkv, d, "bf16")
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+        buf[1:].copy_(t.cuda())
+        return buf[1:]
+    ws_buf = torch.empty(b.basp_unfused_workspace_bytes(plan) + 2, dtype=torch.uint8, device="cuda")
+    out_buf = torch.zeros(plan.info["qkv_elems"] + 1, dtype=torch.bfloat16, device="cuda")
+    out = out_buf[1:]
+    b.basp_seq_to_head_unfused(plan, shifted(q), shifted(k), shifted(v), out, ws_buf.data_ptr() + 2)
+    torch.cuda.synchronize()
+    want = oracle.seq_to_head_qkv(inputs.raw_bits(q), inputs.raw_bits(k), inputs.raw_bits(v),
+                                  1, N, B, S, Hq, Hkv, d)
+    assert np.array_equal(bits(out), want)
+
+
 # ------------------------------------------------------------ error paths --
 
 def test_device_error_paths():
