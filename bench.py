@@ -50,6 +50,7 @@ import argparse
 import csv
 import glob
 import hashlib
+import itertools
 import json
 import os
 import statistics
@@ -104,6 +105,10 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tune-shapes", metavar="OUT")
     ap.add_argument("--tune-autotunes", type=int, default=3, help="autotune runs per plan for --tune-shapes")
+    ap.add_argument("--tune-sweep-mib", type=int, default=128,
+                    help="--tune-shapes also sweeps each direction whose call moves at most this many MiB")
+    ap.add_argument("--tune-workloads", default="",
+                    help="comma-separated workloads for --tune-shapes (others keep the current table's entries)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--trace-summary", metavar="TRACE_DIR")
     ap.add_argument("--counter-summary", nargs="+", metavar="PMC_DIR")
@@ -637,14 +642,85 @@ def measure_pair(b, p, sets, R, n):
             "h2s_us": u * 1e6, "h2s_gbs": rate(hb, u)}
 
 
+SWEEP_KEEP = 2   # shapes per swept direction that enter the pair comparison
+
+
+def sweep_grid(B):
+    """Launch shapes of the per-direction sweep: both kernels, every
+    work-group size and tile order, 1, 2 or 4 vectors per lane, 1-8 heads per
+    tile, direct tiles of one pass or of 8 or 16 tokens (several passes), both
+    lane orders of the direct kernel, both XCD orders, and both batch orders
+    when there is more than one sequence."""
+    grid = []
+    for bo, stage, block, vpt, th, tt, to, lo, xr in itertools.product(
+            (1, 2) if B > 1 else (1,), (1, 2), (64, 128, 256), (1, 2, 4), (1, 2, 4, 8),
+            (0, 8, 16), (1, 2, 3), (1, 2), (1, 2)):
+        if stage == 2 and (tt or lo == 2):   # a staged tile is one pass; its lanes follow the layouts
+            continue
+        t = {"batch_order": bo, "stage": stage, "block_size": block, "vectors_per_thread": vpt,
+             "tile_heads": th, "tile_order": to, "xcd_remap": xr, "cache_policy": 4}
+        if tt:
+            t["tile_tokens"] = tt
+        if stage == 1:
+            t["lane_order"] = lo
+        grid.append(t)
+    return grid
+
+
+def sweep_direction(b, p, sets, R, direction, grid, keep=SWEEP_KEEP):
+    """The best `keep` shapes of one direction, each direction timed alone
+    with its launches back to back from HIP graphs on the rotating sets: every
+    shape of `grid` from a short graph, then the best 16 in 3 interleaved
+    rounds of longer graphs.  The plan's tuning of that direction is kept."""
+    i = p.info
+    if direction == b.BASP_SEQ_TO_HEAD:
+        nbytes = i["qkv_bytes_moved"]
+
+        def fn(j):
+            s = sets[j % R]
+            b.basp_seq_to_head(p, s["q"], s["k"], s["v"], s["out"])
+    else:
+        nbytes = i["o_bytes_moved"]
+
+        def fn(j):
+            s = sets[j % R]
+            b.basp_head_to_seq(p, s["o"], s["o_out"])
+    held = b.basp_plan_get_tuning(p, direction)
+    est = 2e-6 + nbytes / 6e12                       # seconds per call, roughly
+    short, long_ = max(20, min(200, int(3e-4 / est))), max(60, min(600, int(2e-3 / est)))
+    coarse = []
+    for t in grid:
+        try:
+            b.basp_plan_set_direction_tuning(p, direction, **t)
+        except b.BaspError:                          # beyond the index limits
+            continue
+        coarse.append((graph_seconds(fn, short, reps=2), t))
+    coarse.sort(key=lambda c: c[0])
+    top = [t for _, t in coarse[:16]]
+    times = [[] for _ in top]
+    for _ in range(3):
+        for c, t in enumerate(top):
+            b.basp_plan_set_direction_tuning(p, direction, **t)
+            times[c].append(graph_seconds(fn, long_, reps=3))
+    b.basp_plan_set_direction_tuning(p, direction, **held)
+    order = sorted(range(len(top)), key=lambda c: statistics.median(times[c]))
+    return [top[c] for c in order[:keep]]
+
+
 def tune_shapes(args):
     """The launch-shape table: for every named workload and mode,
     basp_plan_autotune runs --tune-autotunes times (each from the built-in
-    shapes).  Then, per mode, the distinct pairs autotune kept in either
-    mode (the two plans share their tensors' sizes; with B = 1 they are the
-    same plan), the built-in pair and the pair the current table holds are
-    timed as whole back-to-back steps from HIP graphs in 3 interleaved
-    rounds; the pair with the lowest median step time is kept."""
+    shapes).  A direction whose call moves at most --tune-sweep-mib MiB is
+    also swept over a wider grid (sweep_grid), timed alone from HIP graphs:
+    short calls are where the autotuner's one-launch timings rank shapes
+    least like back-to-back runs.  Then, per mode, the distinct pairs
+    autotune kept in either mode (the two plans share their tensors' sizes;
+    with B = 1 they are the same plan), the built-in pair, the pair the
+    current table holds and the pairs of the swept shapes are timed as whole
+    back-to-back steps from HIP graphs in 3 interleaved rounds; the pair with
+    the lowest median step time is kept.  With --tune-workloads only the
+    named workloads are measured; the others keep the current table's
+    entries."""
     import torch
     from sequence_re_layout_amd import binding as b
     from sequence_re_layout_amd import launch_shapes, workloads
@@ -655,7 +731,13 @@ def tune_shapes(args):
            "kernel_sources_sha256": kernel_sources_sha256(), "shapes": {}}
     dirs = (("seq_to_head", b.BASP_SEQ_TO_HEAD), ("head_to_seq", b.BASP_HEAD_TO_SEQ))
     modes = (("basp", b.BASP_MODE_BASP), ("ulysses", b.BASP_MODE_ULYSSES))
+    only = set(args.tune_workloads.split(",")) if args.tune_workloads else None
+    current = launch_shapes.table().get("shapes", {})
     for (name, N, B, S, Hq, Hkv, d) in workloads.ALL + workloads.EXTRA:
+        if only is not None and name not in only:
+            if name in current:
+                out["shapes"][name] = current[name]
+            continue
         out["shapes"][name] = {}
         picks = {}
         for mode, code in modes:   # autotune's picks in each mode
@@ -682,9 +764,24 @@ def tune_shapes(args):
             cands = [({}, {})]
             held = launch_shapes.lookup(name, mode)
             other = [m for m, _ in modes if m != mode][0]
-            for pair in ([tuple(held)] if held is not None else []) + picks[mode] + picks[other]:
+            base = ([tuple(held)] if held is not None else []) + picks[mode] + picks[other] + [({}, {})]
+            for pair in base:
                 if pair not in cands:
                     cands.append(pair)
+            # the swept shapes of each direction, paired with each other and
+            # with the first base pair's shape of the other direction
+            swept = []
+            for (_, dcode), nbytes in zip(dirs, (i["qkv_bytes_moved"], i["o_bytes_moved"])):
+                top = []
+                if nbytes <= args.tune_sweep_mib << 20:
+                    b.basp_plan_set_direction_tuning(p, dcode, **base[0][dcode])
+                    top = sweep_direction(b, p, sets, R, dcode, sweep_grid(B))
+                swept.append(top)
+            for ts in swept[0] + [base[0][0]]:
+                for th in swept[1] + [base[0][1]]:
+                    pair = ({k: v for k, v in ts.items() if v}, {k: v for k, v in th.items() if v})
+                    if pair not in cands:
+                        cands.append(pair)
             times = [[] for _ in cands]
             for _ in range(3):
                 for c, (ts, th) in enumerate(cands):
@@ -699,8 +796,9 @@ def tune_shapes(args):
                 "step_us": med[best], "s2h_us": statistics.median(t["s2h_us"] for t in pick),
                 "h2s_us": statistics.median(t["h2s_us"] for t in pick),
                 "candidates": len(cands), "candidate_step_us": med}
-            print("tune-shapes: %s %s: %d candidates, step %.1f us (built-in %.1f us)"
-                  % (name, mode, len(cands), med[best], med[0]), file=sys.stderr, flush=True)
+            print("tune-shapes: %s %s: %d candidates (%d from the sweep), step %.1f us (built-in %.1f us)"
+                  % (name, mode, len(cands), sum(map(len, swept)), med[best], med[0]), file=sys.stderr,
+                  flush=True)
             del sets
             torch.cuda.empty_cache()
     with open(args.tune_shapes, "w") as f:

@@ -177,3 +177,26 @@ def test_optional_leg_records_errors(capsys):
     assert out == {"error": "ZeroDivisionError: division by zero"}
     assert "ZeroDivisionError" in capsys.readouterr().err
     json.dumps(out)
+
+
+def test_sweep_grid_shapes_are_valid_tunings():
+    """Every shape of the launch-shape sweep is a distinct tuning that the
+    library accepts for both directions of the named workloads; staged shapes
+    are single-pass tiles without a lane order, and the batch order varies
+    only with more than one sequence."""
+    from sequence_re_layout_amd import binding as b, workloads
+    for B in (1, 2):
+        grid = bench.sweep_grid(B)
+        keys = {tuple(sorted(t.items())) for t in grid}
+        assert len(keys) == len(grid)
+        assert {t["batch_order"] for t in grid} == ({1} if B == 1 else {1, 2})
+        for t in grid:
+            if t["stage"] == 2:
+                assert "tile_tokens" not in t and "lane_order" not in t
+    for name, N, B, S, Hq, Hkv, d in (workloads.TINY, workloads.BY_NAME["llama3.2-1b_s8k_b1"]):
+        p = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, b.BASP_MODE_BASP)
+        for t in bench.sweep_grid(B):
+            for direction in (b.BASP_SEQ_TO_HEAD, b.BASP_HEAD_TO_SEQ):
+                b.basp_plan_set_direction_tuning(p, direction, **t)
+                got = b.basp_plan_get_tuning(p, direction)
+                assert all(got[k] == v for k, v in t.items())

@@ -230,6 +230,20 @@ def test_workloads_scaled(emu, w, mode):
     check_h2s(emu, w[1:], mode, 0, 2)
 
 
+@pytest.mark.parametrize("mode", ["basp", "ulysses"])
+@pytest.mark.parametrize("w", SCALED, ids=[w[0] + "_S/16" for w in SCALED])
+def test_workloads_scaled_table_shapes(emu, w, mode):
+    """Each workload's launch shapes from the measured table (the ones the
+    benchmark times), each direction with its own, at a sixteenth of S."""
+    from sequence_re_layout_amd import launch_shapes
+    shapes = launch_shapes.lookup(w[0], mode)
+    if shapes is None:
+        pytest.skip("no table entry")
+    m = {"basp": 1, "ulysses": 0}[mode]
+    check_s2h(emu, w[1:], m, 0, 2, shapes[0])
+    check_h2s(emu, w[1:], m, 0, 2, shapes[1])
+
+
 @pytest.mark.parametrize("mode", [1, 0], ids=["basp", "ulysses"])
 def test_llama1b_full_size(emu, mode):
     check_s2h(emu, workloads.LLAMA_1B[1:], mode, 0, 2)
