@@ -77,5 +77,9 @@ def test_pins_catch_mutant(tmp_path, name, old, new, occ):
                    check=True)
     code = ("import sys; sys.path.insert(0, %r); import oracle; oracle._use_library(%r); "
             "from tests import oracle_pins; oracle_pins.run_all()" % (ROOT, str(lib)))
-    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=600)
+    # two OpenMP threads per child: with several test workers at once, a
+    # child per worker with a thread per core oversubscribes the CPUs, and
+    # the oracle's many small parallel loops then crawl
+    env = dict(os.environ, OMP_NUM_THREADS="2")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=600, env=env)
     assert res.returncode != 0, "mutant %s survived every pin" % name
