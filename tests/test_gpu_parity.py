@@ -1099,33 +1099,39 @@ def swept_shapes():
     return grid + [dict(t, vectors_per_thread=8) for t in grid if t["vectors_per_thread"] == 4]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "int32"])
+@pytest.mark.parametrize("layout", [0, 1], ids=["head_major", "token_major"])
 @pytest.mark.parametrize("mode", ["basp", "ulysses"])
 @pytest.mark.parametrize("shape", [(8, 2, 8 * 37, 24, 8, 128), (4, 2, 4 * 203, 8, 4, 64)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_every_swept_launch_shape(shape, mode):
+def test_every_swept_launch_shape(shape, mode, layout, dtype):
     """Both directions with each of the 4 032 launch shapes of the sweep
     grid, on ragged shapes (partial token blocks, head counts that tiles of
-    4 and 8 heads do not divide, 128- and 256-byte rows): every output
-    element against the oracle, on a sentinel-filled output each time."""
+    4 and 8 heads do not divide, 128- to 512-byte rows), both layouts, bf16
+    values and int32 tags: every output element against the oracle, on a
+    sentinel-filled output each time."""
     needs_gpu()
     N, B, S, Hq, Hkv, d = shape
     m = MODE[mode]
-    plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, m)
-    q, k, v = seq_inputs(B, S, Hq, Hkv, d, "bf16")
-    o = inputs.normal_bf16(B * S * Hq * d, inputs.SEED_O)
-    dev = lambda a: torch.from_numpy(a.view(np.int16)).cuda()
-    want_qkv = dev(oracle.seq_to_head_qkv(bits(q), bits(k), bits(v), m, N, B, S, Hq, Hkv, d))
-    want_o = dev(oracle.head_to_seq(bits(o), m, N, B, S, Hq, d))
+    code, view = (b.BASP_BF16, torch.int16) if dtype == "bf16" else (b.BASP_INT32, torch.int32)
+    plan = b.basp_plan_create_ex(N, B, S, Hq, Hkv, d, code, m, layout)
+    q, k, v = seq_inputs(B, S, Hq, Hkv, d, dtype)
+    nq = B * S * Hq * d
+    o = inputs.normal_bf16(nq, inputs.SEED_O) if dtype == "bf16" else inputs.tags_int32(nq, 7)
+    npv = np.int16 if dtype == "bf16" else np.int32
+    dev = lambda a: torch.from_numpy(a.view(npv)).cuda()
+    want_qkv = dev(oracle.seq_to_head_qkv(bits(q), bits(k), bits(v), m, N, B, S, Hq, Hkv, d, layout))
+    want_o = dev(oracle.head_to_seq(bits(o), m, N, B, S, Hq, d, layout))
     q, k, v, o = (t.cuda() for t in (q, k, v, o))
-    qkv = torch.empty(want_qkv.numel(), dtype=torch.bfloat16, device="cuda")
-    o_out = torch.empty(want_o.numel(), dtype=torch.bfloat16, device="cuda")
+    qkv = torch.empty(want_qkv.numel(), dtype=q.dtype, device="cuda")
+    o_out = torch.empty(want_o.numel(), dtype=q.dtype, device="cuda")
     shapes = swept_shapes()
-    print("sweep grid", shape, mode, len(shapes), "shapes", flush=True)
+    print("sweep grid", shape, mode, layout, dtype, len(shapes), "shapes", flush=True)
     for t in shapes:
         b.basp_plan_set_tuning(plan, **t)
-        qkv.view(torch.int16).fill_(-1)
-        o_out.view(torch.int16).fill_(-1)
+        qkv.view(view).fill_(-1)
+        o_out.view(view).fill_(-1)
         b.basp_seq_to_head(plan, q, k, v, qkv)
         b.basp_head_to_seq(plan, o, o_out)
-        assert torch.equal(qkv.view(torch.int16), want_qkv), ("seq->head", t)
-        assert torch.equal(o_out.view(torch.int16), want_o), ("head->seq", t)
+        assert torch.equal(qkv.view(view), want_qkv), ("seq->head", t)
+        assert torch.equal(o_out.view(view), want_o), ("head->seq", t)

@@ -370,24 +370,25 @@ def test_random_general_groups(emu, seed):
         check_h2s(emu, shape, oracle.GROUPS, layout, es, tuning, G=G)
 
 
+@pytest.mark.parametrize("layout", [0, 1], ids=["head_major", "token_major"])
 @pytest.mark.parametrize("mode", [1, 0], ids=["basp", "ulysses"])
 @pytest.mark.parametrize("shape", [(8, 2, 8 * 5, 24, 8, 128), (4, 2, 4 * 13, 8, 4, 64)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_every_swept_launch_shape(emu, shape, mode):
+def test_every_swept_launch_shape(emu, shape, mode, layout):
     """Each of the launch shapes the table's per-direction sweep can pick
     (bench.py sweep_grid, plus 8 vectors per lane), both directions, on small
-    ragged shapes: every access inside its descriptor and the oracle's
-    result."""
+    ragged shapes in both layouts: every access inside its descriptor and the
+    oracle's result."""
     import bench
     N, B, S, Hq, Hkv, d = shape
     rng = np.random.default_rng(11)
     q, k, v, o = (_rand(B * S * H * d, 2, rng) for H in (Hq, Hkv, Hkv, Hq))
-    want_qkv = oracle.seq_to_head_qkv(q, k, v, mode, N, B, S, Hq, Hkv, d)
-    want_o = oracle.head_to_seq(o, mode, N, B, S, Hq, d)
+    want_qkv = oracle.seq_to_head_qkv(q, k, v, mode, N, B, S, Hq, Hkv, d, layout)
+    want_o = oracle.head_to_seq(o, mode, N, B, S, Hq, d, layout)
     grid = bench.sweep_grid(2)
     grid += [dict(t, vectors_per_thread=8) for t in grid if t["vectors_per_thread"] == 4]
     for t in grid:
-        run = Run(emu, shape, mode, 0, 2, t)
+        run = Run(emu, shape, mode, layout, 2, t)
         out = _empty(want_qkv.size, 2)
         run("emu_seq_to_head", q, k, v, out)
         assert np.array_equal(out, want_qkv), ("seq->head", t)
