@@ -1135,3 +1135,33 @@ def test_every_swept_launch_shape(shape, mode, layout, dtype):
         b.basp_head_to_seq(plan, o, o_out)
         assert torch.equal(qkv.view(view), want_qkv), ("seq->head", t)
         assert torch.equal(o_out.view(view), want_o), ("head->seq", t)
+
+
+@pytest.mark.parametrize("layout", [0, 1], ids=["head_major", "token_major"])
+def test_every_swept_launch_shape_general_groups(layout):
+    """The 4 032 launch shapes of the sweep grid on a general G-group plan in
+    which G, P and Bl all exceed 1 (8 ranks, 4 sequences, 2 groups of 4
+    ranks holding 2 sequences each; 37 tokens per rank), both directions:
+    every output element against the oracle."""
+    needs_gpu()
+    N, B, S, Hq, Hkv, d, G = 8, 4, 4 * 37, 8, 4, 64, 2
+    m = MODE["groups"]
+    plan = b.basp_plan_create_groups(N, B, S, Hq, Hkv, d, b.BASP_BF16, G, layout)
+    q, k, v = seq_inputs(B, S, Hq, Hkv, d, "bf16")
+    o = inputs.normal_bf16(B * S * Hq * d, inputs.SEED_O)
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).cuda()
+    want_qkv = dev(oracle.seq_to_head_qkv(bits(q), bits(k), bits(v), m, N, B, S, Hq, Hkv, d, layout, G=G))
+    want_o = dev(oracle.head_to_seq(bits(o), m, N, B, S, Hq, d, layout, G=G))
+    q, k, v, o = (t.cuda() for t in (q, k, v, o))
+    qkv = torch.empty(want_qkv.numel(), dtype=torch.bfloat16, device="cuda")
+    o_out = torch.empty(want_o.numel(), dtype=torch.bfloat16, device="cuda")
+    shapes = swept_shapes()
+    print("sweep grid, general groups", layout, len(shapes), "shapes", flush=True)
+    for t in shapes:
+        b.basp_plan_set_tuning(plan, **t)
+        qkv.view(torch.int16).fill_(-1)
+        o_out.view(torch.int16).fill_(-1)
+        b.basp_seq_to_head(plan, q, k, v, qkv)
+        b.basp_head_to_seq(plan, o, o_out)
+        assert torch.equal(qkv.view(torch.int16), want_qkv), ("seq->head", t)
+        assert torch.equal(o_out.view(torch.int16), want_o), ("head->seq", t)

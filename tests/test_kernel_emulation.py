@@ -395,3 +395,26 @@ def test_every_swept_launch_shape(emu, shape, mode, layout):
         out = _empty(want_o.size, 2)
         run("emu_head_to_seq", o, out)
         assert np.array_equal(out, want_o), ("head->seq", t)
+
+
+@pytest.mark.parametrize("layout", [0, 1], ids=["head_major", "token_major"])
+def test_every_swept_launch_shape_general_groups(emu, layout):
+    """The sweep grid's launch shapes on a general G-group plan with G, P and
+    Bl all above 1 (8 ranks, 4 sequences, 2 groups), both directions."""
+    import bench
+    N, B, S, Hq, Hkv, d, G = 8, 4, 4 * 5, 8, 4, 16, 2
+    shape = (N, B, S, Hq, Hkv, d)
+    rng = np.random.default_rng(12)
+    q, k, v, o = (_rand(B * S * H * d, 2, rng) for H in (Hq, Hkv, Hkv, Hq))
+    want_qkv = oracle.seq_to_head_qkv(q, k, v, oracle.GROUPS, N, B, S, Hq, Hkv, d, layout, G=G)
+    want_o = oracle.head_to_seq(o, oracle.GROUPS, N, B, S, Hq, d, layout, G=G)
+    grid = bench.sweep_grid(2)
+    grid += [dict(t, vectors_per_thread=8) for t in grid if t["vectors_per_thread"] == 4]
+    for t in grid:
+        run = Run(emu, shape, oracle.GROUPS, layout, 2, t, G)
+        out = _empty(want_qkv.size, 2)
+        run("emu_seq_to_head", q, k, v, out)
+        assert np.array_equal(out, want_qkv), ("seq->head", t)
+        out = _empty(want_o.size, 2)
+        run("emu_head_to_seq", o, out)
+        assert np.array_equal(out, want_o), ("head->seq", t)
