@@ -288,14 +288,14 @@ basp_status basp_seq_to_head_unfused_noalloc(const basp_plan *plan, const void *
  * basp_seq_to_head and basp_seq_to_head_o, BASP_HEAD_TO_SEQ to
  * basp_head_to_seq and basp_head_to_seq_qkv (the unfused baseline has a
  * fixed shape).  Zero fields keep the built-in choice, which depends on the
- * row size d*elem_size (measured on MI355X over the Llama/Qwen attention
- * shapes).  Results never depend on these values, only the speed does.
+ * row size d*elem_size and on the bytes the call moves (measured on MI355X
+ * over the Llama/Qwen attention shapes; listed below the fields).  Results
+ * never depend on these values, only the speed does.
  *   vectors_per_thread   1, 2, 4 or 8 (16-byte vectors held in flight per
- *                        lane; built-in 1)
+ *                        lane)
  *   tile_tokens          tokens per work tile (>= 1; built-in: one pass of
  *                        the work-group)
- *   tile_heads           heads per work tile (>= 1, clamped to H/P; built-in
- *                        8 for rows of at most 128 bytes, else 1)
+ *   tile_heads           heads per work tile (>= 1, clamped to H/P)
  *   cache_policy         1 = plain loads and stores, 2 = non-temporal stores,
  *                        3 = non-temporal loads and stores, 4 = non-temporal
  *                        loads, non-temporal device-scope stores (gfx950
@@ -304,26 +304,35 @@ basp_status basp_seq_to_head_unfused_noalloc(const basp_plan *plan, const void *
  *   max_grid             cap on work-groups along x, the tiles of one
  *                        (group member, batch index) pair (tiles loop beyond it)
  *   lane_order           1 = lanes run along tokens first, 2 = along heads
- *                        first (built-in)
- *   xcd_remap            1 = tiles in work-group order (built-in), 2 = each of
- *                        the 8 XCDs takes one contiguous eighth of the tiles
- *                        of a (group member, batch index) pair
+ *                        first
+ *   xcd_remap            1 = tiles in work-group order, 2 = each of the 8
+ *                        XCDs takes one contiguous eighth of the tiles of a
+ *                        (group member, batch index) pair
  *   tile_order           1 = token blocks fastest (the head-sharded side's
  *                        order), 2 = head blocks fastest (the sequence-sharded
- *                        side's order; built-in), 3 = token blocks fastest
- *                        within one source member's token chunk, that
- *                        member's tiles of the neighbouring heads next
+ *                        side's order), 3 = token blocks fastest within one
+ *                        source member's token chunk, that member's tiles of
+ *                        the neighbouring heads next
  *   stage                1 = rows go straight from load to store registers
  *                        (built-in),
  *                        2 = each tile passes through LDS: loads
  *                        run along the source's contiguous axis, stores along
  *                        the destination's (used with 16-byte vectors and
  *                        tiles of one pass of the work-group)
- *   block_size           threads per work-group: 64, 128 or 256 (built-in
- *                        256)
+ *   block_size           threads per work-group: 64, 128 or 256
  *   batch_order          1 = the batch indices one after another (built-in),
  *                        2 = batch indices interleaved with the tiles, so
  *                        that neighbouring work-groups alternate sequences
+ * Built-in choices of the fields that depend on the call (a call's bytes
+ * being what it reads plus what it writes):
+ *   calls above 32 MiB with rows of at most 128 bytes, and above 160 MiB
+ *   with longer rows: 256 threads, 1 vector per lane, 8 heads per tile for
+ *   rows of at most 128 bytes and 1 for longer ones, tile order 2, lanes
+ *   along heads, tiles in work-group order;
+ *   smaller calls with rows of at most 128 bytes: 128 threads, 2 vectors
+ *   per lane, 4 heads per tile, tile order 3, lanes along tokens, XCD
+ *   remap;
+ *   smaller calls with longer rows: as for large calls, with tile order 1.
  * vectors_per_thread and block_size apply to 16-byte vectors; rows that
  * need narrower vectors run 256 threads with 4 vectors each.
  * basp_plan_set_tuning sets both directions, basp_plan_set_direction_tuning

@@ -24,7 +24,23 @@ constexpr uint32_t kGridCap = 1u << 22;  // work-groups per launch at most
 // vector per lane, head blocks fastest in work-group order, lanes along
 // heads, non-temporal loads and non-temporal device-scope stores; 8 heads
 // per tile for 128-byte rows, one head for longer rows.
+//
+// Smaller calls, bound by start-up and drain more than by bandwidth, got a
+// rule of their own, chosen the same way over the named workloads' calls of
+// 4 to 384 MiB (HIP graph replays, 1 296 shapes per call), which lifted the
+// worst ratio there from 0.87-0.89 to 0.95-0.96:
+// * rows of at most 128 bytes, calls of at most 32 MiB: 128 threads, two
+//   vectors per lane, 4 heads per tile, token blocks fastest within a source
+//   member (tile order 3), lanes along tokens, XCD-contiguous tiles;
+// * longer rows, calls of at most 160 MiB: token blocks fastest (tile order
+//   1), the rest as for large calls.
 // basp_plan_autotune replaces these by measurement.
+constexpr uint64_t kSmallCallShortRows = uint64_t{32} << 20;
+constexpr uint64_t kSmallCallLongRows = uint64_t{160} << 20;
+
+// a + b, or the largest value where that overflows (call sizes of plans
+// near the 2^62-byte buffer limit only need to compare as large)
+uint64_t add_sat(uint64_t a, uint64_t b) { return a > ~uint64_t{0} - b ? ~uint64_t{0} : a + b; }
 struct Shape {
     int vpt, policy;
     int block;                          // threads per work-group
@@ -38,20 +54,24 @@ struct Shape {
     bool batch_x;
 };
 
-Shape resolve(const basp_plan &p, const basp_tuning &t)
+// call_bytes: the bytes the launch reads and writes (the algorithmic bytes
+// of the call), which picks between the rules above.
+Shape resolve(const basp_plan &p, const basp_tuning &t, uint64_t call_bytes)
 {
     const bool short_rows = p.row_bytes <= 128;
+    const bool small = call_bytes <= (short_rows ? kSmallCallShortRows : kSmallCallLongRows);
+    const bool small_short = small && short_rows;
     Shape s;
-    s.vpt = t.vectors_per_thread ? t.vectors_per_thread : 1;
+    s.vpt = t.vectors_per_thread ? t.vectors_per_thread : (small_short ? 2 : 1);
     s.policy = t.cache_policy ? t.cache_policy : 4;
-    s.block = t.block_size ? t.block_size : kBlock;
+    s.block = t.block_size ? t.block_size : (small_short ? 128 : kBlock);
     s.tile_tokens = uint32_t(t.tile_tokens);
-    s.tile_heads = t.tile_heads ? uint32_t(t.tile_heads) : (short_rows ? 8 : 1);
+    s.tile_heads = t.tile_heads ? uint32_t(t.tile_heads) : (short_rows ? (small ? 4 : 8) : 1);
     s.heads_given = t.tile_heads != 0;
-    s.s_fast = t.lane_order == 1;
-    s.order = t.tile_order ? t.tile_order : 2;
+    s.s_fast = t.lane_order ? t.lane_order == 1 : small_short;
+    s.order = t.tile_order ? t.tile_order : (small ? (short_rows ? 3 : 1) : 2);
     s.grid_cap = t.max_grid ? uint32_t(t.max_grid) : kGridCap;
-    s.xcd = t.xcd_remap == 2;
+    s.xcd = t.xcd_remap ? t.xcd_remap == 2 : small_short;
     s.stage = t.stage == 2;
     s.batch_x = t.batch_order == 2;
     return s;
@@ -182,8 +202,11 @@ int build_tiles(const basp_plan &p, const SegSpec *segs, int nseg, bool s2h, Til
         return BASP_ERR_UNSUPPORTED;
     const int vw = vector_width(p);
     const uint32_t A = uint32_t(p.row_bytes / vw);
-    const Shape sh =
-        for_vector_width(resolve(p, p.tuning[s2h ? BASP_SEQ_TO_HEAD : BASP_HEAD_TO_SEQ]), vw, A);
+    uint64_t call_bytes = 0;        // read once and written once
+    for (int i = 0; i < nseg; ++i)
+        call_bytes = add_sat(call_bytes, 2 * (uint64_t(p.B) * p.S * segs[i].H * p.row_bytes));
+    const Shape sh = for_vector_width(
+        resolve(p, p.tuning[s2h ? BASP_SEQ_TO_HEAD : BASP_HEAD_TO_SEQ], call_bytes), vw, A);
     TileDesc &D = L.D;
     D.St = uint32_t(p.St);
     D.S = uint32_t(p.S);
@@ -337,23 +360,29 @@ basp_status check_launch_limits(const basp_plan &p, const basp_tuning &t)
     if (p.St > int64_t(kI31Max) || p.row_bytes > int64_t(kI31Max) ||
         int64_t(p.Hq) * p.row_bytes > int64_t(kI31Max) || !grid_fits(p))
         return BASP_ERR_UNSUPPORTED;
-    const Shape resolved = resolve(p, t);
     const uint32_t heads[3] = {uint32_t(p.Hq), uint32_t(p.Hkv), uint32_t(p.Hkv)};
-    // every vector width a launch may pick, with the tile it then uses
-    for (int vw = 16; vw >= p.es; vw /= 2) {
-        if (p.row_bytes % vw)
-            continue;
-        const uint32_t A = uint32_t(p.row_bytes / vw);
-        const Shape sh = for_vector_width(resolved, vw, A);
-        uint64_t total = 0;
-        for (int i = 0; i < 3; ++i) {
-            TileShape ts;
-            if (!fitted_shape(p, sh, heads[i], A, ts))
+    // the built-in choices depend on the call's size: those of a one-tensor
+    // call (O, dO) and of a fused one (Q, K, V)
+    const uint64_t one = 2 * (uint64_t(p.q_elems) * p.es);
+    const uint64_t fused = add_sat(one, add_sat(2 * (uint64_t(p.kv_elems) * p.es), 2 * (uint64_t(p.kv_elems) * p.es)));
+    for (const uint64_t call_bytes : {one, fused}) {
+        const Shape resolved = resolve(p, t, call_bytes);
+        // every vector width a launch may pick, with the tile it then uses
+        for (int vw = 16; vw >= p.es; vw /= 2) {
+            if (p.row_bytes % vw)
+                continue;
+            const uint32_t A = uint32_t(p.row_bytes / vw);
+            const Shape sh = for_vector_width(resolved, vw, A);
+            uint64_t total = 0;
+            for (int i = 0; i < 3; ++i) {
+                TileShape ts;
+                if (!fitted_shape(p, sh, heads[i], A, ts))
+                    return BASP_ERR_UNSUPPORTED;
+                total += ts.ntiles;
+            }
+            if (total * (sh.batch_x ? uint64_t(p.B) : 1u) > kI31Max)
                 return BASP_ERR_UNSUPPORTED;
-            total += ts.ntiles;
         }
-        if (total * (sh.batch_x ? uint64_t(p.B) : 1u) > kI31Max)
-            return BASP_ERR_UNSUPPORTED;
     }
     return BASP_OK;
 }
