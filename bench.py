@@ -99,6 +99,8 @@ def parse_args(argv=None):
     ap.add_argument("--detail-iters", type=int, default=60)
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="skip the table of every named workload")
+    ap.add_argument("--workload-rounds", type=int, default=5,
+                    help="interleaved rounds of the workload table's graph replays (median over them)")
     ap.add_argument("--workload-steps", type=int, default=60,
                     help="least launches per HIP graph in the table of every workload")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -557,53 +559,112 @@ def groups_rates(args):
     return out
 
 
+class GraphTimer:
+    """`calls` back-to-back calls fn(i), captured once in a HIP graph (so that
+    no host gap falls between the kernels) and replayed once untimed;
+    seconds() replays it once more and returns the seconds per call."""
+
+    def __init__(self, fn, calls):
+        import torch
+        torch.cuda.synchronize()
+        self.calls = calls
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            for i in range(calls):
+                fn(i)
+        self.graph.replay()
+        torch.cuda.synchronize()
+        self.start = torch.cuda.Event(enable_timing=True)
+        self.stop = torch.cuda.Event(enable_timing=True)
+
+    def seconds(self):
+        import torch
+        self.start.record()
+        self.graph.replay()
+        self.stop.record()
+        torch.cuda.synchronize()
+        return self.start.elapsed_time(self.stop) * 1e-3 / self.calls
+
+
 def workload_table(args):
     """Fused seq->head and head->seq rates of every named workload in both
     modes (device-filled random bf16: the rate does not depend on values),
-    with the launch shapes of the table.  Each rate is a HIP graph of
-    back-to-back launches on rotating buffer sets (graph_seconds): whole
-    steps, then each direction alone; at least --workload-steps launches per
-    graph, more for small calls.  Once per workload, the plain copy pair at
-    the same byte counts, run the same way."""
+    with the launch shapes of the table, beside the plain copy at the same
+    byte counts.  Per workload, each of nine items -- the copy at each
+    direction's byte count and as a pair, and each mode's whole step,
+    seq->head alone and head->seq alone -- is a HIP graph of back-to-back
+    launches on rotating buffer sets (at least --workload-steps launches,
+    more for small calls).  The nine graphs are replayed in
+    --workload-rounds interleaved rounds, so that slow drift of the device
+    falls on the kernels and the copy alike, and each figure is the median
+    over the rounds.  Both modes' buffers have the same sizes, so they share
+    one buffer set."""
     import torch
     from sequence_re_layout_amd import binding as b
     from sequence_re_layout_amd import launch_shapes, workloads
     steps = args.workload_steps
     out = {}
     for (name, N, B, S, Hq, Hkv, d) in workloads.ALL + workloads.EXTRA:
-        out[name] = {}
+        plans, sources = {}, {}
         for mode, code in (("basp", b.BASP_MODE_BASP), ("ulysses", b.BASP_MODE_ULYSSES)):
-            p = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, code)
-            i = p.info
-            sb, hb = i["qkv_bytes_moved"], i["o_bytes_moved"]
-            R = max(2, -(-(3 << 30) // (sb + hb)))
-            n = max(steps, min(10 * steps, steps * (400 << 20) // sb))
-            sets = table_sets(i, R)
-            source = "built-in"
+            plans[mode] = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, code)
+        i = plans["basp"].info
+        sb, hb = i["qkv_bytes_moved"], i["o_bytes_moved"]
+        R = max(2, -(-(3 << 30) // (sb + hb)))
+        n = max(steps, min(10 * steps, steps * (400 << 20) // sb))
+        sets = table_sets(i, R)
+        for mode, p in plans.items():
+            sources[mode] = "built-in"
             if not args.builtin_shapes:
                 if not args.autotune and launch_shapes.apply(b, p, name, mode):
-                    source = "table"
+                    sources[mode] = "table"
                 else:
-                    b.basp_plan_autotune(p, sets[0]["q"], sets[0]["k"], sets[0]["v"], sets[0]["out"],
-                                         sets[0]["o"], sets[0]["o_out"])
-                    source = "autotuned"
-            t = measure_pair(b, p, sets, R, n)
-            out[name][mode] = dict(t, G=i["G"], P=i["P"], Bl=i["Bl"], launches_per_graph=n, shapes=source,
-                                   s2h_frac=t["s2h_gbs"] / HBM_PEAK_GBS, h2s_frac=t["h2s_gbs"] / HBM_PEAK_GBS)
-            if mode == "basp":   # both modes move the same bytes: one copy pair per workload
-                qkv_b, o_b = sb // 2, hb // 2
+                    s0 = sets[0]
+                    b.basp_plan_autotune(p, s0["q"], s0["k"], s0["v"], s0["out"], s0["o"], s0["o_out"])
+                    sources[mode] = "autotuned"
+        qkv_b, o_b = sb // 2, hb // 2   # bytes each copy reads (and writes)
 
-                def cs(j):
-                    b.basp_stream_copy(sets[j % R]["out"], sets[j % R]["x"], qkv_b)
+        def cs(j):
+            b.basp_stream_copy(sets[j % R]["out"], sets[j % R]["x"], qkv_b)
 
-                def ch(j):
-                    b.basp_stream_copy(sets[j % R]["o_out"], sets[j % R]["x"], o_b)
+        def ch(j):
+            b.basp_stream_copy(sets[j % R]["o_out"], sets[j % R]["x"], o_b)
 
-                out[name]["copy"] = {"s2h_bytes_gbs": rate(2 * qkv_b, graph_seconds(cs, n)),
-                                     "h2s_bytes_gbs": rate(2 * o_b, graph_seconds(ch, n)),
-                                     "step_gbs": rate(2 * (qkv_b + o_b), graph_seconds(lambda j: (cs(j), ch(j)), n))}
-            del sets
-            torch.cuda.empty_cache()
+        def s2h(p):
+            return lambda j: b.basp_seq_to_head(p, sets[j % R]["q"], sets[j % R]["k"], sets[j % R]["v"],
+                                                sets[j % R]["out"])
+
+        def h2s(p):
+            return lambda j: b.basp_head_to_seq(p, sets[j % R]["o"], sets[j % R]["o_out"])
+
+        items = {("copy", "s2h"): cs, ("copy", "h2s"): ch, ("copy", "step"): lambda j: (cs(j), ch(j))}
+        for mode, p in plans.items():
+            fs, fh = s2h(p), h2s(p)
+            items[(mode, "step")] = lambda j, fs=fs, fh=fh: (fs(j), fh(j))
+            items[(mode, "s2h")] = fs
+            items[(mode, "h2s")] = fh
+        timers = {key: GraphTimer(fn, n) for key, fn in items.items()}
+        times = {key: [] for key in items}
+        for _ in range(args.workload_rounds):
+            for key, t in timers.items():
+                times[key].append(t.seconds())
+        del timers
+        med = {key: statistics.median(t) for key, t in times.items()}
+        out[name] = {"copy": {"s2h_bytes_gbs": rate(sb, med[("copy", "s2h")]),
+                              "h2s_bytes_gbs": rate(hb, med[("copy", "h2s")]),
+                              "step_gbs": rate(sb + hb, med[("copy", "step")])}}
+        for mode, p in plans.items():
+            pi = p.info
+            wall, t, u = med[(mode, "step")], med[(mode, "s2h")], med[(mode, "h2s")]
+            out[name][mode] = {
+                "step_us": wall * 1e6, "step_gbs": rate(sb + hb, wall), "s2h_us": t * 1e6, "s2h_gbs": rate(sb, t),
+                "h2s_us": u * 1e6, "h2s_gbs": rate(hb, u), "G": pi["G"], "P": pi["P"], "Bl": pi["Bl"],
+                "launches_per_graph": n, "rounds": args.workload_rounds, "shapes": sources[mode],
+                "s2h_frac": rate(sb, t) / HBM_PEAK_GBS, "h2s_frac": rate(hb, u) / HBM_PEAK_GBS,
+                "s2h_us_range": [min(times[(mode, "s2h")]) * 1e6, max(times[(mode, "s2h")]) * 1e6],
+                "h2s_us_range": [min(times[(mode, "h2s")]) * 1e6, max(times[(mode, "h2s")]) * 1e6]}
+        del sets, plans
+        torch.cuda.empty_cache()
         print("workload table: %s done" % name, file=sys.stderr, flush=True)
     return out
 
