@@ -1085,6 +1085,7 @@ def make_line(args, r, traffic, cpu):
 
     def brief(x):
         return {"G": x["G"], "P": x["P"], "Bl": x["Bl"], "peers_per_rank": x["peers_per_rank"],
+                "cross_rank_bytes_qkv": x["cross_rank_bytes_qkv"],
                 "s2h_gbs": round(x["s2h_gbs"], 1), "s2h_frac": round(x["s2h_gbs"] / HBM_PEAK_GBS, 4),
                 "s2h_avg_us": round(x["s2h"]["avg_us"], 2),
                 "h2s_gbs": round(x["h2s_gbs"], 1), "h2s_frac": round(x["h2s_gbs"] / HBM_PEAK_GBS, 4),

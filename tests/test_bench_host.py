@@ -119,6 +119,7 @@ def _fake_run():
 
     def mode(G, P, Bl, s_us, h_us):
         return {"G": G, "P": P, "Bl": Bl, "peers_per_rank": P - 1, "ms_per_step": 0.33,
+                "cross_rank_bytes_qkv": (P - 1) * (sb // 2) // P,
                 "step_gbs": (sb + hb) / 0.33e-3 / 1e9, "s2h_bytes": sb, "h2s_bytes": hb,
                 "s2h": {"avg_us": s_us, "median_us": s_us, "min_us": s_us, "max_us": s_us, "launches": 50},
                 "h2s": {"avg_us": h_us, "median_us": h_us, "min_us": h_us, "max_us": h_us, "launches": 50},
@@ -154,6 +155,9 @@ def test_json_line_contract():
     assert roof["frac"] == pytest.approx(line["value"] / 8000.0) and roof["traffic"] == 1342181000.0
     assert set(line["basp_vs_ulysses"]) == {"basp", "ulysses"}
     assert line["basp_vs_ulysses"]["ulysses"]["P"] == 8
+    # the exchange volume the two schemes differ in: (P-1)/P of the bytes read
+    assert line["basp_vs_ulysses"]["basp"]["cross_rank_bytes_qkv"] == 503316480
+    assert line["basp_vs_ulysses"]["ulysses"]["cross_rank_bytes_qkv"] == 587202560
     text = json.dumps(line)
     assert len(text) < 3000, len(text)
     assert "\n" not in text
