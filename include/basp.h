@@ -50,7 +50,8 @@
  * ---------------------------------------------------------------------------
  * - Pointers named q, k, v, o, in, out, dq, dk, dv, ws are DEVICE pointers on
  *   the current HIP device; the caller allocates and owns them.  The library
- *   never allocates, frees or keeps device memory or pointers after a call.
+ *   keeps no device memory or pointers after a call.  Only basp_plan_autotune
+ *   allocates device memory, for its own duration (below).
  * - stream is a hipStream_t passed as void*; NULL is the null stream.  Every
  *   call that launches work is asynchronous on that stream and does not
  *   synchronise.
@@ -382,8 +383,15 @@ basp_status basp_plan_get_tuning(const basp_plan *plan, basp_direction dir, basp
  * overlap any of q, k, v, o or each other (BASP_ERR_ALIAS, before any
  * launch).  Every candidate computes the
  * same re-layout, so on BASP_OK qkv and o_out hold the results of the two
- * calls.  Runs on stream and waits for it; creates and destroys HIP events
- * but allocates no device memory.  A pending basp_time_next_call request is
+ * calls.  Runs on stream and waits for it; creates and destroys HIP events.
+ * When the six buffers together are smaller than 512 MiB, they would fit in
+ * the device's caches and the timed launches would run from there, where
+ * other shapes win than in a loop of calls that streams from HBM; the timed
+ * launches then rotate over buffers of the same sizes in a temporary pool of
+ * about 1 GiB (up to 256 sets), allocated with hipMalloc and freed before the
+ * call returns, and the chosen shapes run once more on the caller's buffers
+ * at the end.  If the pool cannot be allocated, the caller's buffers are
+ * timed alone.  A pending basp_time_next_call request is
  * dropped.  Errors as for the two calls; on BASP_ERR_HIP the plan keeps its
  * previous tuning.  The plan must not be used by another thread meanwhile.
  */

@@ -477,31 +477,114 @@ struct Job {
     float ms;
 };
 
+// The six buffers of one autotuner step: seq->head reads q, k, v and writes
+// qkv; head->seq reads o and writes o_out.
+struct TuneBufs {
+    const void *q, *k, *v;
+    void *qkv;
+    const void *o;
+    void *o_out;
+};
+
+// Buffers the autotuner times on.  When the six buffers together fit in the
+// device's caches (4 MB of L2 per XCD and the 256 MB Infinity Cache), timed
+// launches on them would read from the caches, and a shape that is fastest
+// there can be slower in a loop of calls that streams from HBM (measured on
+// the 12 MiB and 42 MB calls).  Below kRotateBelow the timed launches
+// therefore rotate over copies of the buffers' sizes in a temporary pool of
+// about kRotationBytes, so that every launch finds its inputs in HBM.  The
+// pool holds no meaningful values (the kernels copy bits and every shape
+// computes the same permutation); it is freed when the autotuner returns.
+// If it cannot be allocated, the caller's buffers are used alone.
+constexpr uint64_t kRotateBelow = uint64_t{512} << 20;
+constexpr uint64_t kRotationBytes = uint64_t{1} << 30;
+constexpr uint64_t kMaxRotation = 256;
+
+class TuneSets {
+public:
+    TuneSets(const basp_plan &p, const TuneBufs &caller, hipStream_t st) : st_(st)
+    {
+        const uint64_t qb = round_up(uint64_t(p.q_elems) * p.es);
+        const uint64_t kb = round_up(uint64_t(p.kv_elems) * p.es);
+        const uint64_t tb = round_up(uint64_t(p.q_elems + 2 * p.kv_elems) * p.es);
+        const uint64_t set = 3 * qb + 2 * kb + tb;   // q, k, v, qkv, o, o_out
+        if (set < kRotateBelow) {
+            const uint64_t r = std::min(kMaxRotation, std::max<uint64_t>(2, (kRotationBytes + set - 1) / set));
+            if (hipMalloc(&pool_, r * set) == hipSuccess) {
+                char *base = static_cast<char *>(pool_);
+                for (uint64_t i = 0; i < r; ++i) {
+                    char *b = base + i * set;
+                    sets_.push_back({b, b + qb, b + qb + kb, b + qb + 2 * kb, b + qb + 2 * kb + tb,
+                                     b + 2 * qb + 2 * kb + tb});
+                }
+            } else {
+                pool_ = nullptr;
+                (void)hipGetLastError();   // the caller's buffers serve alone
+            }
+        }
+        if (sets_.empty())
+            sets_.push_back(caller);
+    }
+    ~TuneSets()
+    {
+        if (pool_) {   // nothing may still use the pool when it is freed
+            (void)hipStreamSynchronize(st_);
+            (void)hipFree(pool_);
+        }
+    }
+    TuneSets(const TuneSets &) = delete;
+    TuneSets &operator=(const TuneSets &) = delete;
+
+    // The buffers of the next timed step, in turn.
+    const TuneBufs &take()
+    {
+        const TuneBufs &b = sets_[next_];
+        next_ = (next_ + 1) % sets_.size();
+        return b;
+    }
+    size_t count() const { return sets_.size(); }
+
+private:
+    static uint64_t round_up(uint64_t n) { return (n + 255) & ~uint64_t{255}; }
+    hipStream_t st_;
+    void *pool_ = nullptr;
+    std::vector<TuneBufs> sets_;
+    size_t next_ = 0;
+};
+
+// A direction's launch on one set of buffers with the plan's current tuning.
+int prepare_dir(const basp_plan &p, int dir, const TuneBufs &b, TileLaunch &L)
+{
+    return dir == BASP_SEQ_TO_HEAD ? prepare_seq_to_head(p, b.q, b.k, b.v, b.qkv, L)
+                                   : prepare_head_to_seq(p, b.o, b.o_out, L);
+}
+
 // Launch every job once, each timed from its own dispatch timestamps, in
 // batches of kPool launches that share a pool of events.  Each timed launch
-// comes right after an untimed launch of the other direction (partner), as
-// in a step that runs the two back to back: a launch timed alone starts on a
-// drained memory system, and launch shapes ranked that way did not keep
-// their order back to back.  False on a HIP error; a job whose shape the
-// plan rejects gets a time < 0.
+// comes right after an untimed launch of the other direction (partner, with
+// the plan's shape on entry) on the same buffers, as in a step that runs the
+// two back to back: a launch timed alone starts on a drained memory system,
+// and launch shapes ranked that way did not keep their order back to back.
+// False on a HIP error; a job whose shape the plan rejects gets a time < 0.
 constexpr int kPool = 64;
 
 bool run_jobs(basp_plan &p, const std::vector<basp_tuning> &cands, std::vector<Job> &jobs,
-              const TileLaunch (&partner)[2], const void *q, const void *k, const void *v,
-              void *qkv, const void *o, void *o_out, void *stream, hipEvent_t *ev)
+              const basp_tuning (&entry)[2], TuneSets &ts, void *stream, hipEvent_t *ev)
 {
     for (size_t first = 0; first < jobs.size(); first += kPool) {
         const size_t last = std::min(jobs.size(), first + kPool);
         for (size_t j = first; j < last; ++j) {
             Job &job = jobs[j];
+            const TuneBufs &b = ts.take();
+            TileLaunch partner, L;
+            p.tuning[1 - job.dir] = entry[1 - job.dir];
             p.tuning[job.dir] = cands[job.cand];
-            TileLaunch L;
-            const int st = job.dir == BASP_SEQ_TO_HEAD ? prepare_seq_to_head(p, q, k, v, qkv, L)
-                                                       : prepare_head_to_seq(p, o, o_out, L);
             job.ms = -1.f;
-            if (st != BASP_OK)
+            if (prepare_dir(p, 1 - job.dir, b, partner) != BASP_OK)
+                return false;   // the entry shapes were accepted on the caller's buffers
+            if (prepare_dir(p, job.dir, b, L) != BASP_OK)
                 continue;
-            if (launch(partner[1 - job.dir], stream) != BASP_OK)
+            if (launch(partner, stream) != BASP_OK)
                 return false;
             t_timing.start = ev[2 * (j - first)];
             t_timing.stop = ev[2 * (j - first) + 1];
@@ -526,8 +609,7 @@ bool run_jobs(basp_plan &p, const std::vector<basp_tuning> &cands, std::vector<J
 // slow drifts of the device affect all candidates alike.
 bool measure_rounds(basp_plan &p, const std::vector<basp_tuning> &cands,
                     const std::vector<int> (&pick)[2], int rounds, std::vector<float> (&med)[2],
-                    const TileLaunch (&partner)[2], const void *q, const void *k, const void *v,
-                    void *qkv, const void *o, void *o_out, void *stream, hipEvent_t *ev)
+                    const basp_tuning (&entry)[2], TuneSets &ts, void *stream, hipEvent_t *ev)
 {
     const size_t n = std::max(pick[0].size(), pick[1].size());
     std::vector<std::vector<float>> times[2];
@@ -539,7 +621,7 @@ bool measure_rounds(basp_plan &p, const std::vector<basp_tuning> &cands,
             for (int dir = 0; dir < 2; ++dir)
                 if (i < pick[dir].size())
                     jobs.push_back({dir, pick[dir][i], 0.f});
-        if (!run_jobs(p, cands, jobs, partner, q, k, v, qkv, o, o_out, stream, ev))
+        if (!run_jobs(p, cands, jobs, entry, ts, stream, ev))
             return false;
         size_t idx[2] = {0, 0};
         for (const Job &job : jobs)
@@ -556,13 +638,13 @@ bool measure_rounds(basp_plan &p, const std::vector<basp_tuning> &cands,
 }
 
 // Median seconds per step, over `rounds` rounds, of each pair (seq->head
-// shape, head->seq shape): kSteps steps run back to back, timed by events
-// recorded only before the first and after the last launch.  False on a
-// HIP error; a pair whose shapes the plan rejects gets a time < 0.
+// shape, head->seq shape): kSteps steps run back to back, each on the next
+// set of buffers, timed by events recorded only before the first and after
+// the last launch (the launches are prepared before the first event).  False
+// on a HIP error; a pair whose shapes the plan rejects gets a time < 0.
 bool measure_pairs(basp_plan &p, const std::vector<basp_tuning> &cands,
                    const std::vector<std::pair<int, int>> &pairs, int rounds, std::vector<float> &med,
-                   const void *q, const void *k, const void *v, void *qkv, const void *o, void *o_out,
-                   void *stream, hipEvent_t *ev)
+                   TuneSets &ts, void *stream, hipEvent_t *ev)
 {
     constexpr int kSteps = 6;
     const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -574,14 +656,19 @@ bool measure_pairs(basp_plan &p, const std::vector<basp_tuning> &cands,
             for (size_t i = first; i < last; ++i) {
                 p.tuning[BASP_SEQ_TO_HEAD] = cands[pairs[i].first];
                 p.tuning[BASP_HEAD_TO_SEQ] = cands[pairs[i].second];
-                TileLaunch ls, lh;
-                if (prepare_seq_to_head(p, q, k, v, qkv, ls) != BASP_OK ||
-                    prepare_head_to_seq(p, o, o_out, lh) != BASP_OK)
+                TileLaunch ls[kSteps], lh[kSteps];
+                bool fits = true;
+                for (int n = 0; n < kSteps && fits; ++n) {
+                    const TuneBufs &b = ts.take();
+                    fits = prepare_dir(p, BASP_SEQ_TO_HEAD, b, ls[n]) == BASP_OK &&
+                           prepare_dir(p, BASP_HEAD_TO_SEQ, b, lh[n]) == BASP_OK;
+                }
+                if (!fits)
                     continue;
                 if (hipEventRecord(ev[2 * (i - first)], st) != hipSuccess)
                     return false;
                 for (int n = 0; n < kSteps; ++n)
-                    if (launch(ls, stream) != BASP_OK || launch(lh, stream) != BASP_OK)
+                    if (launch(ls[n], stream) != BASP_OK || launch(lh[n], stream) != BASP_OK)
                         return false;
                 if (hipEventRecord(ev[2 * (i - first) + 1], st) != hipSuccess)
                     return false;
@@ -617,17 +704,18 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
     basp::t_timing = basp::Timing();
     if (!p)
         return record(BASP_ERR_INVALID);
-    // the partner launches: each direction with the plan's shape on entry
-    basp::TileLaunch partner[2];
+    // both directions must launch on the caller's buffers with the shapes on
+    // entry (the partner launches of the timed rounds use those shapes)
+    basp::TileLaunch entry_launch[2];
+    const basp::TuneBufs caller = {q, k, v, qkv, o, o_out};
     int s = basp::check_autotune_buffers(*p, q, k, v, qkv, o, o_out);
-    if (s == BASP_OK)
-        s = basp::prepare_seq_to_head(*p, q, k, v, qkv, partner[BASP_SEQ_TO_HEAD]);
-    if (s == BASP_OK)
-        s = basp::prepare_head_to_seq(*p, o, o_out, partner[BASP_HEAD_TO_SEQ]);
+    for (int dir = 0; dir < 2 && s == BASP_OK; ++dir)
+        s = basp::prepare_dir(*p, dir, caller, entry_launch[dir]);
     if (s != BASP_OK || p->S == 0)
         return record(basp_status(s));
 
     constexpr int kCoarse = 3, kFine = 7, kKeep = 6, kPairs = 3, kPairRounds = 5;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
     hipEvent_t ev[2 * basp::kPool];
     int made = 0;
     // timing-only events: without the system-scope fence an event otherwise
@@ -638,6 +726,7 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
             break;
     const basp_tuning saved[2] = {p->tuning[0], p->tuning[1]};
     bool ok = made == 2 * basp::kPool;
+    basp::TuneSets ts(*p, caller, st);
     const std::vector<basp_tuning> cands = basp::autotune_candidates(*p);
     std::vector<int> pick[2];
     for (int dir = 0; dir < 2; ++dir)
@@ -647,7 +736,7 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
     std::vector<float> med[2];
     // coarse pass over every candidate, then a longer one over the best few;
     // a direction without any measured candidate keeps its tuning
-    ok = ok && basp::measure_rounds(*p, cands, pick, kCoarse, med, partner, q, k, v, qkv, o, o_out, stream, ev);
+    ok = ok && basp::measure_rounds(*p, cands, pick, kCoarse, med, saved, ts, stream, ev);
     for (int dir = 0; dir < 2 && ok; ++dir) {
         std::vector<std::pair<float, int>> order;
         for (size_t i = 0; i < pick[dir].size(); ++i)
@@ -658,7 +747,7 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
         for (size_t i = 0; i < order.size() && int(i) < kKeep; ++i)
             pick[dir].push_back(order[i].second);
     }
-    ok = ok && basp::measure_rounds(*p, cands, pick, kFine, med, partner, q, k, v, qkv, o, o_out, stream, ev);
+    ok = ok && basp::measure_rounds(*p, cands, pick, kFine, med, saved, ts, stream, ev);
     // the best few of each direction, then every pair of them timed as whole
     // back-to-back steps: the shapes of the two directions affect each other
     std::vector<int> top[2];
@@ -683,7 +772,7 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
             pairs.push_back({a, c});
     pairs.push_back({entry, entry + 1});
     std::vector<float> step;
-    ok = ok && basp::measure_pairs(*p, shapes, pairs, kPairRounds, step, q, k, v, qkv, o, o_out, stream, ev);
+    ok = ok && basp::measure_pairs(*p, shapes, pairs, kPairRounds, step, ts, stream, ev);
     basp_tuning chosen[2] = {saved[0], saved[1]};
     int best = -1;
     for (size_t i = 0; ok && i < pairs.size(); ++i)
@@ -699,6 +788,14 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
     }
     p->tuning[0] = chosen[0];
     p->tuning[1] = chosen[1];
+    // the two calls once more on the caller's buffers, with the chosen
+    // shapes: their outputs then hold the results whichever buffers the
+    // timed launches used
+    for (int dir = 0; dir < 2 && ok; ++dir) {
+        basp::TileLaunch L;
+        ok = basp::prepare_dir(*p, dir, caller, L) == BASP_OK && basp::launch(L, stream) == BASP_OK;
+    }
+    ok = ok && hipStreamSynchronize(st) == hipSuccess;
     for (int i = 0; i < made; ++i)
         (void)hipEventDestroy(ev[i]);
     if (!ok) {
