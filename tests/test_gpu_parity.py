@@ -545,7 +545,11 @@ def test_timed_call_records_kernel_time_and_keeps_results():
                          ids=["llama1b-basp", "ragged-ulysses"])
 def test_autotune_keeps_results(shape, mode):
     """basp_plan_autotune stores a valid launch shape per direction and the
-    re-layout stays bit-exact with it."""
+    re-layout stays bit-exact with it.  The Llama-3.2-1B plan's six buffers
+    (670 MB) are timed on themselves; the ragged plan's are below 512 MiB, so
+    its launches are timed on the temporary pool and only the final run of
+    the chosen shapes writes the caller's outputs, which start sentinel-filled
+    here."""
     needs_gpu()
     N, B, S, Hq, Hkv, d = shape
     plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_BF16, mode)
@@ -554,6 +558,8 @@ def test_autotune_keeps_results(shape, mode):
     o = inputs.normal_bf16(i["q_elems"], inputs.SEED_O).cuda()
     qkv = torch.empty(i["qkv_elems"], dtype=torch.bfloat16, device="cuda")
     o_out = torch.empty(i["q_elems"], dtype=torch.bfloat16, device="cuda")
+    qkv.view(torch.int16).fill_(-1)
+    o_out.view(torch.int16).fill_(-1)
     b.basp_plan_autotune(plan, q, k, v, qkv, o, o_out)
     torch.cuda.synchronize()
     want = oracle.seq_to_head_qkv(bits(q), bits(k), bits(v), mode, N, B, S, Hq, Hkv, d)
