@@ -384,14 +384,17 @@ basp_status basp_plan_get_tuning(const basp_plan *plan, basp_direction dir, basp
  * launch).  Every candidate computes the
  * same re-layout, so on BASP_OK qkv and o_out hold the results of the two
  * calls.  Runs on stream and waits for it; creates and destroys HIP events.
- * When the six buffers together are smaller than 512 MiB, they would fit in
- * the device's caches and the timed launches would run from there, where
- * other shapes win than in a loop of calls that streams from HBM; the timed
+ * When the six buffers together are smaller than 32 MiB, they fit in the
+ * device's caches and the timed launches would run from there, where other
+ * shapes win than in a loop of calls that streams from HBM; the timed
  * launches then rotate over buffers of the same sizes in a temporary pool of
  * about 1 GiB (up to 256 sets), allocated with hipMalloc and freed before the
- * call returns, and the chosen shapes run once more on the caller's buffers
- * at the end.  If the pool cannot be allocated, the caller's buffers are
- * timed alone.  A pending basp_time_next_call request is
+ * call returns, the pairs are timed from HIP graphs on a private stream
+ * (created and destroyed in the call; they touch only the pool), and the
+ * chosen shapes run once more on the caller's buffers at the end.  If the
+ * pool cannot be allocated, the caller's buffers are timed alone.  Larger
+ * calls are timed on the caller's buffers, whose placement some shapes'
+ * speed depends on.  A pending basp_time_next_call request is
  * dropped.  Errors as for the two calls; on BASP_ERR_HIP the plan keeps its
  * previous tuning.  The plan must not be used by another thread meanwhile.
  */

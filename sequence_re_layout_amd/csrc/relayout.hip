@@ -486,17 +486,23 @@ struct TuneBufs {
     void *o_out;
 };
 
-// Buffers the autotuner times on.  When the six buffers together fit in the
-// device's caches (4 MB of L2 per XCD and the 256 MB Infinity Cache), timed
-// launches on them would read from the caches, and a shape that is fastest
-// there can be slower in a loop of calls that streams from HBM (measured on
-// the 12 MiB and 42 MB calls).  Below kRotateBelow the timed launches
-// therefore rotate over copies of the buffers' sizes in a temporary pool of
-// about kRotationBytes, so that every launch finds its inputs in HBM.  The
-// pool holds no meaningful values (the kernels copy bits and every shape
-// computes the same permutation); it is freed when the autotuner returns.
-// If it cannot be allocated, the caller's buffers are used alone.
-constexpr uint64_t kRotateBelow = uint64_t{512} << 20;
+// Buffers the autotuner times on.  When the six buffers together fit well
+// inside the device's caches (4 MB of L2 per XCD and the 256 MB Infinity
+// Cache), timed launches on them read from the caches, and a shape that is
+// fastest there can be slower in a loop of calls that streams from HBM
+// (measured on the tiny workload's 16 MiB).  Below kRotateBelow the timed
+// launches therefore rotate over copies of the buffers' sizes in a temporary
+// pool of about kRotationBytes, so that every launch finds its inputs in
+// HBM, and the pairs are ranked from HIP graph replays.  Larger calls are
+// timed on the caller's own buffers: some shapes run up to 16% faster or
+// slower depending on where their buffers lie relative to each other, so the
+// caller's placement is the one to measure.  On the pool's placement the
+// picks for 56 MB and 335 MB working sets were worse than on the caller's
+// buffers.  The pool holds no meaningful values (the kernels copy bits and
+// every shape computes the same permutation); it is freed when the
+// autotuner returns.  If it cannot be allocated, the caller's buffers are
+// used alone.
+constexpr uint64_t kRotateBelow = uint64_t{32} << 20;
 constexpr uint64_t kRotationBytes = uint64_t{1} << 30;
 constexpr uint64_t kMaxRotation = 256;
 
@@ -543,6 +549,7 @@ public:
         return b;
     }
     size_t count() const { return sets_.size(); }
+    bool pooled() const { return pool_ != nullptr; }
 
 private:
     static uint64_t round_up(uint64_t n) { return (n + 255) & ~uint64_t{255}; }
@@ -692,6 +699,80 @@ bool measure_pairs(basp_plan &p, const std::vector<basp_tuning> &cands,
     return true;
 }
 
+// Seconds per step of each pair (seq->head shape, head->seq shape) from HIP
+// graphs, for calls timed on the pool: each pair's `steps` back-to-back steps,
+// each on the next set of pool buffers, are captured once on a private
+// stream and the graphs are replayed in `rounds` interleaved rounds, so no
+// host launch time enters a step (a small call's step is about as short as
+// the host's launch of it) and slow drift of the device affects every pair
+// alike.  The graphs touch only the pool, so the private stream needs no
+// ordering with the caller's.  False on a HIP error (the caller then times
+// the pairs eagerly); a pair whose shapes the plan rejects gets a time < 0.
+bool measure_pairs_graphs(basp_plan &p, const std::vector<basp_tuning> &cands,
+                          const std::vector<std::pair<int, int>> &pairs, int rounds, int steps,
+                          std::vector<float> &med, TuneSets &ts, hipEvent_t *ev)
+{
+    hipStream_t cs;
+    if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess)
+        return false;
+    std::vector<hipGraphExec_t> exec(pairs.size(), nullptr);
+    std::vector<TileLaunch> ls(steps), lh(steps);
+    bool ok = true;
+    for (size_t i = 0; i < pairs.size() && ok; ++i) {
+        p.tuning[BASP_SEQ_TO_HEAD] = cands[pairs[i].first];
+        p.tuning[BASP_HEAD_TO_SEQ] = cands[pairs[i].second];
+        bool fits = true;
+        for (int n = 0; n < steps && fits; ++n) {
+            const TuneBufs &b = ts.take();
+            fits = prepare_dir(p, BASP_SEQ_TO_HEAD, b, ls[n]) == BASP_OK &&
+                   prepare_dir(p, BASP_HEAD_TO_SEQ, b, lh[n]) == BASP_OK;
+        }
+        if (!fits)
+            continue;
+        if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+            ok = false;
+            break;
+        }
+        bool captured = true;
+        for (int n = 0; n < steps && captured; ++n)
+            captured = launch(ls[n], cs) == BASP_OK && launch(lh[n], cs) == BASP_OK;
+        hipGraph_t g = nullptr;
+        ok = hipStreamEndCapture(cs, &g) == hipSuccess && captured && g;
+        ok = ok && hipGraphInstantiate(&exec[i], g, nullptr, nullptr, 0) == hipSuccess;
+        if (g)
+            (void)hipGraphDestroy(g);
+        ok = ok && hipGraphLaunch(exec[i], cs) == hipSuccess;   // untimed first replay
+    }
+    ok = ok && hipStreamSynchronize(cs) == hipSuccess;
+    std::vector<std::vector<float>> times(pairs.size());
+    for (int r = 0; r < rounds && ok; ++r)
+        for (size_t i = 0; i < pairs.size() && ok; ++i) {
+            float ms = -1.f;
+            if (exec[i]) {
+                ok = hipEventRecord(ev[0], cs) == hipSuccess && hipGraphLaunch(exec[i], cs) == hipSuccess &&
+                     hipEventRecord(ev[1], cs) == hipSuccess && hipStreamSynchronize(cs) == hipSuccess &&
+                     hipEventElapsedTime(&ms, ev[0], ev[1]) == hipSuccess;
+                ms /= steps;
+            }
+            times[i].push_back(ms);
+        }
+    for (hipGraphExec_t e : exec)
+        if (e)
+            (void)hipGraphExecDestroy(e);
+    (void)hipStreamSynchronize(cs);
+    (void)hipStreamDestroy(cs);
+    if (!ok) {
+        (void)hipGetLastError();
+        return false;
+    }
+    med.clear();
+    for (std::vector<float> &t : times) {
+        std::nth_element(t.begin(), t.begin() + t.size() / 2, t.end());
+        med.push_back(t[t.size() / 2]);
+    }
+    return true;
+}
+
 }  // namespace
 }  // namespace basp
 
@@ -714,7 +795,7 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
     if (s != BASP_OK || p->S == 0)
         return record(basp_status(s));
 
-    constexpr int kCoarse = 3, kFine = 7, kKeep = 6, kPairs = 3, kPairRounds = 5;
+    constexpr int kCoarse = 3, kFine = 7, kKeep = 6, kPairRounds = 5;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     hipEvent_t ev[2 * basp::kPool];
     int made = 0;
@@ -727,6 +808,9 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
     const basp_tuning saved[2] = {p->tuning[0], p->tuning[1]};
     bool ok = made == 2 * basp::kPool;
     basp::TuneSets ts(*p, caller, st);
+    // calls timed on the pool rank their pairs from HIP graph replays, which
+    // time a step as a loop of calls runs it, so more pairs are worth timing
+    const int kPairs = ts.pooled() ? 6 : 3;
     const std::vector<basp_tuning> cands = basp::autotune_candidates(*p);
     std::vector<int> pick[2];
     for (int dir = 0; dir < 2; ++dir)
@@ -772,7 +856,15 @@ extern "C" basp_status basp_plan_autotune(basp_plan *p, const void *q, const voi
             pairs.push_back({a, c});
     pairs.push_back({entry, entry + 1});
     std::vector<float> step;
-    ok = ok && basp::measure_pairs(*p, shapes, pairs, kPairRounds, step, ts, stream, ev);
+    bool graphed = false;
+    if (ok && ts.pooled()) {
+        // steps per graph: about 0.4 ms of device time per replay
+        const double step_s = double(p->q_elems * 2 + p->kv_elems * 2) * 2 * p->es / 5e12 + 5e-6;
+        const int steps = std::max(6, std::min(100, int(4e-4 / step_s)));
+        graphed = basp::measure_pairs_graphs(*p, shapes, pairs, kPairRounds, steps, step, ts, ev);
+    }
+    if (!graphed)
+        ok = ok && basp::measure_pairs(*p, shapes, pairs, kPairRounds, step, ts, stream, ev);
     basp_tuning chosen[2] = {saved[0], saved[1]};
     int best = -1;
     for (size_t i = 0; ok && i < pairs.size(); ++i)

@@ -546,7 +546,7 @@ def test_timed_call_records_kernel_time_and_keeps_results():
 def test_autotune_keeps_results(shape, mode):
     """basp_plan_autotune stores a valid launch shape per direction and the
     re-layout stays bit-exact with it.  The Llama-3.2-1B plan's six buffers
-    (670 MB) are timed on themselves; the ragged plan's are below 512 MiB, so
+    (670 MB) are timed on themselves; the ragged plan's are below 32 MiB, so
     its launches are timed on the temporary pool and only the final run of
     the chosen shapes writes the caller's outputs, which start sentinel-filled
     here."""
