@@ -204,3 +204,22 @@ def test_sweep_grid_shapes_are_valid_tunings():
                 b.basp_plan_set_direction_tuning(p, direction, **t)
                 got = b.basp_plan_get_tuning(p, direction)
                 assert all(got[k] == v for k, v in t.items())
+
+
+def test_table_entries_set_every_size_dependent_field():
+    """The built-in defaults of unset tuning fields depend on a call's size,
+    so a table entry that left one unset could change kernels when those
+    defaults change.  Every entry sets them all (lane order only matters to
+    the direct kernel)."""
+    from sequence_re_layout_amd import launch_shapes
+    fields = ("vectors_per_thread", "block_size", "tile_heads", "tile_order", "xcd_remap")
+    shapes = launch_shapes.table()["shapes"]
+    assert shapes
+    for name, modes in shapes.items():
+        for mode, entry in modes.items():
+            for direction in ("seq_to_head", "head_to_seq"):
+                t = entry[direction]
+                missing = [f for f in fields if not t.get(f)]
+                if t.get("stage") != 2 and not t.get("lane_order"):
+                    missing.append("lane_order")
+                assert not missing, (name, mode, direction, missing)
