@@ -223,8 +223,10 @@ def basp_plan_get_tuning(plan: Plan, direction: int = BASP_SEQ_TO_HEAD) -> dict:
 
 
 def basp_plan_autotune(plan: Plan, q, k, v, qkv, o, o_out, stream=None) -> None:
-    """Measure launch shapes on these buffers and keep the fastest per
-    direction (qkv and o_out are overwritten)."""
+    """Measure launch shapes and keep the fastest per direction: on these
+    buffers, or, when the six total less than 32 MiB, on a temporary pool the
+    library allocates and frees (see basp.h).  qkv and o_out end up holding
+    the results of the two calls."""
     i = plan.info
     _check(_lib.basp_plan_autotune(
         plan.handle, _ptr(q, plan, i["q_elems"], "q"), _ptr(k, plan, i["kv_elems"], "k"),
