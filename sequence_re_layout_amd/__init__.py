@@ -9,7 +9,7 @@ before the library is built.  Using a binding name without a built
 """
 
 
-_SUBMODULES = ("binding", "build", "inputs", "workloads")
+_SUBMODULES = ("autograd", "binding", "build", "inputs", "launch_shapes", "workloads")
 
 
 def __getattr__(name):

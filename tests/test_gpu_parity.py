@@ -411,6 +411,43 @@ def test_backward_entries(shape, layout, mode):
     assert np.array_equal(bits(dq), wq) and np.array_equal(bits(dk), wk) and np.array_equal(bits(dv), wv)
 
 
+@pytest.mark.parametrize("layout", [0, 1], ids=["head_major", "token_major"])
+@pytest.mark.parametrize("mode", ["basp", "ulysses"])
+def test_autograd_wrappers(mode, layout):
+    """sequence_re_layout_amd.autograd: the forward results are the oracle's,
+    and torch.autograd's gradients through them are the oracle's inverse
+    re-layouts of the upstream gradients (a permutation's adjoint is its
+    inverse), bit for bit; a boundary round trip O := HEAD(Q) gives Q back
+    with the upstream gradient as Q's gradient."""
+    needs_gpu()
+    from sequence_re_layout_amd import autograd as ag
+    N, B, S, Hq, Hkv, d = (6, 3, 6 * 37, 12, 6, 40)
+    m = MODE[mode]
+    plan = b.basp_plan_create_ex(N, B, S, Hq, Hkv, d, b.BASP_BF16, m, layout)
+    i = plan.info
+    q = inputs.normal_bf16(i["q_elems"], 31).cuda().requires_grad_()
+    k = inputs.normal_bf16(i["kv_elems"], 32).cuda().requires_grad_()
+    v = inputs.normal_bf16(i["kv_elems"], 33).cuda().requires_grad_()
+    qkv = ag.seq_to_head_qkv(plan, q, k, v)
+    assert np.array_equal(bits(qkv.detach()), oracle.seq_to_head_qkv(
+        bits(q.detach()), bits(k.detach()), bits(v.detach()), m, N, B, S, Hq, Hkv, d, layout))
+    g = inputs.normal_bf16(i["qkv_elems"], 34)
+    dq, dk, dv = torch.autograd.grad(qkv, (q, k, v), g.cuda())
+    wq, wk, wv = oracle.head_to_seq_qkv(inputs.raw_bits(g), m, N, B, S, Hq, Hkv, d, layout)
+    assert np.array_equal(bits(dq), wq) and np.array_equal(bits(dk), wk) and np.array_equal(bits(dv), wv)
+    o = inputs.normal_bf16(i["q_elems"], 35).cuda().requires_grad_()
+    y = ag.head_to_seq_o(plan, o)
+    assert np.array_equal(bits(y.detach()), oracle.head_to_seq(bits(o.detach()), m, N, B, S, Hq, d, layout))
+    go = inputs.normal_bf16(i["q_elems"], 36)
+    (do,) = torch.autograd.grad(y, (o,), go.cuda())
+    assert np.array_equal(bits(do), oracle.seq_to_head(inputs.raw_bits(go), m, N, B, S, Hq, d, layout))
+    # round trip through both wrappers: Q back, and Q's gradient is the upstream one
+    back = ag.head_to_seq_o(plan, ag.seq_to_head_qkv(plan, q, k, v)[: i["q_elems"]])
+    assert torch.equal(back.detach().view(torch.int16), q.detach().view(torch.int16))
+    (dq2,) = torch.autograd.grad(back, (q,), go.cuda())
+    assert torch.equal(dq2.view(torch.int16), go.cuda().view(torch.int16))
+
+
 @pytest.mark.parametrize("mode", ["basp", "ulysses"])
 @pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("shape", [workloads.LLAMA_1B[1:], workloads.QWEN_1_8B[1:],
