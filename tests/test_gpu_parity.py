@@ -1081,6 +1081,58 @@ def test_plan_shared_by_threads_and_streams():
         assert np.array_equal(results[t][0], want_s) and np.array_equal(results[t][1], want_h), t
 
 
+def test_autotune_in_threads():
+    """Two host threads autotune plans of their own at the same time, each on
+    its own stream (both small enough for the timing pool and the HIP graphs
+    captured on the library's private streams), while a third thread keeps
+    launching re-layouts of a third plan on its stream; every result matches
+    the oracle."""
+    needs_gpu()
+    import threading
+    cases = [((6, 3, 6 * 37, 12, 6, 40), 1, "int32"), (workloads.TINY[1:], 0, "bf16"),
+             ((4, 2, 4 * 29, 8, 4, 64), 1, "int32")]
+    want = []
+    for (N, B, S, Hq, Hkv, d), m, dt in cases:
+        q, k, v = seq_inputs(B, S, Hq, Hkv, d, dt)
+        nq = B * S * Hq * d
+        o = inputs.tags_int32(nq, 5) if dt == "int32" else inputs.normal_bf16(nq, inputs.SEED_O)
+        want.append(((q, k, v, o), oracle.seq_to_head_qkv(bits(q), bits(k), bits(v), m, N, B, S, Hq, Hkv, d),
+                     oracle.head_to_seq(bits(o), m, N, B, S, Hq, d)))
+    results, errors = {}, []
+    torch.cuda.synchronize()
+
+    def worker(t):
+        try:
+            (N, B, S, Hq, Hkv, d), m, dt = cases[t]
+            tdt = torch.int32 if dt == "int32" else torch.bfloat16
+            plan = b.basp_plan_create(N, B, S, Hq, Hkv, d, b.BASP_INT32 if dt == "int32" else b.BASP_BF16, m)
+            i = plan.info
+            torch.cuda.set_device(0)
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                qd, kd, vd, od = (x.cuda() for x in want[t][0])
+                out = torch.empty(i["qkv_elems"], dtype=tdt, device="cuda")
+                back = torch.empty(i["q_elems"], dtype=tdt, device="cuda")
+                if t < 2:
+                    b.basp_plan_autotune(plan, qd, kd, vd, out, od, back)
+                for _ in range(200 if t == 2 else 3):
+                    b.basp_seq_to_head(plan, qd, kd, vd, out)
+                    b.basp_head_to_seq(plan, od, back)
+            stream.synchronize()
+            results[t] = (bits(out), bits(back))
+        except Exception as e:   # reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(3)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    for t in range(3):
+        assert np.array_equal(results[t][0], want[t][1]) and np.array_equal(results[t][1], want[t][2]), t
+
+
 @pytest.mark.parametrize("seed", range(random_cases.COUNT))
 def test_random_shapes_and_tunings(seed):
     """Seeded random plans and launch shapes (odd row sizes, every tuning
