@@ -373,9 +373,10 @@ basp_status basp_plan_get_tuning(const basp_plan *plan, basp_direction dir, basp
  * (q, k, v -> qkv) and for head->seq on (o -> o_out), in rounds that
  * alternate the two directions, each timed launch right after an untimed
  * launch of the other direction with the plan's shape on entry (as the two
- * run back to back in a step).  The best three shapes of each direction are
- * then paired, and every pair is timed as whole back-to-back steps, together
- * with the pair of the plan's shapes on entry.  The pair with the lowest
+ * run back to back in a step).  The best three shapes of each direction (six
+ * on the timing pool described below) are then paired, and every pair is
+ * timed as whole back-to-back steps, together with the pair of the plan's
+ * shapes on entry.  The pair with the lowest
  * median step time is stored in the plan, replacing its tuning (the shapes
  * on entry stay when they win).  The buffers are those of basp_seq_to_head
  * and basp_head_to_seq, with the same checks, and because the two calls run
