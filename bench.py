@@ -285,7 +285,7 @@ def step_loop(b, s_fn, h_fn, steps, warmup, every, min_launches, marker=True):
     torch.cuda.synchronize()
     every = max(1, every)
     total = max(steps, every * max(1, min_launches))
-    nsamp = -(-total // every)
+    nsamp = total // every   # steps every-1, 2*every-1, ... (at least min_launches)
     ev = make_events(4 * nsamp)
     if marker:
         torch.cuda._sleep(MARKER_CYCLES)
@@ -296,7 +296,9 @@ def step_loop(b, s_fn, h_fn, steps, warmup, every, min_launches, marker=True):
         if i == steps:
             torch.cuda.synchronize()
             wall = time.perf_counter() - t0
-        j = i // every if i % every == 0 else -1
+        # the 10th, 20th, ... step (with every = 10): the first step after a
+        # short warm-up still runs in the device's ramp-up
+        j = i // every if (i + 1) % every == 0 else -1
         if j >= 0:
             b.basp_time_next_call(ev[4 * j], ev[4 * j + 1])
         s_fn(i)
